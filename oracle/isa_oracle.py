@@ -1,0 +1,336 @@
+"""Blockwise fp64 CPU oracle for the In-context Sparse Attention (ISA) forward pass.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke entry point and the
+benchmark's CPU-baseline leg may import this module. The HIP library never
+calls it, and it shares no code with the HIP path.
+
+What it computes, per (batch, head), written from these pages:
+
+* [RB] paper.rainbus.top structured summary of arXiv 2605.04569
+  ("LIVEditor-14B ... In-Context Sparse Attention"), sections "Prerequisites"
+  (block-sparse and pooling attention; 0th-order Taylor attention), "Core
+  method" and "Method steps" steps (1)-(6).
+* [TW] techwalker.com news article on the same paper, section 4 (the ISA
+  workflow) and section 5 (block-wise 0th-order Taylor sparse attention).
+* [HF] the LIVEditor model card, section "Method".
+
+ISA is an approximation, so the oracle is the algorithm itself, step by
+step, in float64, on the exact input values given to the GPU (bf16 values
+widened to fp64). Outputs are computed with a max-shifted two-pass softmax.
+
+Readings where the pages are silent or contradict each other (each is
+listed with its reason in the repository's design notes):
+
+R1  alpha_f is the fraction of query blocks sent to the flat (Taylor) path
+    ([RB] "Method steps" step (3)); alpha_s=1, alpha_f=0 is then dense
+    attention.
+R2  counts round toward more exact work: k_ctx = ceil(alpha_s*N_ctx),
+    n_flat = floor(alpha_f*N), k_ns = min(N_kv, ceil(alpha_ns*N_kv)).
+R3  blocks are cut per segment (source, then context), each tail block holds
+    the remaining n_j < b tokens, and means are over the n_j valid tokens.
+R4  sharpness of query block i is the population variance of the softmax of
+    its coarse scores over the source key-block columns.
+R5  every query block (source and context) gets a sharpness and a path.
+R6  the context score is the raw scaled coarse score summed over the source
+    query rows.
+R7  the sharp and the flat path both see only the kept KV blocks J (all
+    source blocks plus the selected context blocks); pruned context blocks
+    contribute nothing, and the "total block count" for alpha_ns is |J|.
+R8  the exact set E_i of a flat block is the top k_ns of its coarse row over
+    J; the Taylor weight of block j is n_j (the step (5) factor L_K), applied
+    to numerator and denominator.
+R9  the low-frequency residual gamma*O_coarse of step (6) is omitted
+    (gamma = 0; the pages never give gamma).
+R10 ties: the lower index wins in every top-k; in the split a lower index
+    counts as sharper.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_EPS_ROUND = 1e-9
+
+
+# ---------------------------------------------------------------- counts (R2)
+def _ceil(x: float) -> int:
+    return int(math.ceil(x - _EPS_ROUND))
+
+
+def _floor(x: float) -> int:
+    return int(math.floor(x + _EPS_ROUND))
+
+
+@dataclass(frozen=True)
+class Plan:
+    L_src: int
+    L_ctx: int
+    b: int
+    N_src: int
+    N_ctx: int
+    N: int
+    k_ctx: int
+    N_kv: int
+    n_flat: int
+    n_sharp: int
+    k_ns: int
+    starts: tuple = field(repr=False)
+    counts: tuple = field(repr=False)
+
+
+def make_plan(L_src: int, L_ctx: int, b: int, alpha_s: float, alpha_f: float,
+              alpha_ns: float) -> Plan:
+    """Block partition and selection counts.
+
+    [RB] "Method steps" step (1) cuts Q/K/V into b-token blocks with padding;
+    step (2) keeps alpha_s * ceil(L_ctx/b) context blocks; step (3) routes a
+    fraction alpha_f of query blocks to the flat path; step (5) computes
+    alpha_ns * (block count) blocks exactly per flat query block.
+    """
+    if L_src < 1 or L_ctx < 0 or b < 1:
+        raise ValueError("need L_src >= 1, L_ctx >= 0, b >= 1")
+    for a in (alpha_s, alpha_f, alpha_ns):
+        if not (0.0 <= a <= 1.0):
+            raise ValueError("ratios must lie in [0, 1]")
+    N_src = -(-L_src // b)
+    N_ctx = -(-L_ctx // b)
+    N = N_src + N_ctx
+    k_ctx = min(N_ctx, _ceil(alpha_s * N_ctx))
+    N_kv = N_src + k_ctx
+    n_flat = min(N, _floor(alpha_f * N))
+    k_ns = min(N_kv, _ceil(alpha_ns * N_kv))
+    starts, counts = [], []
+    # R3: source blocks first, then context blocks; no block straddles the
+    # source/context boundary.
+    for j in range(N_src):
+        starts.append(j * b)
+        counts.append(min(b, L_src - j * b))
+    for j in range(N_ctx):
+        starts.append(L_src + j * b)
+        counts.append(min(b, L_ctx - j * b))
+    return Plan(L_src, L_ctx, b, N_src, N_ctx, N, k_ctx, N_kv, n_flat, N - n_flat,
+                k_ns, tuple(starts), tuple(counts))
+
+
+# ------------------------------------------------------------ selection steps
+def pool(X: np.ndarray, plan: Plan) -> np.ndarray:
+    """Mean of each block's valid tokens ([RB] step (1); R3). X is [L, D]."""
+    X = np.asarray(X, dtype=np.float64)
+    out = np.empty((plan.N, X.shape[1]), dtype=np.float64)
+    for j, (s, n) in enumerate(zip(plan.starts, plan.counts)):
+        out[j] = X[s:s + n].mean(axis=0)
+    return out
+
+
+def coarse_scores(Qc: np.ndarray, Kc: np.ndarray) -> np.ndarray:
+    """S = Qc Kc^T / sqrt(D) at block resolution ([RB] step (1))."""
+    D = Qc.shape[1]
+    return (Qc @ Kc.T) / math.sqrt(D)
+
+
+def context_scores(S: np.ndarray, plan: Plan) -> np.ndarray:
+    """Importance of each context block: its coarse-score column summed over
+    the source query rows ([RB] step (2); R6)."""
+    return S[:plan.N_src, plan.N_src:].sum(axis=0)
+
+
+def top_k(scores: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest scores, lower index first on ties (R10),
+    returned sorted ascending."""
+    scores = np.asarray(scores, dtype=np.float64)
+    order = np.lexsort((np.arange(scores.size), -scores))
+    return np.sort(order[:k]).astype(np.int64)
+
+
+def sharpness(S: np.ndarray, plan: Plan) -> np.ndarray:
+    """M_i = Var(softmax(S[i, source columns])) ([RB] "Core method" and step (3);
+    R4, R5). Population variance over the N_src probabilities."""
+    x = S[:, :plan.N_src]
+    x = x - x.max(axis=1, keepdims=True)
+    e = np.exp(x)
+    p = e / e.sum(axis=1, keepdims=True)
+    return ((p - 1.0 / plan.N_src) ** 2).mean(axis=1)
+
+
+def split(M: np.ndarray, plan: Plan):
+    """Rank blocks by descending sharpness (ties: lower index sharper, R10);
+    the first n_sharp are sharp, the rest flat ([RB] step (3); R1).
+    Both lists are returned sorted ascending."""
+    order = np.lexsort((np.arange(M.size), -M))
+    return np.sort(order[:plan.n_sharp]).astype(np.int64), np.sort(order[plan.n_sharp:]).astype(np.int64)
+
+
+def kept_blocks(ctx_idx: np.ndarray, plan: Plan) -> np.ndarray:
+    """J: every source block plus the selected context blocks ([RB] step (2):
+    source KV concatenated with the gathered context KV), ascending global ids."""
+    return np.concatenate([np.arange(plan.N_src), plan.N_src + np.asarray(ctx_idx, dtype=np.int64)])
+
+
+def exact_sets(S: np.ndarray, J: np.ndarray, flat_idx: np.ndarray, plan: Plan) -> np.ndarray:
+    """E_i for every flat block i: the k_ns blocks of J with the largest coarse
+    score S[i, j] ([RB] step (5); R8, R10). Rows aligned with flat_idx,
+    each sorted ascending (global block ids)."""
+    out = np.empty((len(flat_idx), plan.k_ns), dtype=np.int64)
+    for r, i in enumerate(flat_idx):
+        sel = top_k(S[i, J], plan.k_ns)
+        out[r] = np.sort(J[sel])
+    return out
+
+
+def _topk_gap(scores: np.ndarray, k: int) -> float:
+    """Score of the k-th kept element minus the best dropped one (inf if
+    nothing is dropped or nothing kept)."""
+    if k <= 0 or k >= scores.size:
+        return math.inf
+    s = np.sort(np.asarray(scores, dtype=np.float64))[::-1]
+    return float(s[k - 1] - s[k])
+
+
+# --------------------------------------------------------------- attention
+def _token_range(plan: Plan, j: int) -> np.ndarray:
+    s = plan.starts[j]
+    return np.arange(s, s + plan.counts[j])
+
+
+def _sharp_block_out(Qi, K, V, key_tok, D):
+    """Exact softmax attention of Qi over the listed key tokens
+    ([RB] step (4)), two-pass max-shifted."""
+    logits = (Qi @ K[key_tok].T) / math.sqrt(D)
+    m = logits.max(axis=1, keepdims=True)
+    w = np.exp(logits - m)
+    return (w @ V[key_tok]) / w.sum(axis=1, keepdims=True)
+
+
+def _flat_block_out(Qi, K, V, Kc, Vc, exact_tok, taylor_blocks, n_taylor, D):
+    """[RB] step (5) and the 0th-order Taylor paragraph of "Prerequisites";
+    [TW] section 5: exact terms for the tokens of E_i, and for every other
+    kept block j the term n_j * exp(q . Kc_j / sqrt(D)) added to the
+    denominator and that weight times Vc_j to the numerator (R8)."""
+    scale = 1.0 / math.sqrt(D)
+    le = (Qi @ K[exact_tok].T) * scale
+    lt = (Qi @ Kc[taylor_blocks].T) * scale
+    m = np.full((Qi.shape[0], 1), -np.inf)
+    if le.size:
+        m = np.maximum(m, le.max(axis=1, keepdims=True))
+    if lt.size:
+        m = np.maximum(m, lt.max(axis=1, keepdims=True))
+    we = np.exp(le - m)
+    wt = np.exp(lt - m) * n_taylor[None, :]
+    num = we @ V[exact_tok] + wt @ Vc[taylor_blocks]
+    den = we.sum(axis=1, keepdims=True) + wt.sum(axis=1, keepdims=True)
+    return num / den
+
+
+@dataclass
+class HeadResult:
+    O: np.ndarray               # [L, D] float64 (rows not requested are NaN)
+    ctx_idx: np.ndarray         # [k_ctx] context-local ids, ascending
+    sharp_idx: np.ndarray       # [n_sharp] ascending
+    flat_idx: np.ndarray        # [n_flat] ascending
+    flat_exact_idx: np.ndarray  # [n_flat, k_ns] global ids, rows ascending
+    ctx_score: np.ndarray       # [N_ctx]
+    sharpness: np.ndarray       # [N]
+    S: np.ndarray               # [N, N] coarse scores
+    Qc: np.ndarray
+    Kc: np.ndarray
+    Vc: np.ndarray
+    ctx_gap: float
+    split_gap: float            # on normalised sharpness N_src^2 * M
+    exact_gaps: np.ndarray      # [n_flat]
+
+
+def isa_head(Q, K, V, plan: Plan, selections: dict | None = None, rows=None,
+             compute_output: bool = True) -> HeadResult:
+    """ISA forward for one (batch, head). Q, K, V: [L, D] arrays.
+
+    `selections` may inject ctx_idx / sharp_idx / flat_idx / flat_exact_idx
+    (used when a selection legitimately differs inside a score tie band);
+    the remaining steps then use the injected lists. `rows` restricts the
+    output to the given token indices (others are NaN).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    L, D = Q.shape
+    assert L == plan.L_src + plan.L_ctx
+    sel = selections or {}
+
+    Qc, Kc, Vc = pool(Q, plan), pool(K, plan), pool(V, plan)
+    S = coarse_scores(Qc, Kc)
+    r = context_scores(S, plan)
+    ctx_idx = np.asarray(sel["ctx_idx"], dtype=np.int64) if "ctx_idx" in sel else top_k(r, plan.k_ctx)
+    J = kept_blocks(ctx_idx, plan)
+    M = sharpness(S, plan)
+    if "sharp_idx" in sel:
+        sharp_idx = np.asarray(sel["sharp_idx"], dtype=np.int64)
+        flat_idx = np.asarray(sel["flat_idx"], dtype=np.int64)
+    else:
+        sharp_idx, flat_idx = split(M, plan)
+    E = (np.asarray(sel["flat_exact_idx"], dtype=np.int64) if "flat_exact_idx" in sel
+         else exact_sets(S, J, flat_idx, plan))
+
+    Mn = M * plan.N_src ** 2
+    ordM = np.sort(Mn)[::-1]
+    split_gap = (math.inf if plan.n_flat in (0, plan.N) else
+                 float(ordM[plan.n_sharp - 1] - ordM[plan.n_sharp]))
+    exact_gaps = np.array([_topk_gap(S[i, J], plan.k_ns) for i in flat_idx])
+
+    O = np.full((L, D), np.nan)
+    if compute_output:
+        want = None if rows is None else np.zeros(L, dtype=bool)
+        if want is not None:
+            want[np.asarray(rows, dtype=np.int64)] = True
+        counts = np.asarray(plan.counts, dtype=np.float64)
+        J_tok = np.concatenate([_token_range(plan, j) for j in J])
+        for i in sharp_idx:
+            tok = _token_range(plan, i)
+            if want is not None:
+                tok = tok[want[tok]]
+            if tok.size:
+                O[tok] = _sharp_block_out(Q[tok], K, V, J_tok, D)
+        for rix, i in enumerate(flat_idx):
+            tok = _token_range(plan, i)
+            if want is not None:
+                tok = tok[want[tok]]
+            if not tok.size:
+                continue
+            Ei = E[rix]
+            Ti = np.setdiff1d(J, Ei)
+            exact_tok = (np.concatenate([_token_range(plan, j) for j in Ei])
+                         if Ei.size else np.zeros(0, dtype=np.int64))
+            O[tok] = _flat_block_out(Q[tok], K, V, Kc, Vc, exact_tok, Ti, counts[Ti], D)
+
+    return HeadResult(O, ctx_idx, sharp_idx, flat_idx, E, r, M, S, Qc, Kc, Vc,
+                      _topk_gap(r, plan.k_ctx), split_gap, exact_gaps)
+
+
+def isa_forward(Q, K, V, L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns, heads=None):
+    """ISA over [B, H, L, D] inputs; returns (O [B,H,L,D] float64, results
+    dict keyed by (b_idx, h)). `heads` restricts the work to listed heads."""
+    plan = make_plan(L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns)
+    Bn, Hn, L, D = np.shape(Q)
+    O = np.full((Bn, Hn, L, D), np.nan)
+    res = {}
+    for (bi, h) in (heads if heads is not None else [(x, y) for x in range(Bn) for y in range(Hn)]):
+        hr = isa_head(Q[bi, h], K[bi, h], V[bi, h], plan)
+        O[bi, h] = hr.O
+        res[(bi, h)] = hr
+    return O, res
+
+
+def dense_attention(Q, K, V, rows=None) -> np.ndarray:
+    """softmax(Q K^T / sqrt(D)) V over every token (no mask), fp64; the
+    dense baseline the pages measure against ([RB] "Prerequisites",
+    SDPA and FlashAttention paragraph)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    L, D = Q.shape
+    idx = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.full((L, D), np.nan)
+    for s in range(0, idx.size, 256):
+        t = idx[s:s + 256]
+        out[t] = _sharp_block_out(Q[t], K, V, np.arange(L), D)
+    return out
