@@ -1,0 +1,262 @@
+"""Python binding of the MI355X In-context Sparse Attention (ISA) library.
+
+Argument marshalling only: every step of the method runs in the HIP kernels
+of libisa_mi355x.so (built from csrc/ for gfx950). PyTorch supplies device
+memory and the current HIP stream; the functions below check shapes and
+dtypes, allocate outputs and workspace with torch, and call the C entry
+points of include/isa.h by the same names. There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libisa_mi355x.so")
+
+ISA_OK = 0
+ISA_ERR_ARG = -1
+ISA_ERR_UNSUPPORTED = -2
+ISA_ERR_WORKSPACE = -3
+ISA_ERR_HIP = -4
+
+EXPORTED = ("isa_plan", "isa_pool_coarse", "isa_ctx_topk", "isa_sharpness_split",
+            "isa_sharp_attn", "isa_flat_taylor_attn", "isa_forward", "isa_dense_attn",
+            "isa_strerror")
+
+
+class IsaParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L_src", ctypes.c_int32),
+                ("L_ctx", ctypes.c_int32), ("D", ctypes.c_int32), ("b", ctypes.c_int32),
+                ("alpha_s", ctypes.c_double), ("alpha_f", ctypes.c_double),
+                ("alpha_ns", ctypes.c_double)]
+
+
+class IsaPlan(ctypes.Structure):
+    _fields_ = [("N_src", ctypes.c_int32), ("N_ctx", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("k_ctx", ctypes.c_int32), ("N_kv", ctypes.c_int32), ("n_flat", ctypes.c_int32),
+                ("n_sharp", ctypes.c_int32), ("k_ns", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t), ("scores_bytes", ctypes.c_size_t)]
+
+
+class IsaDebug(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("qc", "kc", "ctx_score", "ctx_idx", "sharpness",
+                                              "sharp_idx", "flat_idx", "flat_exact_idx")]
+
+
+class IsaError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {code} ({strerror(code)})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"ISA HIP library not built: {LIB_PATH} is missing "
+                               "(run __graft_entry__.build() or python -m "
+                               "block_sparse_attention_blockwise_amd._build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        P = ctypes.POINTER(IsaParams)
+        L.isa_plan.argtypes = [P, ctypes.POINTER(IsaPlan)]
+        L.isa_pool_coarse.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.isa_ctx_topk.argtypes = [P, vp, vp, vp, vp, vp]
+        L.isa_sharpness_split.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.isa_sharp_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        L.isa_flat_taylor_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.isa_forward.argtypes = [P, vp, vp, vp, vp, vp, sz, ctypes.POINTER(IsaDebug), vp]
+        L.isa_dense_attn.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.isa_strerror.argtypes = [ctypes.c_int]
+        L.isa_strerror.restype = ctypes.c_char_p
+        for n in EXPORTED[:-1]:
+            getattr(L, n).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().isa_strerror(code).decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != ISA_OK:
+        raise IsaError(fn, rc)
+
+
+@dataclass(frozen=True)
+class Params:
+    B: int
+    H: int
+    L_src: int
+    L_ctx: int
+    D: int
+    b: int = 64
+    alpha_s: float = 0.125
+    alpha_f: float = 0.5
+    alpha_ns: float = 0.0625
+
+    def c(self) -> IsaParams:
+        return IsaParams(self.B, self.H, self.L_src, self.L_ctx, self.D, self.b,
+                         self.alpha_s, self.alpha_f, self.alpha_ns)
+
+
+def plan(p: Params) -> dict:
+    """Counts and workspace sizes (host only; no GPU needed)."""
+    out = IsaPlan()
+    _check("isa_plan", lib().isa_plan(ctypes.byref(p.c()), ctypes.byref(out)))
+    return {f: getattr(out, f) for f, _ in IsaPlan._fields_}
+
+
+# ------------------------------------------------------------- torch glue
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _check_qkv(p: Params, *ts):
+    torch = _torch()
+    shape = (p.B, p.H, p.L_src + p.L_ctx, p.D)
+    for t in ts:
+        if not (t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous()):
+            raise ValueError("Q, K, V must be contiguous bfloat16 tensors on a HIP device")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"expected shape {shape}, got {tuple(t.shape)}")
+        if t.data_ptr() % 16:
+            raise ValueError("tensor base must be 16-byte aligned")
+
+
+def _empty(shape, dtype, device):
+    return _torch().empty(shape, dtype=dtype, device=device)
+
+
+def forward(Q, K, V, p: Params, debug: bool = False, out=None, workspace=None):
+    """ISA forward (steps 1-6). Returns O, or (O, debug dict) when debug=True."""
+    torch = _torch()
+    _check_qkv(p, Q, K, V)
+    pl = plan(p)
+    dev = Q.device
+    O = out if out is not None else torch.empty_like(Q)
+    ws = workspace if workspace is not None else _empty((pl["workspace_bytes"],), torch.uint8, dev)
+    dbg_t, dbg_c = None, None
+    if debug:
+        BH = p.B * p.H
+        dbg_t = {
+            "qc": _empty((p.B, p.H, pl["N"], p.D), torch.float64, dev),
+            "kc": _empty((p.B, p.H, pl["N"], p.D), torch.float64, dev),
+            "ctx_score": _empty((p.B, p.H, pl["N_ctx"]), torch.float64, dev),
+            "ctx_idx": _empty((p.B, p.H, pl["k_ctx"]), torch.int32, dev),
+            "sharpness": _empty((p.B, p.H, pl["N"]), torch.float64, dev),
+            "sharp_idx": _empty((p.B, p.H, pl["n_sharp"]), torch.int32, dev),
+            "flat_idx": _empty((p.B, p.H, pl["n_flat"]), torch.int32, dev),
+            "flat_exact_idx": _empty((p.B, p.H, pl["n_flat"], pl["k_ns"]), torch.int32, dev),
+        }
+        assert BH >= 1
+        dbg_c = IsaDebug(**{k: v.data_ptr() for k, v in dbg_t.items()})
+    rc = lib().isa_forward(ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                           O.data_ptr(), ws.data_ptr(), ws.numel(),
+                           ctypes.byref(dbg_c) if dbg_c is not None else None, _stream(dev))
+    _check("isa_forward", rc)
+    return (O, dbg_t) if debug else O
+
+
+def pool_coarse(Q, K, V, p: Params):
+    """Step (1) pooling: returns (qc, kc fp64, kc_bf16, vc_bf16)."""
+    torch = _torch()
+    _check_qkv(p, Q, K, V)
+    pl = plan(p)
+    dev = Q.device
+    qc = _empty((p.B, p.H, pl["N"], p.D), torch.float64, dev)
+    kc = _empty((p.B, p.H, pl["N"], p.D), torch.float64, dev)
+    kcb = _empty((p.B, p.H, pl["N"], p.D), torch.bfloat16, dev)
+    vcb = _empty((p.B, p.H, pl["N"], p.D), torch.bfloat16, dev)
+    _check("isa_pool_coarse", lib().isa_pool_coarse(ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(),
+                                                    V.data_ptr(), qc.data_ptr(), kc.data_ptr(),
+                                                    kcb.data_ptr(), vcb.data_ptr(), _stream(dev)))
+    return qc, kc, kcb, vcb
+
+
+def ctx_topk(qc, kc, p: Params):
+    """Step (2): returns (ctx_idx int32 global ids, ctx_score fp64)."""
+    torch = _torch()
+    pl = plan(p)
+    dev = qc.device
+    idx = _empty((p.B, p.H, pl["k_ctx"]), torch.int32, dev)
+    score = _empty((p.B, p.H, pl["N_ctx"]), torch.float64, dev)
+    _check("isa_ctx_topk", lib().isa_ctx_topk(ctypes.byref(p.c()), qc.data_ptr(), kc.data_ptr(),
+                                              _ptr(idx) if idx.numel() else None,
+                                              _ptr(score) if score.numel() else None, _stream(dev)))
+    return idx, score
+
+
+def sharpness_split(qc, kc, ctx_idx, p: Params):
+    """Steps (1) coarse rows, (3), (5) selection: returns
+    (sharpness, sharp_idx, flat_idx, flat_exact_idx)."""
+    torch = _torch()
+    pl = plan(p)
+    dev = qc.device
+    sharp = _empty((p.B, p.H, pl["N"]), torch.float64, dev)
+    si = _empty((p.B, p.H, pl["n_sharp"]), torch.int32, dev)
+    fi = _empty((p.B, p.H, pl["n_flat"]), torch.int32, dev)
+    ei = _empty((p.B, p.H, pl["n_flat"], pl["k_ns"]), torch.int32, dev)
+    ws = _empty((pl["scores_bytes"],), torch.uint8, dev)
+    nz = lambda t: t.data_ptr() if t.numel() else None
+    _check("isa_sharpness_split", lib().isa_sharpness_split(
+        ctypes.byref(p.c()), qc.data_ptr(), kc.data_ptr(), nz(ctx_idx), sharp.data_ptr(),
+        nz(si), nz(fi), nz(ei), ws.data_ptr(), ws.numel(), _stream(dev)))
+    return sharp, si, fi, ei
+
+
+def sharp_attn(Q, K, V, ctx_idx, sharp_idx, p: Params, out=None):
+    """Step (4): writes the sharp rows of `out` (allocated zero if None)."""
+    torch = _torch()
+    _check_qkv(p, Q, K, V)
+    O = out if out is not None else torch.zeros_like(Q)
+    nz = lambda t: t.data_ptr() if t.numel() else None
+    _check("isa_sharp_attn", lib().isa_sharp_attn(ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(),
+                                                  V.data_ptr(), nz(ctx_idx), nz(sharp_idx),
+                                                  O.data_ptr(), _stream(Q.device)))
+    return O
+
+
+def flat_taylor_attn(Q, K, V, kc_bf16, vc_bf16, ctx_idx, flat_idx, flat_exact_idx, p: Params,
+                     out=None):
+    """Step (5): writes the flat rows of `out` (allocated zero if None)."""
+    torch = _torch()
+    _check_qkv(p, Q, K, V)
+    O = out if out is not None else torch.zeros_like(Q)
+    nz = lambda t: t.data_ptr() if t.numel() else None
+    _check("isa_flat_taylor_attn", lib().isa_flat_taylor_attn(
+        ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(), V.data_ptr(), kc_bf16.data_ptr(),
+        vc_bf16.data_ptr(), nz(ctx_idx), nz(flat_idx), nz(flat_exact_idx), O.data_ptr(),
+        _stream(Q.device)))
+    return O
+
+
+def dense_attn(Q, K, V, out=None):
+    """Dense softmax attention baseline over all tokens, [B,H,L,D] bf16."""
+    torch = _torch()
+    B, H, L, D = Q.shape
+    for t in (Q, K, V):
+        if not (t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous()) or t.shape != Q.shape:
+            raise ValueError("Q, K, V must be contiguous bfloat16 [B,H,L,D] tensors on a HIP device")
+    O = out if out is not None else torch.empty_like(Q)
+    _check("isa_dense_attn", lib().isa_dense_attn(B, H, L, D, Q.data_ptr(), K.data_ptr(),
+                                                  V.data_ptr(), O.data_ptr(), _stream(Q.device)))
+    return O

@@ -1,0 +1,252 @@
+// Host side of the ISA library: argument validation, the counts of the
+// method's steps, workspace layout and the extern "C" entry points.
+//
+// The counts follow the method steps of In-context Sparse Attention as given
+// in the paper.rainbus.top summary of arXiv 2605.04569, section "Method
+// steps": step (1) cuts the sequence into b-token blocks, step (2) keeps
+// alpha_s times the number of context blocks, step (3) sends a fraction
+// alpha_f of the query blocks to the flat path, step (5) computes
+// alpha_ns times the kept block count exactly per flat block. Where a
+// product is fractional the count is rounded toward more exact work.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "isa_internal.h"
+
+namespace {
+
+constexpr double kRoundTol = 1e-9;
+
+int ceil_count(double x) { return (int)std::ceil(x - kRoundTol); }
+int floor_count(double x) { return (int)std::floor(x + kRoundTol); }
+
+bool ratio_ok(double a) { return !std::isnan(a) && a >= 0.0 && a <= 1.0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t qc, kc, kcb, vcb, ctx_idx, ctx_score, sharp, sharp_idx, flat_idx, exact, srows, total;
+};
+
+Layout make_layout(const IsaShape& s) {
+  const size_t bh = (size_t)s.B * s.H;
+  const size_t nd = bh * s.N * s.D;
+  auto at_least1 = [](size_t x) { return x ? x : (size_t)1; };
+  Layout l;
+  size_t o = 0;
+  l.qc = o;        o = align256(o + nd * 8);
+  l.kc = o;        o = align256(o + nd * 8);
+  l.kcb = o;       o = align256(o + nd * 2);
+  l.vcb = o;       o = align256(o + nd * 2);
+  l.ctx_idx = o;   o = align256(o + at_least1(bh * s.k_ctx) * 4);
+  l.ctx_score = o; o = align256(o + at_least1(bh * s.N_ctx) * 8);
+  l.sharp = o;     o = align256(o + bh * s.N * 8);
+  l.sharp_idx = o; o = align256(o + at_least1(bh * s.n_sharp) * 4);
+  l.flat_idx = o;  o = align256(o + at_least1(bh * s.n_flat) * 4);
+  l.exact = o;     o = align256(o + at_least1(bh * s.n_flat * (size_t)s.k_ns) * 4);
+  l.srows = o;     o = align256(o + bh * s.N * (size_t)s.N_kv * 8);
+  l.total = o;
+  return l;
+}
+
+// Workspace of isa_sharpness_split: the coarse rows S[i, J] of every query
+// block, then room for the sharpness values when the caller passes none.
+size_t scores_rows_bytes(const IsaShape& s) {
+  return align256((size_t)s.B * s.H * s.N * (size_t)s.N_kv * 8);
+}
+size_t scores_bytes(const IsaShape& s) {
+  return scores_rows_bytes(s) + align256((size_t)s.B * s.H * s.N * 8);
+}
+
+// Validates the parameters and derives every count. Makes no HIP call.
+int make_shape(const isa_params_t* p, IsaShape* s) {
+  if (!p || !s) return ISA_ERR_ARG;
+  if (p->B < 1 || p->H < 1 || p->L_src < 1 || p->L_ctx < 0 || p->D < 1 || p->b < 1)
+    return ISA_ERR_ARG;
+  if (!ratio_ok(p->alpha_s) || !ratio_ok(p->alpha_f) || !ratio_ok(p->alpha_ns)) return ISA_ERR_ARG;
+  if (p->D != 64 && p->D != 128) return ISA_ERR_UNSUPPORTED;
+  if (p->b != 32 && p->b != 64) return ISA_ERR_UNSUPPORTED;
+  const int64_t N_src = ((int64_t)p->L_src + p->b - 1) / p->b;
+  const int64_t N_ctx = ((int64_t)p->L_ctx + p->b - 1) / p->b;
+  if (N_src > ISA_MAX_SEG_BLOCKS || N_ctx > ISA_MAX_SEG_BLOCKS) return ISA_ERR_UNSUPPORTED;
+  IsaShape r;
+  r.B = p->B; r.H = p->H; r.L_src = p->L_src; r.L_ctx = p->L_ctx;
+  r.L = p->L_src + p->L_ctx; r.D = p->D; r.b = p->b;
+  r.N_src = (int)N_src; r.N_ctx = (int)N_ctx; r.N = r.N_src + r.N_ctx;
+  r.k_ctx = ceil_count(p->alpha_s * r.N_ctx);
+  if (r.k_ctx > r.N_ctx) r.k_ctx = r.N_ctx;
+  r.N_kv = r.N_src + r.k_ctx;
+  if (r.N_kv > ISA_MAX_NKV) return ISA_ERR_UNSUPPORTED;
+  r.n_flat = floor_count(p->alpha_f * r.N);
+  if (r.n_flat > r.N) r.n_flat = r.N;
+  r.n_sharp = r.N - r.n_flat;
+  r.k_ns = ceil_count(p->alpha_ns * r.N_kv);
+  if (r.k_ns > r.N_kv) r.k_ns = r.N_kv;
+  *s = r;
+  return ISA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ISA_OK : ISA_ERR_HIP; }
+
+hipStream_t as_stream(void* st) { return reinterpret_cast<hipStream_t>(st); }
+
+}  // namespace
+
+extern "C" {
+
+int isa_plan(const isa_params_t* p, isa_plan_t* out) {
+  if (!out) return ISA_ERR_ARG;
+  IsaShape s;
+  int rc = make_shape(p, &s);
+  if (rc != ISA_OK) return rc;
+  out->N_src = s.N_src; out->N_ctx = s.N_ctx; out->N = s.N; out->k_ctx = s.k_ctx;
+  out->N_kv = s.N_kv; out->n_flat = s.n_flat; out->n_sharp = s.n_sharp; out->k_ns = s.k_ns;
+  out->workspace_bytes = make_layout(s).total;
+  out->scores_bytes = scores_bytes(s);
+  return ISA_OK;
+}
+
+int isa_pool_coarse(const isa_params_t* p, const void* Q, const void* K, const void* V,
+                    double* qc, double* kc, void* kc_bf16, void* vc_bf16, void* stream) {
+  IsaShape s;
+  int rc = make_shape(p, &s);
+  if (rc != ISA_OK) return rc;
+  if (!Q || !K || !V || !qc || !kc) return ISA_ERR_ARG;
+  return hip_status(isa_launch_pool(s, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V,
+                                    qc, kc, (uint16_t*)kc_bf16, (uint16_t*)vc_bf16,
+                                    as_stream(stream)));
+}
+
+int isa_ctx_topk(const isa_params_t* p, const double* qc, const double* kc, int32_t* ctx_idx,
+                 double* ctx_score, void* stream) {
+  IsaShape s;
+  int rc = make_shape(p, &s);
+  if (rc != ISA_OK) return rc;
+  if (!qc || !kc || (!ctx_idx && s.k_ctx > 0)) return ISA_ERR_ARG;
+  return hip_status(isa_launch_ctx_topk(s, qc, kc, ctx_idx, ctx_score, as_stream(stream)));
+}
+
+int isa_sharpness_split(const isa_params_t* p, const double* qc, const double* kc,
+                        const int32_t* ctx_idx, double* sharpness, int32_t* sharp_idx,
+                        int32_t* flat_idx, int32_t* flat_exact_idx, void* ws, size_t ws_bytes,
+                        void* stream) {
+  IsaShape s;
+  int rc = make_shape(p, &s);
+  if (rc != ISA_OK) return rc;
+  if (!qc || !kc || (!ctx_idx && s.k_ctx > 0) || (!sharp_idx && s.n_sharp > 0) ||
+      (!flat_idx && s.n_flat > 0) || (!flat_exact_idx && s.n_flat > 0 && s.k_ns > 0) || !ws)
+    return ISA_ERR_ARG;
+  if (ws_bytes < scores_bytes(s)) return ISA_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  double* srows = (double*)ws;
+  double* sharp = sharpness ? sharpness : (double*)((char*)ws + scores_rows_bytes(s));
+  hipError_t e = isa_launch_coarse_rows(s, qc, kc, ctx_idx, srows, st);
+  if (e == hipSuccess) e = isa_launch_sharpness(s, srows, sharp, st);
+  if (e == hipSuccess) e = isa_launch_split(s, sharp, sharp_idx, flat_idx, st);
+  if (e == hipSuccess) e = isa_launch_flat_topk(s, srows, ctx_idx, flat_idx, flat_exact_idx, st);
+  return hip_status(e);
+}
+
+int isa_sharp_attn(const isa_params_t* p, const void* Q, const void* K, const void* V,
+                   const int32_t* ctx_idx, const int32_t* sharp_idx, void* O, void* stream) {
+  IsaShape s;
+  int rc = make_shape(p, &s);
+  if (rc != ISA_OK) return rc;
+  if (!Q || !K || !V || !O || (!ctx_idx && s.k_ctx > 0) || (!sharp_idx && s.n_sharp > 0))
+    return ISA_ERR_ARG;
+  return hip_status(isa_launch_sharp_attn(s, (const uint16_t*)Q, (const uint16_t*)K,
+                                          (const uint16_t*)V, ctx_idx, sharp_idx, (uint16_t*)O,
+                                          as_stream(stream)));
+}
+
+int isa_flat_taylor_attn(const isa_params_t* p, const void* Q, const void* K, const void* V,
+                         const void* kc_bf16, const void* vc_bf16, const int32_t* ctx_idx,
+                         const int32_t* flat_idx, const int32_t* flat_exact_idx, void* O,
+                         void* stream) {
+  IsaShape s;
+  int rc = make_shape(p, &s);
+  if (rc != ISA_OK) return rc;
+  if (!Q || !K || !V || !O || !kc_bf16 || !vc_bf16 || (!ctx_idx && s.k_ctx > 0) ||
+      (!flat_idx && s.n_flat > 0) || (!flat_exact_idx && s.n_flat > 0 && s.k_ns > 0))
+    return ISA_ERR_ARG;
+  return hip_status(isa_launch_flat_attn(s, (const uint16_t*)Q, (const uint16_t*)K,
+                                         (const uint16_t*)V, (const uint16_t*)kc_bf16,
+                                         (const uint16_t*)vc_bf16, ctx_idx, flat_idx,
+                                         flat_exact_idx, (uint16_t*)O, as_stream(stream)));
+}
+
+int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void* V, void* O,
+                void* ws, size_t ws_bytes, const isa_debug_t* dbg, void* stream) {
+  IsaShape s;
+  int rc = make_shape(p, &s);
+  if (rc != ISA_OK) return rc;
+  if (!Q || !K || !V || !O || !ws) return ISA_ERR_ARG;
+  const Layout l = make_layout(s);
+  if (ws_bytes < l.total) return ISA_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  char* w = (char*)ws;
+  double* qc = (double*)(w + l.qc);
+  double* kc = (double*)(w + l.kc);
+  uint16_t* kcb = (uint16_t*)(w + l.kcb);
+  uint16_t* vcb = (uint16_t*)(w + l.vcb);
+  int32_t* ctx_idx = (int32_t*)(w + l.ctx_idx);
+  double* ctx_score = (double*)(w + l.ctx_score);
+  double* sharp = (double*)(w + l.sharp);
+  int32_t* sharp_idx = (int32_t*)(w + l.sharp_idx);
+  int32_t* flat_idx = (int32_t*)(w + l.flat_idx);
+  int32_t* exact = (int32_t*)(w + l.exact);
+  double* srows = (double*)(w + l.srows);
+  const uint16_t* q = (const uint16_t*)Q;
+  const uint16_t* k = (const uint16_t*)K;
+  const uint16_t* v = (const uint16_t*)V;
+
+  hipError_t e = isa_launch_pool(s, q, k, v, qc, kc, kcb, vcb, st);
+  if (e == hipSuccess) e = isa_launch_ctx_topk(s, qc, kc, ctx_idx, ctx_score, st);
+  if (e == hipSuccess) e = isa_launch_coarse_rows(s, qc, kc, ctx_idx, srows, st);
+  if (e == hipSuccess) e = isa_launch_sharpness(s, srows, sharp, st);
+  if (e == hipSuccess) e = isa_launch_split(s, sharp, sharp_idx, flat_idx, st);
+  if (e == hipSuccess) e = isa_launch_flat_topk(s, srows, ctx_idx, flat_idx, exact, st);
+  if (e == hipSuccess) e = isa_launch_sharp_attn(s, q, k, v, ctx_idx, sharp_idx, (uint16_t*)O, st);
+  if (e == hipSuccess)
+    e = isa_launch_flat_attn(s, q, k, v, kcb, vcb, ctx_idx, flat_idx, exact, (uint16_t*)O, st);
+  if (e == hipSuccess && dbg) {
+    const size_t bh = (size_t)s.B * s.H;
+    struct { void* dst; const void* src; size_t n; } cp[] = {
+        {dbg->qc, qc, bh * s.N * s.D * 8},
+        {dbg->kc, kc, bh * s.N * s.D * 8},
+        {dbg->ctx_score, ctx_score, bh * s.N_ctx * 8},
+        {dbg->ctx_idx, ctx_idx, bh * s.k_ctx * 4},
+        {dbg->sharpness, sharp, bh * s.N * 8},
+        {dbg->sharp_idx, sharp_idx, bh * s.n_sharp * 4},
+        {dbg->flat_idx, flat_idx, bh * s.n_flat * 4},
+        {dbg->flat_exact_idx, exact, bh * s.n_flat * (size_t)s.k_ns * 4},
+    };
+    for (auto& c : cp) {
+      if (e != hipSuccess) break;
+      if (c.dst && c.n) e = hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, st);
+    }
+  }
+  return hip_status(e);
+}
+
+int isa_dense_attn(int32_t B, int32_t H, int32_t L, int32_t D, const void* Q, const void* K,
+                   const void* V, void* O, void* stream) {
+  if (B < 1 || H < 1 || L < 1 || D < 1 || !Q || !K || !V || !O) return ISA_ERR_ARG;
+  if (D != 64 && D != 128) return ISA_ERR_UNSUPPORTED;
+  return hip_status(isa_launch_dense_attn(B, H, L, D, (const uint16_t*)Q, (const uint16_t*)K,
+                                          (const uint16_t*)V, (uint16_t*)O, as_stream(stream)));
+}
+
+const char* isa_strerror(int status) {
+  switch (status) {
+    case ISA_OK: return "ok";
+    case ISA_ERR_ARG: return "invalid argument (null pointer, bad shape or ratio)";
+    case ISA_ERR_UNSUPPORTED: return "unsupported configuration (D, b or block counts outside the limits)";
+    case ISA_ERR_WORKSPACE: return "workspace too small";
+    case ISA_ERR_HIP: return "HIP launch or copy failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,482 @@
+// Attention kernels of In-context Sparse Attention on gfx950.
+//
+// One tile engine serves three callers:
+//   * sharp path (paper.rainbus.top summary of arXiv 2605.04569, "Method
+//     steps", step (4)): exact softmax attention of the sharp query blocks
+//     over the tokens of the kept blocks J, read through block indices (no
+//     gather copy);
+//   * flat path (same section, step (5), and the 0th-order Taylor paragraph
+//     of "Prerequisites"): exact attention over the tokens of E_i, then the
+//     pooled keys of J \ E_i, each with additive logit log(n_j) so that block
+//     j contributes n_j * exp(q.Kc_j / sqrt(D)) to the denominator and that
+//     weight times Vc_j to the numerator; both kinds of key tiles feed one
+//     online-softmax accumulator (running max, sum, output);
+//   * dense baseline: every token attends every token.
+//
+// Work decomposition (CDNA4, wave64):
+//   * a workgroup owns ROWS query rows; each wave owns 16*QT rows;
+//   * key tiles of 64 keys are staged in LDS, double buffered: global loads
+//     of tile t+1 are in flight while tile t is consumed;
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q
+//     fragments kept in registers); lane (g = lane/16, c = lane%16) then holds
+//     4 keys of each 16-key sub-tile for query c, so the row max and row sum
+//     need only two cross-lane swaps (v_permlane16/32_swap);
+//   * the probabilities, rounded to bf16, are already in the B-operand layout
+//     of O^T += V^T P^T; the V^T operand comes from row-major V in LDS through
+//     the transposing LDS read ds_read_b64_tr_b16;
+//   * O^T accumulates in fp32 with one query per lane, so the online-softmax
+//     rescale is a per-lane scalar multiply, skipped unless some row max grew
+//     by more than 2^8 (the running max is a reference, not the exact max);
+//   * exp is exp2 with log2(e)/sqrt(D) folded into one multiply.
+// K rows are padded to 2D+16 bytes and V rows to 2D+32 bytes in LDS so the
+// 16-byte K reads and the 8-byte transposing V reads are bank-conflict free.
+#include "isa_internal.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef short short4_t __attribute__((__vector_size__(8)));
+typedef float float4_t __attribute__((__vector_size__(16)));
+
+enum : int { kDense = 0, kSharp = 1, kFlat = 2 };
+
+constexpr int kKeyTile = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;   // log2 units
+constexpr float kMinusBig = -1.0e30f;
+
+struct AttnArgs {
+  IsaShape s;                // dense: B, H, L, D only
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  uint16_t* O;
+  const uint16_t* kcb;       // flat: bf16 block means of K  [B,H,N,D]
+  const uint16_t* vcb;       // flat: bf16 block means of V  [B,H,N,D]
+  const int32_t* ctx_idx;    // [B,H,k_ctx] kept context blocks (global ids)
+  const int32_t* qlist;      // sharp_idx or flat_idx [B,H,n_q]
+  const int32_t* exact;      // flat: [B,H,n_flat,k_ns]
+  int n_q;
+  int ntiles_exact;
+  int ntiles;
+};
+
+__device__ inline float xor16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline short4_t lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(p));
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Global block id of position q of the kept list J (source blocks, then the
+// kept context blocks); -1 when out of range.
+__device__ inline int kept_id(const IsaShape& s, const int32_t* ctx_row, int q) {
+  if (q < s.N_src) return q;
+  const int j = ctx_row[q - s.N_src];
+  return (j >= s.N_src && j < s.N) ? j : -1;
+}
+
+__device__ inline bool block_is_partial(const IsaShape& s, int j) {
+  int st, n;
+  isa_block_range(s, j, st, n);
+  return n < s.b;
+}
+
+template <int D, int MODE, int QT, int NWAVES>
+__global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
+  constexpr int NT = NWAVES * 64;
+  constexpr int KSTR = 2 * D + 16;
+  constexpr int VSTR = 2 * D + 32;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int CH = kKeyTile * CPR / NT;    // chunks per thread per tensor
+  constexpr int ROWS_W = 16 * QT;
+  constexpr int ROWS = NWAVES * ROWS_W;
+  constexpr int KK = D / 32;
+  constexpr int DT = D / 16;
+  static_assert(CH >= 1 && (kKeyTile * CPR) % NT == 0, "tile split");
+  static_assert(NT % CPR == 0, "chunk column must be fixed per thread");
+
+  __shared__ __attribute__((aligned(16))) char k_lds[2][kKeyTile * KSTR];
+  __shared__ __attribute__((aligned(16))) char v_lds[2][kKeyTile * VSTR];
+  __shared__ float bias_lds[2][kKeyTile];
+  __shared__ unsigned char emask[MODE == kFlat ? ISA_MAX_NKV : 1];
+
+  const IsaShape& s = a.s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y;
+  const size_t head = (size_t)bh * s.L;     // first token row of this (batch, head)
+  const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
+  const int b = s.b;
+
+  // ---- query rows owned by this lane
+  int qtok[QT];
+  bool qval[QT];
+  int flat_block = -1;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int lr = wave * ROWS_W + 16 * qt + c16;
+    qval[qt] = false;
+    qtok[qt] = 0;
+    if (MODE == kDense) {
+      const int tok = blockIdx.x * ROWS + lr;
+      qval[qt] = tok < s.L;
+      qtok[qt] = tok;
+    } else {
+      const int e = (MODE == kSharp) ? blockIdx.x * (ROWS / b) + lr / b : blockIdx.x;
+      const int o = (MODE == kSharp) ? lr % b : lr;
+      if (e < a.n_q) {
+        const int j = a.qlist[(size_t)bh * a.n_q + e];
+        if (j >= 0 && j < s.N) {
+          int st, n;
+          isa_block_range(s, j, st, n);
+          qval[qt] = o < n;
+          qtok[qt] = st + o;
+          if (MODE == kFlat) flat_block = j;
+        }
+      }
+    }
+  }
+  (void)flat_block;
+
+  bf16x8_t qf[QT][KK];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (qval[qt]) w = *reinterpret_cast<const uint4*>(a.Q + (head + qtok[qt]) * D + 32 * kk + 8 * g);
+      qf[qt][kk] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+
+  const int32_t* exact_row = nullptr;
+  if (MODE == kFlat) {
+    exact_row = a.exact + ((size_t)bh * s.n_flat + blockIdx.x) * s.k_ns;
+    for (int p = tid; p < s.N_kv; p += NT) emask[p] = 0;
+    __syncthreads();
+    for (int q = tid; q < s.k_ns; q += NT) {
+      const int j = exact_row[q];
+      int p = -1;
+      if (j >= 0 && j < s.N_src) {
+        p = j;
+      } else if (j >= s.N_src && j < s.N) {
+        int lo = 0, hi = s.k_ctx;     // lower bound of j in the ascending kept list
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (ctx_row[mid] < j) lo = mid + 1; else hi = mid;
+        }
+        if (lo < s.k_ctx && ctx_row[lo] == j) p = s.N_src + lo;
+      }
+      if (p >= 0) emask[p] = 1;
+    }
+    __syncthreads();
+  }
+
+  // ---- key tile source: row pointers (null = padding) and additive logit
+  const int per = kKeyTile / b;   // blocks per key tile (exact tiles)
+  auto slot_src = [&](int t, int slot, const uint16_t*& kp, const uint16_t*& vp, float& bias) {
+    kp = nullptr;
+    vp = nullptr;
+    bias = -INFINITY;
+    if (MODE == kDense) {
+      const int tok = t * kKeyTile + slot;
+      if (tok < s.L) {
+        kp = a.K + (head + tok) * D;
+        vp = a.V + (head + tok) * D;
+        bias = 0.0f;
+      }
+      return;
+    }
+    if (MODE == kFlat && t >= a.ntiles_exact) {
+      const int p = (t - a.ntiles_exact) * kKeyTile + slot;
+      if (p < s.N_kv && !emask[p]) {
+        const int j = kept_id(s, ctx_row, p);
+        if (j >= 0) {
+          int st, n;
+          isa_block_range(s, j, st, n);
+          const size_t row = ((size_t)bh * s.N + j) * D;
+          kp = a.kcb + row;
+          vp = a.vcb + row;
+          bias = __log2f((float)n);
+        }
+      }
+      return;
+    }
+    const int q = t * per + slot / b, o = slot % b;
+    int j = -1;
+    if (MODE == kSharp) {
+      if (q < s.N_kv) j = kept_id(s, ctx_row, q);
+    } else {
+      if (q < s.k_ns) {
+        j = exact_row[q];
+        if (j < 0 || j >= s.N) j = -1;
+      }
+    }
+    if (j >= 0) {
+      int st, n;
+      isa_block_range(s, j, st, n);
+      if (o < n) {
+        kp = a.K + (head + st + o) * D;
+        vp = a.V + (head + st + o) * D;
+        bias = 0.0f;
+      }
+    }
+  };
+
+  // Whether tile t carries any non-zero additive logit (uniform).
+  auto tile_has_bias = [&](int t) -> bool {
+    if (MODE == kDense) return (t + 1) * kKeyTile > s.L;
+    if (MODE == kFlat && t >= a.ntiles_exact) return true;
+    for (int u = 0; u < per; ++u) {
+      const int q = t * per + u;
+      int j;
+      if (MODE == kSharp) j = q < s.N_kv ? kept_id(s, ctx_row, q) : -1;
+      else j = q < s.k_ns ? exact_row[q] : -1;
+      if (j < 0 || j >= s.N || block_is_partial(s, j)) return true;
+    }
+    return false;
+  };
+
+  uint4 kr[CH], vr[CH];
+  float br[CH];
+  const int c8 = tid % CPR;
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int slot = (tid + i * NT) / CPR;
+      const uint16_t *kp, *vp;
+      float bias;
+      slot_src(t, slot, kp, vp, bias);
+      br[i] = bias;
+      if (kp) {
+        kr[i] = *reinterpret_cast<const uint4*>(kp + c8 * 8);
+        vr[i] = *reinterpret_cast<const uint4*>(vp + c8 * 8);
+      } else {
+        kr[i] = make_uint4(0, 0, 0, 0);
+        vr[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int slot = (tid + i * NT) / CPR;
+      *reinterpret_cast<uint4*>(&k_lds[buf][slot * KSTR + c8 * 16]) = kr[i];
+      *reinterpret_cast<uint4*>(&v_lds[buf][slot * VSTR + c8 * 16]) = vr[i];
+      if (c8 == 0) bias_lds[buf][slot] = br[i];
+    }
+  };
+
+  const float cscale = kLog2e / sqrtf((float)D);
+  float m[QT], lsum[QT];
+  float4_t oacc[QT][DT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m[qt] = kMinusBig;
+    lsum[qt] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  load_tile(0);
+  store_tile(0);
+  const int ntiles = a.ntiles;
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(t + 1);
+    const bool has_bias = tile_has_bias(t);
+    __syncthreads();
+    const char* kb = k_lds[buf];
+    const char* vb = v_lds[buf];
+
+    float4_t sacc[QT][4];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) sacc[qt][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kb + (16 * mt + c16) * KSTR + (32 * kk + 8 * g) * 2);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          sacc[qt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qt][kk], sacc[qt][mt], 0, 0, 0);
+      }
+    }
+
+    bf16x8_t pb[QT][2];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float x[16];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[4 * mt + j] = sacc[qt][mt][j] * cscale;
+      if (has_bias) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[4 * mt + j] += bias_lds[buf][16 * mt + 4 * g + j];
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+      mx = xor16_max(mx);
+      mx = xor32_max(mx);
+      if (__ballot(mx > m[qt] + kRescaleSlack)) {
+        const float mn = fmaxf(m[qt], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
+        lsum[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= alpha;
+        m[qt] = mn;
+      }
+      float ps = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[i] = __builtin_amdgcn_exp2f(x[i] - m[qt]);
+        ps += x[i];
+      }
+      lsum[qt] += ps;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        uint4 w;
+        w.x = pack_bf16x2(x[8 * kc + 0], x[8 * kc + 1]);
+        w.y = pack_bf16x2(x[8 * kc + 2], x[8 * kc + 3]);
+        w.z = pack_bf16x2(x[8 * kc + 4], x[8 * kc + 5]);
+        w.w = pack_bf16x2(x[8 * kc + 6], x[8 * kc + 7]);
+        pb[qt][kc] = __builtin_bit_cast(bf16x8_t, w);
+      }
+    }
+
+    const int tr_row = 4 * g + (c16 >> 2);
+    const int tr_col = 4 * (c16 & 3);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const short4_t lo = lds_read_tr(vb + (32 * kc + tr_row) * VSTR + (16 * dt + tr_col) * 2);
+        const short4_t hi = lds_read_tr(vb + (32 * kc + 16 + tr_row) * VSTR + (16 * dt + tr_col) * 2);
+        const bf16x8_t va = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qt][kc], oacc[qt][dt], 0, 0, 0);
+      }
+    }
+
+    if (more) store_tile(buf ^ 1);
+  }
+
+  // ---- normalise and write the owned rows
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float lt = xor16_sum(lsum[qt]);
+    lt = xor32_sum(lt);
+    if (!qval[qt]) continue;
+    const float inv = 1.0f / lt;
+    uint16_t* orow = a.O + (head + qtok[qt]) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      uint2 w;
+      w.x = pack_bf16x2(oacc[qt][dt][0] * inv, oacc[qt][dt][1] * inv);
+      w.y = pack_bf16x2(oacc[qt][dt][2] * inv, oacc[qt][dt][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = w;
+    }
+  }
+}
+
+template <int D, int MODE, int QT, int NWAVES>
+hipError_t launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  attn_kernel<D, MODE, QT, NWAVES><<<grid, NWAVES * 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+AttnArgs base_args(const IsaShape& s, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                   uint16_t* O) {
+  AttnArgs a{};
+  a.s = s;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  return a;
+}
+
+}  // namespace
+
+hipError_t isa_launch_sharp_attn(const IsaShape& s, const uint16_t* Q, const uint16_t* K,
+                                 const uint16_t* V, const int32_t* ctx_idx,
+                                 const int32_t* sharp_idx, uint16_t* O, hipStream_t st) {
+  if (s.n_sharp == 0) return hipSuccess;
+  AttnArgs a = base_args(s, Q, K, V, O);
+  a.ctx_idx = ctx_idx;
+  a.qlist = sharp_idx;
+  a.n_q = s.n_sharp;
+  a.ntiles = (s.N_kv * s.b + kKeyTile - 1) / kKeyTile;
+  const int rows = 8 * 32;
+  const int blocks_per_wg = rows / s.b;
+  dim3 grid((s.n_sharp + blocks_per_wg - 1) / blocks_per_wg, s.B * s.H);
+  return s.D == 128 ? launch<128, kSharp, 2, 8>(a, grid, st) : launch<64, kSharp, 2, 8>(a, grid, st);
+}
+
+hipError_t isa_launch_flat_attn(const IsaShape& s, const uint16_t* Q, const uint16_t* K,
+                                const uint16_t* V, const uint16_t* kc_bf16,
+                                const uint16_t* vc_bf16, const int32_t* ctx_idx,
+                                const int32_t* flat_idx, const int32_t* flat_exact_idx,
+                                uint16_t* O, hipStream_t st) {
+  if (s.n_flat == 0) return hipSuccess;
+  AttnArgs a = base_args(s, Q, K, V, O);
+  a.kcb = kc_bf16;
+  a.vcb = vc_bf16;
+  a.ctx_idx = ctx_idx;
+  a.qlist = flat_idx;
+  a.exact = flat_exact_idx;
+  a.n_q = s.n_flat;
+  a.ntiles_exact = (s.k_ns * s.b + kKeyTile - 1) / kKeyTile;
+  const int pooled = s.k_ns < s.N_kv ? (s.N_kv + kKeyTile - 1) / kKeyTile : 0;
+  a.ntiles = a.ntiles_exact + pooled;
+  dim3 grid(s.n_flat, s.B * s.H);
+  if (s.b == 64)
+    return s.D == 128 ? launch<128, kFlat, 1, 4>(a, grid, st) : launch<64, kFlat, 1, 4>(a, grid, st);
+  return s.D == 128 ? launch<128, kFlat, 1, 2>(a, grid, st) : launch<64, kFlat, 1, 2>(a, grid, st);
+}
+
+hipError_t isa_launch_dense_attn(int B, int H, int L, int D, const uint16_t* Q,
+                                 const uint16_t* K, const uint16_t* V, uint16_t* O,
+                                 hipStream_t st) {
+  IsaShape s{};
+  s.B = B;
+  s.H = H;
+  s.L = L;
+  s.L_src = L;
+  s.D = D;
+  s.b = kKeyTile;
+  AttnArgs a = base_args(s, Q, K, V, O);
+  a.ntiles = (L + kKeyTile - 1) / kKeyTile;
+  dim3 grid((L + 255) / 256, B * H);
+  return D == 128 ? launch<128, kDense, 2, 8>(a, grid, st) : launch<64, kDense, 2, 8>(a, grid, st);
+}

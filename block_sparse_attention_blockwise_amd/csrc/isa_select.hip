@@ -1,0 +1,348 @@
+// Selection path of In-context Sparse Attention, all scores in fp64.
+//
+// Steps, as given in the paper.rainbus.top summary of arXiv 2605.04569,
+// section "Method steps":
+//   step (2): context importance = coarse scores of the source query blocks
+//             summed per context key block; keep the top alpha_s fraction;
+//   step (1)+(3): coarse rows S[i, J] = Qc_i . Kc_j / sqrt(D) over the kept
+//             blocks J; sharpness M_i = variance of the softmax of S[i, :]
+//             restricted to the source key blocks; the least sharp alpha_f
+//             fraction of query blocks is "flat";
+//   step (5): per flat block, the exact set E_i = top alpha_ns fraction of J
+//             by coarse score.
+// Every top-k prefers the lower index among equal scores, and every output
+// list is ascending. Selection uses an exact radix bisection on the ordered
+// bit pattern of the fp64 scores (no floating-point comparison tolerance),
+// then resolves ties at the threshold by index order with a block-wide scan.
+#include "isa_internal.h"
+
+namespace {
+
+// Maps an fp64 value to an unsigned key with the same order (no NaN input).
+__device__ inline unsigned long long order_key(double x) {
+  unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+__device__ inline int wave_sum_int(int x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ inline double wave_sum_f64(double x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ inline double wave_max_f64(double x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x = fmax(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+// Sum of one int per thread over the workgroup; every thread gets the sum.
+// `scratch` holds NT/64 ints of LDS.
+template <int NT>
+__device__ inline int block_sum_int(int x, int* scratch) {
+  x = wave_sum_int(x);
+  const int wave = threadIdx.x / 64;
+  if ((threadIdx.x & 63) == 0) scratch[wave] = x;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) t += scratch[w];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive prefix sum over threads in thread order; `scratch` NT/64 ints.
+template <int NT>
+__device__ inline int block_exclusive_scan(int x, int* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x / 64;
+  int inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) scratch[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += scratch[w];
+  __syncthreads();
+  return before + inc - x;
+}
+
+// Marks the k largest keys among the valid items (lower index wins ties).
+// Thread t holds items t*IPT .. t*IPT+IPT-1 (index order == thread order).
+template <int NT, int IPT>
+__device__ void block_topk(const unsigned long long (&key)[IPT], const bool (&valid)[IPT], int k,
+                           bool (&sel)[IPT], int* scratch) {
+  if (k <= 0) {
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) sel[u] = false;
+    return;
+  }
+  // Largest threshold T with #{key >= T} >= k: the k-th largest key.
+  unsigned long long T = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const unsigned long long trial = T | (1ull << bit);
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) c += (valid[u] && key[u] >= trial) ? 1 : 0;
+    if (block_sum_int<NT>(c, scratch) >= k) T = trial;
+  }
+  int gt = 0, ties = 0;
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) {
+    gt += (valid[u] && key[u] > T) ? 1 : 0;
+    ties += (valid[u] && key[u] == T) ? 1 : 0;
+  }
+  const int need = k - block_sum_int<NT>(gt, scratch);
+  int tie_rank = block_exclusive_scan<NT>(ties, scratch);
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) {
+    const bool tie = valid[u] && key[u] == T;
+    sel[u] = (valid[u] && key[u] > T) || (tie && tie_rank < need);
+    if (tie) ++tie_rank;
+  }
+}
+
+// Writes the items with flag == want, in index order, to out[pos] = map(i).
+template <int NT, int IPT, typename Map>
+__device__ void block_compact(const bool (&flag)[IPT], const bool (&valid)[IPT], bool want,
+                              int32_t* out, Map map, int* scratch) {
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) cnt += (valid[u] && flag[u] == want) ? 1 : 0;
+  int pos = block_exclusive_scan<NT>(cnt, scratch);
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) {
+    if (valid[u] && flag[u] == want) out[pos++] = map(threadIdx.x * IPT + u);
+  }
+}
+
+__device__ inline int kept_block_id(const IsaShape& s, const int32_t* ctx_row, int p) {
+  return p < s.N_src ? p : ctx_row[p - s.N_src];
+}
+
+// ---------------------------------------------------------------- step (2)
+constexpr int kCtxThreads = 1024;
+constexpr int kCtxIPT = ISA_MAX_SEG_BLOCKS / kCtxThreads;
+
+__global__ __launch_bounds__(kCtxThreads) void ctx_topk_kernel(IsaShape s, const double* __restrict__ qc,
+                                                               const double* __restrict__ kc,
+                                                               int32_t* __restrict__ ctx_idx,
+                                                               double* __restrict__ ctx_score) {
+  const int bh = blockIdx.x;
+  __shared__ double part[kCtxThreads];
+  __shared__ double qbar[128];
+  __shared__ int scratch[kCtxThreads / 64];
+  const int D = s.D;
+  const int parts = kCtxThreads / D;
+  {
+    const int d = threadIdx.x % D, pp = threadIdx.x / D;
+    double acc = 0.0;
+    for (int i = pp; i < s.N_src; i += parts) acc += qc[((size_t)bh * s.N + i) * D + d];
+    part[threadIdx.x] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    double acc = 0.0;
+    for (int pp = 0; pp < parts; ++pp) acc += part[pp * D + threadIdx.x];
+    qbar[threadIdx.x] = acc;
+  }
+  __syncthreads();
+  const double sq = sqrt((double)D);
+  unsigned long long key[kCtxIPT];
+  bool valid[kCtxIPT], sel[kCtxIPT];
+#pragma unroll
+  for (int u = 0; u < kCtxIPT; ++u) {
+    const int j = threadIdx.x * kCtxIPT + u;
+    valid[u] = j < s.N_ctx;
+    key[u] = 0;
+    if (valid[u]) {
+      const double* krow = kc + ((size_t)bh * s.N + s.N_src + j) * D;
+      double acc = 0.0;
+      for (int d = 0; d < D; ++d) acc = fma(qbar[d], krow[d], acc);
+      const double r = acc / sq;
+      if (ctx_score) ctx_score[(size_t)bh * s.N_ctx + j] = r;
+      key[u] = order_key(r);
+    }
+  }
+  if (s.k_ctx == 0) return;
+  block_topk<kCtxThreads, kCtxIPT>(key, valid, s.k_ctx, sel, scratch);
+  const int n_src = s.N_src;
+  block_compact<kCtxThreads, kCtxIPT>(sel, valid, true, ctx_idx + (size_t)bh * s.k_ctx,
+                                      [n_src](int j) { return n_src + j; }, scratch);
+}
+
+// ------------------------------------------------- step (1) coarse rows
+constexpr int kCoarseRows = 16, kCoarseCols = 64, kCoarseDc = 32;
+
+__global__ __launch_bounds__(256) void coarse_rows_kernel(IsaShape s, const double* __restrict__ qc,
+                                                          const double* __restrict__ kc,
+                                                          const int32_t* __restrict__ ctx_idx,
+                                                          double* __restrict__ srows) {
+  const int i0 = blockIdx.x * kCoarseRows, p0 = blockIdx.y * kCoarseCols, bh = blockIdx.z;
+  const int D = s.D;
+  __shared__ double qs[kCoarseRows][kCoarseDc + 1];
+  __shared__ double ks[kCoarseCols][kCoarseDc + 1];
+  __shared__ int gid[kCoarseCols];
+  const int32_t* ctx_row = ctx_idx + (size_t)bh * s.k_ctx;
+  if (threadIdx.x < kCoarseCols) {
+    const int p = p0 + threadIdx.x;
+    int g = p < s.N_kv ? kept_block_id(s, ctx_row, p) : -1;
+    gid[threadIdx.x] = (g >= 0 && g < s.N) ? g : -1;   // ids outside [0, N) read as zero rows
+  }
+  const int col = threadIdx.x % kCoarseCols, rg = threadIdx.x / kCoarseCols;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  __syncthreads();
+  for (int d0 = 0; d0 < D; d0 += kCoarseDc) {
+    for (int t = threadIdx.x; t < kCoarseRows * kCoarseDc; t += 256) {
+      const int r = t / kCoarseDc, dd = t % kCoarseDc, i = i0 + r;
+      qs[r][dd] = i < s.N ? qc[((size_t)bh * s.N + i) * D + d0 + dd] : 0.0;
+    }
+    for (int t = threadIdx.x; t < kCoarseCols * kCoarseDc; t += 256) {
+      const int c = t / kCoarseDc, dd = t % kCoarseDc, g = gid[c];
+      ks[c][dd] = g >= 0 ? kc[((size_t)bh * s.N + g) * D + d0 + dd] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int dd = 0; dd < kCoarseDc; ++dd) {
+      const double kv = ks[col][dd];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = fma(qs[rg * 4 + r][dd], kv, acc[r]);
+    }
+    __syncthreads();
+  }
+  const double sq = sqrt((double)D);
+  const int p = p0 + col;
+  if (p < s.N_kv) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + rg * 4 + r;
+      if (i < s.N) srows[((size_t)bh * s.N + i) * s.N_kv + p] = acc[r] / sq;
+    }
+  }
+}
+
+// ------------------------------------------------------ step (3) sharpness
+__global__ __launch_bounds__(256) void sharpness_kernel(IsaShape s, const double* __restrict__ srows,
+                                                        double* __restrict__ sharp) {
+  const int wave = threadIdx.x / 64, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave, bh = blockIdx.y;
+  if (i >= s.N) return;   // whole wave; no workgroup barrier below
+  const double* row = srows + ((size_t)bh * s.N + i) * s.N_kv;   // source columns first
+  const int n = s.N_src;
+  double mx = -INFINITY;
+  for (int j = lane; j < n; j += 64) mx = fmax(mx, row[j]);
+  mx = wave_max_f64(mx);
+  double z = 0.0;
+  for (int j = lane; j < n; j += 64) z += exp(row[j] - mx);
+  z = wave_sum_f64(z);
+  const double inv_n = 1.0 / (double)n;
+  double acc = 0.0;
+  for (int j = lane; j < n; j += 64) {
+    const double pr = exp(row[j] - mx) / z - inv_n;
+    acc += pr * pr;
+  }
+  acc = wave_sum_f64(acc);
+  if (lane == 0) sharp[(size_t)bh * s.N + i] = acc / (double)n;
+}
+
+// ----------------------------------------------------------- step (3) split
+constexpr int kSplitThreads = 1024;
+constexpr int kSplitIPT = 2 * ISA_MAX_SEG_BLOCKS / kSplitThreads;
+
+__global__ __launch_bounds__(kSplitThreads) void split_kernel(IsaShape s, const double* __restrict__ sharp,
+                                                              int32_t* __restrict__ sharp_idx,
+                                                              int32_t* __restrict__ flat_idx) {
+  const int bh = blockIdx.x;
+  __shared__ int scratch[kSplitThreads / 64];
+  unsigned long long key[kSplitIPT];
+  bool valid[kSplitIPT], sel[kSplitIPT];
+#pragma unroll
+  for (int u = 0; u < kSplitIPT; ++u) {
+    const int i = threadIdx.x * kSplitIPT + u;
+    valid[u] = i < s.N;
+    key[u] = valid[u] ? order_key(sharp[(size_t)bh * s.N + i]) : 0;
+  }
+  block_topk<kSplitThreads, kSplitIPT>(key, valid, s.n_sharp, sel, scratch);
+  auto ident = [](int i) { return i; };
+  if (s.n_sharp > 0)
+    block_compact<kSplitThreads, kSplitIPT>(sel, valid, true, sharp_idx + (size_t)bh * s.n_sharp,
+                                            ident, scratch);
+  if (s.n_flat > 0)
+    block_compact<kSplitThreads, kSplitIPT>(sel, valid, false, flat_idx + (size_t)bh * s.n_flat,
+                                            ident, scratch);
+}
+
+// --------------------------------------------- step (5) exact set per block
+constexpr int kFlatTopkThreads = 256;
+constexpr int kFlatTopkIPT = ISA_MAX_NKV / kFlatTopkThreads;
+
+__global__ __launch_bounds__(kFlatTopkThreads) void flat_topk_kernel(IsaShape s, const double* __restrict__ srows,
+                                                                     const int32_t* __restrict__ ctx_idx,
+                                                                     const int32_t* __restrict__ flat_idx,
+                                                                     int32_t* __restrict__ exact) {
+  const int r = blockIdx.x, bh = blockIdx.y;
+  __shared__ int scratch[kFlatTopkThreads / 64];
+  const int i = flat_idx[(size_t)bh * s.n_flat + r];
+  const double* row = srows + ((size_t)bh * s.N + i) * s.N_kv;
+  unsigned long long key[kFlatTopkIPT];
+  bool valid[kFlatTopkIPT], sel[kFlatTopkIPT];
+#pragma unroll
+  for (int u = 0; u < kFlatTopkIPT; ++u) {
+    const int p = threadIdx.x * kFlatTopkIPT + u;
+    valid[u] = p < s.N_kv;
+    key[u] = valid[u] ? order_key(row[p]) : 0;
+  }
+  block_topk<kFlatTopkThreads, kFlatTopkIPT>(key, valid, s.k_ns, sel, scratch);
+  const int32_t* ctx_row = ctx_idx + (size_t)bh * s.k_ctx;
+  const IsaShape sh = s;
+  block_compact<kFlatTopkThreads, kFlatTopkIPT>(
+      sel, valid, true, exact + ((size_t)bh * s.n_flat + r) * s.k_ns,
+      [sh, ctx_row](int p) { return kept_block_id(sh, ctx_row, p); }, scratch);
+}
+
+}  // namespace
+
+hipError_t isa_launch_ctx_topk(const IsaShape& s, const double* qc, const double* kc,
+                               int32_t* ctx_idx, double* ctx_score, hipStream_t st) {
+  if (s.N_ctx == 0) return hipSuccess;
+  ctx_topk_kernel<<<s.B * s.H, kCtxThreads, 0, st>>>(s, qc, kc, ctx_idx, ctx_score);
+  return hipGetLastError();
+}
+
+hipError_t isa_launch_coarse_rows(const IsaShape& s, const double* qc, const double* kc,
+                                  const int32_t* ctx_idx, double* srows, hipStream_t st) {
+  dim3 grid((s.N + kCoarseRows - 1) / kCoarseRows, (s.N_kv + kCoarseCols - 1) / kCoarseCols,
+            s.B * s.H);
+  coarse_rows_kernel<<<grid, 256, 0, st>>>(s, qc, kc, ctx_idx, srows);
+  return hipGetLastError();
+}
+
+hipError_t isa_launch_sharpness(const IsaShape& s, const double* srows, double* sharp,
+                                hipStream_t st) {
+  dim3 grid((s.N + 3) / 4, s.B * s.H);
+  sharpness_kernel<<<grid, 256, 0, st>>>(s, srows, sharp);
+  return hipGetLastError();
+}
+
+hipError_t isa_launch_split(const IsaShape& s, const double* sharp, int32_t* sharp_idx,
+                            int32_t* flat_idx, hipStream_t st) {
+  split_kernel<<<s.B * s.H, kSplitThreads, 0, st>>>(s, sharp, sharp_idx, flat_idx);
+  return hipGetLastError();
+}
+
+hipError_t isa_launch_flat_topk(const IsaShape& s, const double* srows, const int32_t* ctx_idx,
+                                const int32_t* flat_idx, int32_t* flat_exact_idx,
+                                hipStream_t st) {
+  if (s.n_flat == 0 || s.k_ns == 0) return hipSuccess;
+  dim3 grid(s.n_flat, s.B * s.H);
+  flat_topk_kernel<<<grid, kFlatTopkThreads, 0, st>>>(s, srows, ctx_idx, flat_idx, flat_exact_idx);
+  return hipGetLastError();
+}

@@ -1,0 +1,259 @@
+"""GPU parity of the HIP ISA path against the CPU oracle, through the C ABI.
+
+Small shapes compare every output element; the full workload shapes compare
+every selection of every head and sampled output rows of a few heads (the
+oracle computes those rows one by one). Special cases of the method are
+re-checked on the GPU."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import isa_inputs
+from oracle import isa_oracle
+from parity_util import bf16_tensor, compare_head
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+isa = pytest.importorskip("block_sparse_attention_blockwise_amd")
+
+
+def log(msg):
+    print(f"[gpu-parity {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    isa.lib()
+    return torch.device("cuda:0")
+
+
+def _inputs(cfg_id, p, heads=None, tile_heads=False):
+    """bf16 inputs [B,H,L,D]. With tile_heads, only `heads` are generated and
+    copied round-robin into the other head slots (the launch shape stays the
+    full one; only the listed heads are checked)."""
+    if not tile_heads:
+        return isa_inputs.make_inputs(cfg_id, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    gen = isa_inputs.make_inputs(cfg_id, p.B, p.H, p.L_src, p.L_ctx, p.D, heads=heads)
+    for nm in "QKV":
+        bits, val = gen[nm]
+        for bi in range(p.B):
+            for h in range(p.H):
+                if (bi, h) not in heads:
+                    src = heads[h % len(heads)]
+                    bits[bi, h] = bits[src]
+                    val[bi, h] = val[src]
+    return gen
+
+
+def _run(p, inp, dev):
+    Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
+    O, dbg = isa.forward(Q, K, V, p, debug=True)
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in dbg.items()}
+    out["O"] = O.float().cpu().numpy()
+    return out
+
+
+def _gpu_head(res, bi, h):
+    return {k: res[k][bi, h] for k in ("ctx_idx", "sharp_idx", "flat_idx", "flat_exact_idx", "O")}
+
+
+def _sample_rows(plan, n, seed):
+    rng = np.random.default_rng(seed)
+    L = plan.L_src + plan.L_ctx
+    rows = set(rng.choice(L, size=min(n, L), replace=False).tolist())
+    # first and last rows of both segments, and of the tail blocks
+    for t in (0, plan.L_src - 1, plan.L_src, L - 1, plan.starts[plan.N_src - 1], plan.starts[-1]):
+        rows.add(int(t))
+    return np.array(sorted(rows))
+
+
+def _check(p, inp, res, out_heads, rows_per_head, seed=0, all_sel=True):
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    heads = [(bi, h) for bi in range(p.B) for h in range(p.H)] if all_sel else list(out_heads)
+    worst = 0.0
+    for (bi, h) in heads:
+        Qv, Kv, Vv = (inp[n][1][bi, h] for n in "QKV")
+        if (bi, h) in out_heads:
+            rows = None if rows_per_head is None else _sample_rows(plan, rows_per_head, seed + h)
+            rep = compare_head(plan, Qv, Kv, Vv, _gpu_head(res, bi, h), rows=rows)
+            worst = max(worst, rep["max_abs"])
+            log(f"  head ({bi},{h}): max-abs {rep['max_abs']:.2e} mean-abs {rep['mean_abs']:.2e} "
+                f"rel-L2 {rep['rel_l2']:.2e} excused {rep['excused']}")
+        else:
+            # selections only
+            compare_head(plan, Qv, Kv, Vv, _gpu_head(res, bi, h), rows=np.zeros(0, dtype=np.int64))
+    return worst
+
+
+# ------------------------------------------------------------- workloads
+def test_tiny_all_rows(dev):
+    c = isa_inputs.CONFIGS[1]
+    p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"])
+    inp = _inputs(1, p)
+    log("tiny: forward")
+    res = _run(p, inp, dev)
+    _check(p, inp, res, {(0, 0), (0, 1)}, None)
+
+
+@pytest.mark.parametrize("cfg_id", [2, 3, 4])
+def test_workload_configs(dev, cfg_id):
+    c = isa_inputs.CONFIGS[cfg_id]
+    p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"])
+    log(f"cfg {cfg_id}: generating inputs")
+    inp = _inputs(cfg_id, p)
+    log(f"cfg {cfg_id}: forward")
+    res = _run(p, inp, dev)
+    log(f"cfg {cfg_id}: checking selections of {p.H} heads, outputs of 3 heads")
+    _check(p, inp, res, {(0, 0), (0, 17), (0, p.H - 1)}, 384, seed=cfg_id)
+
+
+SWEEP = [  # (b, alpha_s, alpha_ns, alpha_f) points of the 131072-token sweep
+    (64, 0.125, 0.0625, 0.5),
+    (32, 0.125, 0.0625, 0.5),
+    (64, 0.25, 0.125, 0.25),
+    (32, 0.25, 0.125, 0.75),
+]
+
+
+@pytest.mark.parametrize("b,a_s,a_ns,a_f", SWEEP)
+def test_128k_sweep_points(dev, b, a_s, a_ns, a_f):
+    c = isa_inputs.CONFIGS[5]
+    p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], b, a_s, a_f, a_ns)
+    heads = [(0, 3), (0, 29)]
+    log(f"128k b={b} a_s={a_s} a_ns={a_ns} a_f={a_f}: inputs")
+    inp = _inputs(5, p, heads=heads, tile_heads=True)
+    log("128k: forward")
+    res = _run(p, inp, dev)
+    _check(p, inp, res, set(heads), 128, seed=b, all_sel=False)
+
+
+# -------------------------------------------------------- special cases
+def _small(dev, L_src, L_ctx, D, b, a_s, a_f, a_ns, H=2, cfg_id=1, modify=None):
+    p = isa.Params(1, H, L_src, L_ctx, D, b, a_s, a_f, a_ns)
+    inp = _inputs(cfg_id, p)
+    if modify:
+        modify(inp, p)
+    res = _run(p, inp, dev)
+    return p, inp, res
+
+
+@pytest.mark.parametrize("D,b", [(128, 64), (64, 32), (128, 32), (64, 64)])
+def test_small_shapes_all_rows(dev, D, b):
+    p, inp, res = _small(dev, 700, 451, D, b, 0.25, 0.5, 0.125)
+    _check(p, inp, res, {(0, 0), (0, 1)}, None)
+
+
+def test_dense_equality_and_dense_kernel(dev):
+    for D in (64, 128):
+        p, inp, res = _small(dev, 333, 410, D, 64, 1.0, 0.0, 0.0625)
+        assert res["flat_idx"].size == 0
+        Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
+        Od = isa.dense_attn(Q, K, V).float().cpu().numpy()
+        for h in range(p.H):
+            ref = isa_oracle.dense_attention(inp["Q"][1][0, h], inp["K"][1][0, h], inp["V"][1][0, h])
+            e1 = np.abs(res["O"][0, h] - ref)
+            e2 = np.abs(Od[0, h] - ref)
+            log(f"dense-equality D={D} h={h}: isa {e1.max():.2e} dense {e2.max():.2e}")
+            for e in (e1, e2):
+                assert e.max() <= 2e-2 and e.mean() <= 2e-3
+
+
+@pytest.mark.parametrize("L,D", [(64, 128), (1000, 64), (4097, 128)])
+def test_dense_kernel_ragged(dev, L, D):
+    rng = np.random.default_rng(L)
+    x = [isa_inputs.round_to_bf16(rng.standard_normal((1, 2, L, D)).astype(np.float32)) for _ in range(3)]
+    Q, K, V = (bf16_tensor(b_, dev) for b_, _ in x)
+    O = isa.dense_attn(Q, K, V).float().cpu().numpy()
+    for h in range(2):
+        ref = isa_oracle.dense_attention(x[0][1][0, h], x[1][1][0, h], x[2][1][0, h])
+        e = np.abs(O[0, h] - ref)
+        assert e.max() <= 2e-2 and e.mean() <= 2e-3, (e.max(), e.mean())
+
+
+def test_identical_keys_make_taylor_exact(dev):
+    def flatten_keys(inp, p):
+        plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, 0, 0, 0)
+        bits, val = inp["K"]
+        for s, n in zip(plan.starts, plan.counts):
+            bits[:, :, s:s + n] = bits[:, :, s:s + 1]
+            val[:, :, s:s + n] = val[:, :, s:s + 1]
+    outs = []
+    for a_ns in (0.0, 0.0625, 1.0):
+        p, inp, res = _small(dev, 640, 576, 128, 64, 0.25, 0.5, a_ns, modify=flatten_keys)
+        outs.append(res["O"])
+    exact = isa_oracle.isa_head(inp["Q"][1][0, 0], inp["K"][1][0, 0], inp["V"][1][0, 0],
+                                isa_oracle.make_plan(640, 576, 64, 0.25, 0.0, 0.0)).O
+    for o in outs:
+        e = np.abs(o[0, 0] - exact)
+        assert e.max() <= 2e-2 and e.mean() <= 2e-3
+
+
+def test_kv_permutation_within_blocks(dev):
+    p, inp, res = _small(dev, 768, 640, 128, 64, 0.25, 0.5, 0.125)
+    plan = isa_oracle.make_plan(768, 640, 64, 0, 0, 0)
+    rng = np.random.default_rng(5)
+    inp2 = {n: (inp[n][0].copy(), inp[n][1].copy()) for n in "QKV"}
+    for s, n in zip(plan.starts, plan.counts):
+        perm = s + rng.permutation(n)
+        for nm in "KV":
+            inp2[nm][0][:, :, s:s + n] = inp[nm][0][:, :, perm]
+            inp2[nm][1][:, :, s:s + n] = inp[nm][1][:, :, perm]
+    res2 = _run(p, inp2, dev)
+    for k in ("ctx_idx", "sharp_idx", "flat_idx", "flat_exact_idx"):
+        assert np.array_equal(res[k], res2[k]), k
+    e = np.abs(res["O"] - res2["O"])
+    assert e.max() <= 2e-2 and e.mean() <= 2e-3
+
+
+def test_no_context_and_all_flat(dev):
+    p, inp, res = _small(dev, 1000, 0, 128, 64, 0.125, 0.5, 0.0625)
+    _check(p, inp, res, {(0, 0), (0, 1)}, None)
+    p, inp, res = _small(dev, 500, 470, 64, 32, 1.0, 1.0, 0.0)
+    assert res["sharp_idx"].size == 0
+    _check(p, inp, res, {(0, 0), (0, 1)}, None)
+
+
+def test_deterministic(dev):
+    p, inp, res = _small(dev, 900, 700, 128, 64, 0.125, 0.5, 0.0625)
+    res2 = _run(p, inp, dev)
+    for k, v in res.items():
+        assert np.array_equal(v, res2[k]), k
+
+
+def test_step_entry_points_compose_to_forward(dev):
+    c = isa_inputs.CONFIGS[3]
+    p = isa.Params(1, 4, c["L_src"], c["L_ctx"], c["D"], c["b"])
+    inp = _inputs(3, p)
+    Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
+    O_ref, dbg = isa.forward(Q, K, V, p, debug=True)
+    qc, kc, kcb, vcb = isa.pool_coarse(Q, K, V, p)
+    ctx, score = isa.ctx_topk(qc, kc, p)
+    sharp, si, fi, ei = isa.sharpness_split(qc, kc, ctx, p)
+    O = torch.zeros_like(Q)
+    isa.sharp_attn(Q, K, V, ctx, si, p, out=O)
+    isa.flat_taylor_attn(Q, K, V, kcb, vcb, ctx, fi, ei, p, out=O)
+    torch.cuda.synchronize()
+    assert torch.equal(O.view(torch.int16), O_ref.view(torch.int16))
+    for a, b in ((qc, "qc"), (kc, "kc"), (ctx, "ctx_idx"), (score, "ctx_score"), (sharp, "sharpness"),
+                 (si, "sharp_idx"), (fi, "flat_idx"), (ei, "flat_exact_idx")):
+        assert torch.equal(a, dbg[b]), b
+    # pooled means are exact sums divided by n_j: bit-identical to the oracle
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    for h in range(p.H):
+        Qc = isa_oracle.pool(inp["Q"][1][0, h], plan)
+        Kc = isa_oracle.pool(inp["K"][1][0, h], plan)
+        assert np.array_equal(qc[0, h].cpu().numpy(), Qc)
+        assert np.array_equal(kc[0, h].cpu().numpy(), Kc)
+        S = isa_oracle.coarse_scores(Qc, Kc)
+        M = isa_oracle.sharpness(S, plan)
+        np.testing.assert_allclose(sharp[0, h].cpu().numpy(), M, rtol=1e-10, atol=0)
+        r = isa_oracle.context_scores(S, plan)
+        np.testing.assert_allclose(score[0, h].cpu().numpy(), r, rtol=1e-10, atol=1e-10)

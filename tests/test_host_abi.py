@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports
+every entry point declared in include/isa.h, isa_plan agrees with the oracle's
+counts, and invalid calls fail with the documented codes before anything is
+launched."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def isa():
+    import block_sparse_attention_blockwise_amd as isa
+    if not os.path.exists(isa.LIB_PATH):
+        from block_sparse_attention_blockwise_amd import _build
+        _build.build()
+    isa.lib()
+    return isa
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "isa.h")).read()
+    return re.findall(r"ISA_API\s+[\w\s\*]+?\b(isa_\w+)\s*\(", txt)
+
+
+def test_exports_every_declared_symbol(isa):
+    names = _declared()
+    assert set(names) == set(isa.EXPORTED)
+    nm = subprocess.run(["nm", "-D", "--defined-only", isa.LIB_PATH], capture_output=True, text=True)
+    exported = {ln.split()[-1] for ln in nm.stdout.splitlines() if " T " in ln}
+    for n in names:
+        assert n in exported, n
+        assert getattr(isa.lib(), n) is not None
+
+
+def test_plan_matches_oracle_counts(isa):
+    from oracle import isa_oracle
+    import isa_inputs
+    cases = []
+    for cid, c in isa_inputs.CONFIGS.items():
+        cases.append((c["L_src"], c["L_ctx"], c["D"], c["b"], c["alpha_s"], c["alpha_f"], c["alpha_ns"]))
+    for b in (32, 64):
+        for a_s in (0.125, 0.25):
+            for a_ns in (0.0625, 0.125):
+                for a_f in (0.25, 0.5, 0.75):
+                    cases.append((65536, 65536, 128, b, a_s, a_f, a_ns))
+    cases += [(1, 0, 64, 32, 0.5, 0.5, 0.5), (100, 0, 64, 32, 0.125, 0.5, 0.0625),
+              (11884, 11884, 128, 64, 0.1, 0.3, 0.07), (777, 333, 64, 64, 1.0, 1.0, 1.0),
+              (777, 333, 64, 64, 0.0, 0.0, 0.0)]
+    for (Ls, Lc, D, b, a_s, a_f, a_ns) in cases:
+        pl = isa.plan(isa.Params(1, 40, Ls, Lc, D, b, a_s, a_f, a_ns))
+        o = isa_oracle.make_plan(Ls, Lc, b, a_s, a_f, a_ns)
+        for k in ("N_src", "N_ctx", "N", "k_ctx", "N_kv", "n_flat", "n_sharp", "k_ns"):
+            assert pl[k] == getattr(o, k), (k, Ls, Lc, b, a_s, a_f, a_ns)
+        assert pl["workspace_bytes"] >= 40 * o.N * o.N_kv * 8
+        assert pl["scores_bytes"] >= 40 * o.N * o.N_kv * 8
+
+
+def _params(isa, **kw):
+    base = dict(B=1, H=2, L_src=1024, L_ctx=1024, D=128, b=64, alpha_s=0.125, alpha_f=0.5,
+                alpha_ns=0.0625)
+    base.update(kw)
+    return isa.IsaParams(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L_src=0), -1), (dict(L_ctx=-1), -1), (dict(B=0), -1), (dict(H=0), -1),
+    (dict(D=0), -1), (dict(b=0), -1),
+    (dict(alpha_s=float("nan")), -1), (dict(alpha_f=1.5), -1), (dict(alpha_ns=-0.1), -1),
+    (dict(D=96), -2), (dict(D=256), -2), (dict(b=16), -2), (dict(b=128), -2),
+    (dict(L_src=64 * 4097), -2), (dict(L_ctx=64 * 4097), -2),
+    (dict(L_src=64 * 4000, L_ctx=64 * 4000, alpha_s=0.05), -2),   # N_kv > 4096
+])
+def test_plan_rejects(isa, kw, code):
+    out = isa.IsaPlan()
+    assert isa.lib().isa_plan(ctypes.byref(_params(isa, **kw)), ctypes.byref(out)) == code
+
+
+def test_calls_fail_before_launch(isa):
+    L = isa.lib()
+    p = _params(isa)
+    fake = 0x1000   # never dereferenced: every call below fails validation first
+    assert L.isa_plan(None, None) == -1
+    assert L.isa_forward(None, fake, fake, fake, fake, fake, 1 << 40, None, None) == -1
+    assert L.isa_forward(ctypes.byref(p), None, fake, fake, fake, fake, 1 << 40, None, None) == -1
+    assert L.isa_forward(ctypes.byref(p), fake, fake, fake, fake, fake, 16, None, None) == -3
+    assert L.isa_sharpness_split(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
+                                 16, None) == -3
+    assert L.isa_sharpness_split(ctypes.byref(p), fake, fake, None, fake, fake, fake, fake, fake,
+                                 1 << 40, None) == -1
+    assert L.isa_pool_coarse(ctypes.byref(p), fake, None, fake, fake, fake, None, None, None) == -1
+    assert L.isa_ctx_topk(ctypes.byref(p), fake, fake, None, None, None) == -1
+    assert L.isa_sharp_attn(ctypes.byref(p), fake, fake, fake, None, fake, fake, None) == -1
+    assert L.isa_flat_taylor_attn(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake,
+                                  fake, fake, None) == -1
+    assert L.isa_dense_attn(1, 1, 0, 128, fake, fake, fake, fake, None) == -1
+    assert L.isa_dense_attn(1, 1, 16, 96, fake, fake, fake, fake, None) == -2
+    assert L.isa_dense_attn(1, 1, 16, 128, None, fake, fake, fake, None) == -1
+    bad = _params(isa, D=96)
+    assert L.isa_forward(ctypes.byref(bad), fake, fake, fake, fake, fake, 1 << 40, None, None) == -2
+
+
+def test_strerror(isa):
+    for code in (0, -1, -2, -3, -4, 7):
+        s = isa.strerror(code)
+        assert isinstance(s, str) and s
+    assert "workspace" in isa.strerror(-3)
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import block_sparse_attention_blockwise_amd as isa
+    monkeypatch.setattr(isa, "_lib", None)
+    monkeypatch.setattr(isa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        isa.lib()
