@@ -1,0 +1,325 @@
+"""Benchmark of the ISA forward pass on one MI355X.
+
+Workload: In-context Sparse Attention forward at 64K tokens
+(B=1, H=40, D=128, L_src = L_ctx = 32768, b=64, alpha_s=0.125, alpha_f=0.5,
+alpha_ns=0.0625), bf16 inputs from the seeded clustered generator, resident in
+HBM before timing starts.
+
+One step = one pass of the whole hot path through the C ABI: pooling,
+context top-k, coarse rows + sharpness + split + exact sets, sharp attention,
+flat exact+Taylor attention. The step is issued as the five entry points on
+torch's current stream with HIP events between them (per-kernel durations
+for the roofline); the isa_forward entry point (same kernels in one call) is
+timed as well, as is the library's dense attention on the same inputs.
+
+Prints one JSON line. `value` is the forward latency in ms (lower is better).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ISA fwd latency (ms) + effective TFLOP/s & MFMA util at 64K tokens, H=40, D=128"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = dict(cfg_id=4, B=1, H=40, L_src=32768, L_ctx=32768, D=128, b=64,
+                alpha_s=0.125, alpha_f=0.5, alpha_ns=0.0625)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sharp_attn_64k_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_blockwise_amd", "csrc", "isa_attn.hip")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def make_inputs(dev):
+    import torch
+    import isa_inputs
+    w = WORKLOAD
+    L = w["L_src"] + w["L_ctx"]
+    shape = (w["B"], w["H"], L, w["D"])
+    out = {n: torch.empty(shape, dtype=torch.bfloat16, device=dev) for n in "QKV"}
+    host = {}
+    for bi in range(w["B"]):
+        for h in range(w["H"]):
+            qkv = isa_inputs.make_head(w["cfg_id"], bi, h, w["L_src"], w["L_ctx"], w["D"])
+            for n, x in zip("QKV", qkv):
+                bits, val = isa_inputs.round_to_bf16(x)
+                out[n][bi, h].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+                if (bi, h) == (0, 0):
+                    host[n] = val
+    return out, host
+
+
+def algorithmic_flops(p, pl, ctx_idx, sharp_idx, flat_idx, exact_idx):
+    """FLOPs of the method from the actual selections (4*D per query-key pair
+    for the exact terms and the pooled terms, 2*D per coarse score)."""
+    from oracle.isa_oracle import make_plan   # block token counts only
+    plan = make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    n = np.asarray(plan.counts, dtype=np.float64)
+    D = p.D
+    f_sharp = f_flat = f_taylor = 0.0
+    for bi in range(p.B):
+        for h in range(p.H):
+            J = np.concatenate([np.arange(pl["N_src"]), ctx_idx[bi, h]])
+            nJ = n[J].sum()
+            f_sharp += 4 * D * n[sharp_idx[bi, h]].sum() * nJ
+            fi = flat_idx[bi, h]
+            if fi.size:
+                nE = n[exact_idx[bi, h]].sum(axis=1)
+                f_flat += 4 * D * (n[fi] * nE).sum()
+                f_taylor += 4 * D * (n[fi] * (pl["N_kv"] - pl["k_ns"])).sum()
+    f_coarse = 2 * D * pl["N"] * pl["N_kv"] * p.B * p.H
+    L = p.L_src + p.L_ctx
+    f_dense = 4 * D * L * L * p.B * p.H
+    return dict(sharp=f_sharp, flat_exact=f_flat, taylor=f_taylor, coarse=f_coarse, dense=f_dense)
+
+
+def traffic_record():
+    """HBM bytes per launch of the sharp kernel from the committed rocprofv3
+    counter summary, valid only for the kernel source it was taken on."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(host, budget_s):
+    """The CPU oracle, untuned, on a bounded sample of the same workload:
+    head (0,0) with its selections in full and outputs for as many sharp and
+    flat query blocks as fit the time budget, extrapolated to the whole
+    forward (all blocks, all heads)."""
+    from oracle import isa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    w = WORKLOAD
+    plan = O.make_plan(w["L_src"], w["L_ctx"], w["b"], w["alpha_s"], w["alpha_f"], w["alpha_ns"])
+    Q, K, V = (host[n].astype(np.float64) for n in "QKV")
+    t0 = time.perf_counter()
+    sel = O.isa_head(Q, K, V, plan, compute_output=False)
+    t_sel = time.perf_counter() - t0
+    sel_d = dict(ctx_idx=sel.ctx_idx, sharp_idx=sel.sharp_idx, flat_idx=sel.flat_idx,
+                 flat_exact_idx=sel.flat_exact_idx)
+    rng = np.random.default_rng(0)
+    sharp_order = rng.permutation(sel.sharp_idx)
+    flat_order = rng.permutation(sel.flat_idx)
+    done = {"sharp": [], "flat": []}
+    deadline = time.perf_counter() + budget_s
+    k = 0
+    while time.perf_counter() < deadline or min(len(done["sharp"]), len(done["flat"])) < 2:
+        for kind, order in (("sharp", sharp_order), ("flat", flat_order)):
+            if k >= len(order):
+                continue
+            i = order[k]
+            s = plan.starts[i]
+            rows = np.arange(s, s + plan.counts[i])
+            t1 = time.perf_counter()
+            O.isa_head(Q, K, V, plan, selections=sel_d, rows=rows)
+            done[kind].append(time.perf_counter() - t1)
+        k += 1
+        if k >= max(len(sharp_order), len(flat_order)):
+            break
+    # isa_head with injected selections repeats the (cheap) pooling/coarse
+    # steps each call; subtract that share using a call with no rows.
+    t1 = time.perf_counter()
+    O.isa_head(Q, K, V, plan, selections=sel_d, rows=np.zeros(0, dtype=np.int64))
+    t_fixed = time.perf_counter() - t1
+    per_sharp = max(np.mean(done["sharp"]) - t_fixed, 0.0)
+    per_flat = max(np.mean(done["flat"]) - t_fixed, 0.0)
+    per_head = t_sel + per_sharp * plan.n_sharp + per_flat * plan.n_flat
+    total_ms = per_head * w["B"] * w["H"] * 1e3
+    return {"value": total_ms, "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "sample": (f"head (0,0) of {w['B'] * w['H']}: selections in full ({t_sel:.2f} s), outputs of "
+                       f"{len(done['sharp'])} sharp and {len(done['flat'])} flat query blocks "
+                       f"(of {plan.n_sharp}/{plan.n_flat}); per-block times extrapolated to all "
+                       f"blocks and heads, numpy fp64 with {threads} BLAS threads")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import block_sparse_attention_blockwise_amd as isa
+
+    dev = torch.device("cuda:0")
+    lib = isa.lib()
+    w = WORKLOAD
+    p = isa.Params(w["B"], w["H"], w["L_src"], w["L_ctx"], w["D"], w["b"], w["alpha_s"],
+                   w["alpha_f"], w["alpha_ns"])
+    pc = p.c()
+    pr = ctypes.byref(pc)
+    pl = isa.plan(p)
+    log("generating inputs")
+    T, host = make_inputs(dev)
+    Q, K, V = T["Q"], T["K"], T["V"]
+    O = torch.empty_like(Q)
+    BH = p.B * p.H
+    e = lambda *s, dt: torch.empty(s, dtype=dt, device=dev)
+    qc = e(BH, pl["N"], p.D, dt=torch.float64)
+    kc = e(BH, pl["N"], p.D, dt=torch.float64)
+    kcb = e(BH, pl["N"], p.D, dt=torch.bfloat16)
+    vcb = e(BH, pl["N"], p.D, dt=torch.bfloat16)
+    ctx = e(BH, pl["k_ctx"], dt=torch.int32)
+    score = e(BH, pl["N_ctx"], dt=torch.float64)
+    sharp = e(BH, pl["N"], dt=torch.float64)
+    si = e(BH, pl["n_sharp"], dt=torch.int32)
+    fi = e(BH, pl["n_flat"], dt=torch.int32)
+    ei = e(BH, pl["n_flat"], pl["k_ns"], dt=torch.int32)
+    ws_s = e(pl["scores_bytes"], dt=torch.uint8)
+    ws_f = e(pl["workspace_bytes"], dt=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def chk(name, rc):
+        if rc != 0:
+            raise RuntimeError(f"{name}: {isa.strerror(rc)}")
+
+    names = ["pool", "ctx_topk", "sharpness_split", "sharp_attn", "flat_taylor_attn"]
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        chk("pool", lib.isa_pool_coarse(pr, Q.data_ptr(), K.data_ptr(), V.data_ptr(), qc.data_ptr(),
+                                        kc.data_ptr(), kcb.data_ptr(), vcb.data_ptr(), sp))
+        if ev: ev[1].record(stream)
+        chk("ctx", lib.isa_ctx_topk(pr, qc.data_ptr(), kc.data_ptr(), ctx.data_ptr(), score.data_ptr(), sp))
+        if ev: ev[2].record(stream)
+        chk("split", lib.isa_sharpness_split(pr, qc.data_ptr(), kc.data_ptr(), ctx.data_ptr(),
+                                             sharp.data_ptr(), si.data_ptr(), fi.data_ptr(),
+                                             ei.data_ptr(), ws_s.data_ptr(), ws_s.numel(), sp))
+        if ev: ev[3].record(stream)
+        chk("sharp", lib.isa_sharp_attn(pr, Q.data_ptr(), K.data_ptr(), V.data_ptr(), ctx.data_ptr(),
+                                        si.data_ptr(), O.data_ptr(), sp))
+        if ev: ev[4].record(stream)
+        chk("flat", lib.isa_flat_taylor_attn(pr, Q.data_ptr(), K.data_ptr(), V.data_ptr(), kcb.data_ptr(),
+                                             vcb.data_ptr(), ctx.data_ptr(), fi.data_ptr(), ei.data_ptr(),
+                                             O.data_ptr(), sp))
+        if ev: ev[5].record(stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = {n: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+           for i, n in enumerate(names)}
+    step_ms = float(np.mean([evs[k][0].elapsed_time(evs[k][5]) for k in range(args.steps)]))
+    p10, p90 = (float(x) for x in np.percentile(
+        [evs[k][0].elapsed_time(evs[k][5]) for k in range(args.steps)], [10, 90]))
+
+    # isa_forward (same kernels, one call)
+    fwd_ms = None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        chk("fwd", lib.isa_forward(pr, Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                                   ws_f.data_ptr(), ws_f.numel(), None, sp))
+    e0.record(stream)
+    for _ in range(args.steps):
+        chk("fwd", lib.isa_forward(pr, Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                                   ws_f.data_ptr(), ws_f.numel(), None, sp))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / args.steps
+    # the decomposed step (five entry points) must produce what isa_forward does
+    O_fwd = O.clone()
+    step()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(O_fwd.view(torch.int16), O.view(torch.int16)))
+
+    flops = algorithmic_flops(p, pl, ctx.view(p.B, p.H, -1).cpu().numpy(),
+                              si.view(p.B, p.H, -1).cpu().numpy(), fi.view(p.B, p.H, -1).cpu().numpy(),
+                              ei.view(p.B, p.H, pl["n_flat"], pl["k_ns"]).cpu().numpy())
+    alg_total = flops["sharp"] + flops["flat_exact"] + flops["taylor"] + flops["coarse"]
+
+    dense_ms = None
+    if not args.no_dense:
+        log("dense baseline")
+        isa.dense_attn(Q, K, V, out=O)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.dense_reps):
+            chk("dense", lib.isa_dense_attn(p.B, p.H, p.L_src + p.L_ctx, p.D, Q.data_ptr(), K.data_ptr(),
+                                            V.data_ptr(), O.data_ptr(), sp))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / args.dense_reps
+
+    sharp_tflops = flops["sharp"] / (per["sharp_attn"] * 1e-3) / 1e12
+    rec = traffic_record()
+    roofline = {"bound": "mfma", "kernel": "isa_sharp_attn (attn_kernel<128,sharp>)",
+                "achieved": sharp_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": sharp_tflops / PEAK_BF16_TFLOPS, "traffic": rec,
+                "algorithmic_flops_per_launch": flops["sharp"],
+                "avg_launch_ms": per["sharp_attn"]}
+    pool_bytes = 3 * BH * (p.L_src + p.L_ctx) * p.D * 2 + BH * pl["N"] * p.D * (8 + 8 + 2 + 2)
+    out = {
+        "metric": METRIC, "value": step_ms, "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded clustered generator)",
+        "config": {"workload": "isa_fwd_64k_tokens_h40_d128", "B": p.B, "H": p.H, "L_src": p.L_src,
+                   "L_ctx": p.L_ctx, "D": p.D, "b": p.b, "alpha_s": p.alpha_s,
+                   "alpha_f": p.alpha_f, "alpha_ns": p.alpha_ns},
+        "latency_p10_p90_ms": [p10, p90],
+        "wall_ms_per_step": wall_ms,
+        "isa_forward_ms": fwd_ms,
+        "forward_matches_steps": same,
+        "per_kernel_ms": per,
+        "tflops_dense_equivalent": flops["dense"] / (step_ms * 1e-3) / 1e12,
+        "tflops_algorithmic": alg_total / (step_ms * 1e-3) / 1e12,
+        "mfma_util": {"sharp_attn": sharp_tflops / PEAK_BF16_TFLOPS,
+                      "flat_taylor_attn": (flops["flat_exact"] + flops["taylor"]) /
+                      (per["flat_taylor_attn"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "pool_hbm_frac": pool_bytes / (per["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "algorithmic_tflop": {k: v / 1e12 for k, v in flops.items()},
+        "dense_ms": dense_ms,
+        "dense_tflops": (flops["dense"] / (dense_ms * 1e-3) / 1e12) if dense_ms else None,
+        "speedup_vs_dense": (dense_ms / step_ms) if dense_ms else None,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(host, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
