@@ -102,6 +102,74 @@ __device__ inline bool block_is_partial(const IsaShape& s, int j) {
   return n < s.b;
 }
 
+// Where the keys of one tile come from (per workgroup, read-only).
+struct TileCtx {
+  const uint16_t* K;      // token rows of this (batch, head)
+  const uint16_t* V;
+  const uint16_t* kc;     // flat: bf16 block means of this (batch, head)
+  const uint16_t* vc;
+  const int* tab;         // LDS: packed (start << 7) | n per listed block
+  const int* ptab;        // LDS (flat): (j << 8) | (n << 1) | in_E per kept block
+  int ntab, L, N_kv, b, lb, per, ntiles_exact;
+};
+
+// One key slot: row pointers that are always safe to read, whether the slot
+// holds a real key, and its additive logit in log2 units.
+struct SlotSrc {
+  const uint16_t* k;
+  const uint16_t* v;
+  bool valid;
+  float bias;
+};
+
+template <int D, int MODE>
+__device__ inline SlotSrc slot_src(const TileCtx& c, int t, int slot) {
+  SlotSrc r;
+  if (MODE == kDense) {
+    const int tok = t * kKeyTile + slot;
+    r.valid = tok < c.L;
+    const size_t row = (size_t)(r.valid ? tok : 0) * D;
+    r.k = c.K + row;
+    r.v = c.V + row;
+    r.bias = r.valid ? 0.0f : -INFINITY;
+    return r;
+  }
+  if (MODE == kFlat && t >= c.ntiles_exact) {
+    const int p = (t - c.ntiles_exact) * kKeyTile + slot;
+    const int e = p < c.N_kv ? c.ptab[p] : 1;
+    const int n = (e >> 1) & 127;
+    r.valid = !(e & 1) && n > 0;
+    const size_t row = (size_t)(r.valid ? (e >> 8) : 0) * D;
+    r.k = c.kc + row;
+    r.v = c.vc + row;
+    r.bias = r.valid ? __log2f((float)n) : -INFINITY;
+    return r;
+  }
+  const int q = t * c.per + (slot >> c.lb), o = slot & (c.b - 1);
+  const int e = q < c.ntab ? c.tab[q] : 0;
+  r.valid = o < (e & 127);
+  const size_t row = (size_t)(r.valid ? (e >> 7) + o : 0) * D;
+  r.k = c.K + row;
+  r.v = c.V + row;
+  r.bias = r.valid ? 0.0f : -INFINITY;
+  return r;
+}
+
+// Whether tile t carries any non-zero additive logit (uniform over the
+// workgroup).
+template <int MODE>
+__device__ inline bool tile_has_bias(const TileCtx& c, int t) {
+  if (MODE == kDense) return (t + 1) * kKeyTile > c.L;
+  if (MODE == kFlat && t >= c.ntiles_exact) return true;
+  bool any = false;
+  for (int u = 0; u < c.per; ++u) {
+    const int q = t * c.per + u;
+    const int e = q < c.ntab ? c.tab[q] : 0;
+    any |= (e & 127) < c.b;
+  }
+  return any;
+}
+
 template <int D, int MODE, int QT, int NWAVES>
 __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
   constexpr int NT = NWAVES * 64;
@@ -119,7 +187,11 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char k_lds[2][kKeyTile * KSTR];
   __shared__ __attribute__((aligned(16))) char v_lds[2][kKeyTile * VSTR];
   __shared__ float bias_lds[2][kKeyTile];
-  __shared__ unsigned char emask[MODE == kFlat ? ISA_MAX_NKV : 1];
+  // Sharp path: token range of every kept block, packed (start << 7) | n_j,
+  // indexed by position in J. Flat path (dynamic LDS): the same for E_i, then
+  // (j << 8) | (n_j << 1) | in_E for every position of J.
+  __shared__ int jtab[MODE == kSharp ? ISA_MAX_NKV : 1];
+  extern __shared__ int dyn_lds[];
 
   const IsaShape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -128,11 +200,11 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
   const size_t head = (size_t)bh * s.L;     // first token row of this (batch, head)
   const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
   const int b = s.b;
+  const int lb = b == 64 ? 6 : 5;
 
   // ---- query rows owned by this lane
   int qtok[QT];
   bool qval[QT];
-  int flat_block = -1;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int lr = wave * ROWS_W + 16 * qt + c16;
@@ -143,8 +215,8 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
       qval[qt] = tok < s.L;
       qtok[qt] = tok;
     } else {
-      const int e = (MODE == kSharp) ? blockIdx.x * (ROWS / b) + lr / b : blockIdx.x;
-      const int o = (MODE == kSharp) ? lr % b : lr;
+      const int e = (MODE == kSharp) ? blockIdx.x * (ROWS >> lb) + (lr >> lb) : blockIdx.x;
+      const int o = (MODE == kSharp) ? (lr & (b - 1)) : lr;
       if (e < a.n_q) {
         const int j = a.qlist[(size_t)bh * a.n_q + e];
         if (j >= 0 && j < s.N) {
@@ -152,12 +224,10 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
           isa_block_range(s, j, st, n);
           qval[qt] = o < n;
           qtok[qt] = st + o;
-          if (MODE == kFlat) flat_block = j;
         }
       }
     }
   }
-  (void)flat_block;
 
   bf16x8_t qf[QT][KK];
 #pragma unroll
@@ -170,10 +240,30 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
     }
   }
 
-  const int32_t* exact_row = nullptr;
-  if (MODE == kFlat) {
-    exact_row = a.exact + ((size_t)bh * s.n_flat + blockIdx.x) * s.k_ns;
-    for (int p = tid; p < s.N_kv; p += NT) emask[p] = 0;
+  int* etab = dyn_lds;                            // flat: [k_ns]
+  int* ptab = dyn_lds + (MODE == kFlat ? s.k_ns : 0);   // flat: [N_kv]
+  if (MODE == kSharp) {
+    for (int q = tid; q < s.N_kv; q += NT) {
+      const int j = kept_id(s, ctx_row, q);
+      int st = 0, n = 0;
+      if (j >= 0) isa_block_range(s, j, st, n);
+      jtab[q] = (st << 7) | n;
+    }
+    __syncthreads();
+  } else if (MODE == kFlat) {
+    const int32_t* exact_row = a.exact + ((size_t)bh * s.n_flat + blockIdx.x) * s.k_ns;
+    for (int q = tid; q < s.k_ns; q += NT) {
+      const int j = exact_row[q];
+      int st = 0, n = 0;
+      if (j >= 0 && j < s.N) isa_block_range(s, j, st, n);
+      etab[q] = (st << 7) | n;
+    }
+    for (int p = tid; p < s.N_kv; p += NT) {
+      const int j = kept_id(s, ctx_row, p);
+      int st = 0, n = 0;
+      if (j >= 0) isa_block_range(s, j, st, n);
+      ptab[p] = j >= 0 ? ((j << 8) | (n << 1)) : 1;
+    }
     __syncthreads();
     for (int q = tid; q < s.k_ns; q += NT) {
       const int j = exact_row[q];
@@ -188,105 +278,51 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
         }
         if (lo < s.k_ctx && ctx_row[lo] == j) p = s.N_src + lo;
       }
-      if (p >= 0) emask[p] = 1;
+      if (p >= 0) ptab[p] |= 1;
     }
     __syncthreads();
   }
 
-  // ---- key tile source: row pointers (null = padding) and additive logit
-  const int per = kKeyTile / b;   // blocks per key tile (exact tiles)
-  auto slot_src = [&](int t, int slot, const uint16_t*& kp, const uint16_t*& vp, float& bias) {
-    kp = nullptr;
-    vp = nullptr;
-    bias = -INFINITY;
-    if (MODE == kDense) {
-      const int tok = t * kKeyTile + slot;
-      if (tok < s.L) {
-        kp = a.K + (head + tok) * D;
-        vp = a.V + (head + tok) * D;
-        bias = 0.0f;
-      }
-      return;
-    }
-    if (MODE == kFlat && t >= a.ntiles_exact) {
-      const int p = (t - a.ntiles_exact) * kKeyTile + slot;
-      if (p < s.N_kv && !emask[p]) {
-        const int j = kept_id(s, ctx_row, p);
-        if (j >= 0) {
-          int st, n;
-          isa_block_range(s, j, st, n);
-          const size_t row = ((size_t)bh * s.N + j) * D;
-          kp = a.kcb + row;
-          vp = a.vcb + row;
-          bias = __log2f((float)n);
-        }
-      }
-      return;
-    }
-    const int q = t * per + slot / b, o = slot % b;
-    int j = -1;
-    if (MODE == kSharp) {
-      if (q < s.N_kv) j = kept_id(s, ctx_row, q);
-    } else {
-      if (q < s.k_ns) {
-        j = exact_row[q];
-        if (j < 0 || j >= s.N) j = -1;
-      }
-    }
-    if (j >= 0) {
-      int st, n;
-      isa_block_range(s, j, st, n);
-      if (o < n) {
-        kp = a.K + (head + st + o) * D;
-        vp = a.V + (head + st + o) * D;
-        bias = 0.0f;
-      }
-    }
-  };
-
-  // Whether tile t carries any non-zero additive logit (uniform).
-  auto tile_has_bias = [&](int t) -> bool {
-    if (MODE == kDense) return (t + 1) * kKeyTile > s.L;
-    if (MODE == kFlat && t >= a.ntiles_exact) return true;
-    for (int u = 0; u < per; ++u) {
-      const int q = t * per + u;
-      int j;
-      if (MODE == kSharp) j = q < s.N_kv ? kept_id(s, ctx_row, q) : -1;
-      else j = q < s.k_ns ? exact_row[q] : -1;
-      if (j < 0 || j >= s.N || block_is_partial(s, j)) return true;
-    }
-    return false;
-  };
+  // ---- key tile source
+  const int per = kKeyTile >> lb;   // blocks per key tile (exact tiles)
+  TileCtx tc;
+  tc.K = a.K + head * D;
+  tc.V = a.V + head * D;
+  tc.kc = (MODE == kFlat) ? a.kcb + (size_t)bh * s.N * D : nullptr;
+  tc.vc = (MODE == kFlat) ? a.vcb + (size_t)bh * s.N * D : nullptr;
+  tc.tab = (MODE == kSharp) ? jtab : etab;
+  tc.ptab = ptab;
+  tc.ntab = (MODE == kSharp) ? s.N_kv : s.k_ns;
+  tc.L = s.L;
+  tc.N_kv = s.N_kv;
+  tc.b = b;
+  tc.lb = lb;
+  tc.per = per;
+  tc.ntiles_exact = a.ntiles_exact;
 
   uint4 kr[CH], vr[CH];
   float br[CH];
+  uint32_t vmask[CH];     // all ones for a real key, zero for padding
   const int c8 = tid % CPR;
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int slot = (tid + i * NT) / CPR;
-      const uint16_t *kp, *vp;
-      float bias;
-      slot_src(t, slot, kp, vp, bias);
-      br[i] = bias;
-      if (kp) {
-        kr[i] = *reinterpret_cast<const uint4*>(kp + c8 * 8);
-        vr[i] = *reinterpret_cast<const uint4*>(vp + c8 * 8);
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int slot = (tid + i * NT) / CPR;
-      *reinterpret_cast<uint4*>(&k_lds[buf][slot * KSTR + c8 * 16]) = kr[i];
-      *reinterpret_cast<uint4*>(&v_lds[buf][slot * VSTR + c8 * 16]) = vr[i];
-      if (c8 == 0) bias_lds[buf][slot] = br[i];
-    }
-  };
+
+#define ISA_LOAD_TILE(T)                                                        \
+  _Pragma("unroll") for (int i = 0; i < CH; ++i) {                              \
+    const SlotSrc ss = slot_src<D, MODE>(tc, (T), (tid + i * NT) / CPR);        \
+    vmask[i] = ss.valid ? 0xffffffffu : 0u;                                     \
+    br[i] = ss.bias;                                                            \
+    kr[i] = *reinterpret_cast<const uint4*>(ss.k + c8 * 8);                     \
+    vr[i] = *reinterpret_cast<const uint4*>(ss.v + c8 * 8);                     \
+  }
+#define ISA_STORE_TILE(BUF)                                                     \
+  _Pragma("unroll") for (int i = 0; i < CH; ++i) {                              \
+    const int slot = (tid + i * NT) / CPR;                                      \
+    const uint32_t m = vmask[i];                                                \
+    *reinterpret_cast<uint4*>(&k_lds[(BUF)][slot * KSTR + c8 * 16]) =           \
+        make_uint4(kr[i].x & m, kr[i].y & m, kr[i].z & m, kr[i].w & m);         \
+    *reinterpret_cast<uint4*>(&v_lds[(BUF)][slot * VSTR + c8 * 16]) =           \
+        make_uint4(vr[i].x & m, vr[i].y & m, vr[i].z & m, vr[i].w & m);         \
+    if (c8 == 0) bias_lds[(BUF)][slot] = br[i];                                 \
+  }
 
   const float cscale = kLog2e / sqrtf((float)D);
   float m[QT], lsum[QT];
@@ -299,14 +335,14 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  load_tile(0);
-  store_tile(0);
+  ISA_LOAD_TILE(0)
+  ISA_STORE_TILE(0)
   const int ntiles = a.ntiles;
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1);
-    const bool has_bias = tile_has_bias(t);
+    if (more) { ISA_LOAD_TILE(t + 1) }
+    const bool has_bias = tile_has_bias<MODE>(tc, t);
     __syncthreads();
     const char* kb = k_lds[buf];
     const char* vb = v_lds[buf];
@@ -316,6 +352,14 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) sacc[qt][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    // The first wave of each SIMD takes the matrix core first, so the second
+    // one runs its softmax while the first multiplies, and vice versa.
+    const bool lead = wave < NWAVES / 2;
+    if (NWAVES >= 8 && lead) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -325,6 +369,12 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
         for (int qt = 0; qt < QT; ++qt)
           sacc[qt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qt][kk], sacc[qt][mt], 0, 0, 0);
       }
+    }
+
+    if (NWAVES >= 8 && lead) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     bf16x8_t pb[QT][2];
@@ -388,8 +438,11 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
       }
     }
 
-    if (more) store_tile(buf ^ 1);
+    if (more) { ISA_STORE_TILE(buf ^ 1) }
   }
+
+#undef ISA_LOAD_TILE
+#undef ISA_STORE_TILE
 
   // ---- normalise and write the owned rows
 #pragma unroll
@@ -411,7 +464,16 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
 
 template <int D, int MODE, int QT, int NWAVES>
 hipError_t launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  attn_kernel<D, MODE, QT, NWAVES><<<grid, NWAVES * 64, 0, st>>>(a);
+  size_t dyn = 0;
+  if (MODE == kFlat) {
+    dyn = (size_t)(a.s.k_ns + a.s.N_kv) * sizeof(int);
+    // Raise the dynamic LDS limit once per instantiation (host-side only).
+    static hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&attn_kernel<D, MODE, QT, NWAVES>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * ISA_MAX_NKV * sizeof(int)));
+    if (attr != hipSuccess) return attr;
+  }
+  attn_kernel<D, MODE, QT, NWAVES><<<grid, NWAVES * 64, dyn, st>>>(a);
   return hipGetLastError();
 }
 
