@@ -33,6 +33,7 @@ def hipcc() -> str:
 def compile_flags() -> list[str]:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-fno-honor-nans", "-mno-amdgpu-ieee",
             "-fvisibility=hidden", f"-I{INCLUDE}", f"-I{CSRC}", "-Wno-unused-result"]
 
 

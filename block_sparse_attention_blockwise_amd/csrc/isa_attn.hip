@@ -15,19 +15,26 @@
 //
 // Work decomposition (CDNA4, wave64):
 //   * a workgroup owns ROWS query rows; each wave owns 16*QT rows;
-//   * key tiles of 64 keys are staged in LDS, double buffered: global loads
-//     of tile t+1 are in flight while tile t is consumed;
+//   * key tiles of 64 keys are staged in LDS; global loads of a later tile
+//     are in flight while the current one is consumed;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q
 //     fragments kept in registers); lane (g = lane/16, c = lane%16) then holds
-//     4 keys of each 16-key sub-tile for query c, so the row max and row sum
-//     need only two cross-lane swaps (v_permlane16/32_swap);
+//     4 keys of each 16-key sub-tile for query c, so the row max needs only
+//     two cross-lane swaps (v_permlane16/32_swap) and the row sum none until
+//     the end;
 //   * the probabilities, rounded to bf16, are already in the B-operand layout
 //     of O^T += V^T P^T; the V^T operand comes from row-major V in LDS through
 //     the transposing LDS read ds_read_b64_tr_b16;
 //   * O^T accumulates in fp32 with one query per lane, so the online-softmax
 //     rescale is a per-lane scalar multiply, skipped unless some row max grew
 //     by more than 2^8 (the running max is a reference, not the exact max);
-//   * exp is exp2 with log2(e)/sqrt(D) folded into one multiply.
+//   * exp is exp2 with log2(e)/sqrt(D) folded into the exponent's fma.
+// The sharp and dense paths are software pipelined: while the softmax of
+// tile t runs on the vector ALUs, the matrix cores already compute the scores
+// of tile t+1 (K double buffered, V and the per-key logit offsets triple
+// buffered in LDS, one workgroup barrier per tile). Tiles that need additive
+// logits (padding, partial blocks) are ordered last so the steady state runs
+// without them.
 // K rows are padded to 2D+16 bytes and V rows to 2D+32 bytes in LDS so the
 // 16-byte K reads and the 8-byte transposing V reads are bank-conflict free.
 #include "isa_internal.h"
@@ -37,6 +44,9 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef short short4_t __attribute__((__vector_size__(8)));
 typedef float float4_t __attribute__((__vector_size__(16)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+struct bf16x2x4_t { bf16x2_t a, b, c, d; };
 
 enum : int { kDense = 0, kSharp = 1, kFlat = 2 };
 
@@ -44,6 +54,7 @@ constexpr int kKeyTile = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 constexpr float kMinusBig = -1.0e30f;
+__device__ constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 struct AttnArgs {
   IsaShape s;                // dense: B, H, L, D only
@@ -59,6 +70,7 @@ struct AttnArgs {
   int n_q;
   int ntiles_exact;
   int ntiles;
+  int ntiles_plain;          // sharp/dense: leading tiles with no additive logit
 };
 
 __device__ inline float xor16_max(float x) {
@@ -170,7 +182,131 @@ __device__ inline bool tile_has_bias(const TileCtx& c, int t) {
   return any;
 }
 
-template <int D, int MODE, int QT, int NWAVES>
+// ---------------------------------------------------------------- tile math
+// S^T tile: s[qt][mt][j] = K[16mt + 4g + j] . Q[16qt + c] for the 64 keys of
+// the LDS tile at `kb` (raw dot products).
+template <int D, int QT>
+__device__ __forceinline__ void qk_tile(const char* kb, const bf16x8_t (&qf)[QT][D / 32],
+                                        float4_t (&s)[QT][4], int g, int c16) {
+  constexpr int KSTR = 2 * D + 16;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) s[qt][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kb + (16 * mt + c16) * KSTR + (32 * kk + 8 * g) * 2);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        s[qt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qt][kk], s[qt][mt], 0, 0, 0);
+    }
+  }
+}
+
+// Turns raw scores into log2-unit logits with the per-key offsets.
+template <int QT>
+__device__ __forceinline__ void apply_logit_offsets(float4_t (&s)[QT][4], const float* bias,
+                                                    float cscale, int g) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const float4_t bv = *reinterpret_cast<const float4_t*>(bias + 16 * mt + 4 * g);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[qt][mt][j] = __builtin_fmaf(s[qt][mt][j], cscale, bv[j]);
+  }
+}
+
+// Row maximum over the 64 keys of the tile, times `xs` (log2 units).
+template <int QT>
+__device__ __forceinline__ void row_max(const float4_t (&s)[QT][4], float xs, float (&mx)[QT]) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float a = __builtin_fmaxf(s[qt][0][0], __builtin_fmaxf(s[qt][0][1], s[qt][0][2]));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][0][3], s[qt][1][0]));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][1][1], s[qt][1][2]));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][1][3], s[qt][2][0]));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][2][1], s[qt][2][2]));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][2][3], s[qt][3][0]));
+    a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][3][1], s[qt][3][2]));
+    a = __builtin_fmaxf(a, s[qt][3][3]);
+    a = xor16_max(a);
+    a = xor32_max(a);
+    mx[qt] = a * xs;
+  }
+}
+
+// Lazy online-softmax rescale: only when some row max exceeds the running
+// reference by more than kRescaleSlack (wave-uniform branch).
+template <int D, int QT>
+__device__ __forceinline__ void rescale(const float (&mx)[QT], float (&m)[QT], float (&lsum)[QT],
+                                        float4_t (&o)[QT][D / 16]) {
+  bool need = false;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) need |= mx[qt] > m[qt] + kRescaleSlack;
+  if (__ballot(need)) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float mn = fmaxf(m[qt], mx[qt]);
+      const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
+      lsum[qt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[qt][dt] *= alpha;
+      m[qt] = mn;
+    }
+  }
+}
+
+// p = exp2(s*xs - m), rounded to bf16 and packed as the B operand of the PV
+// product; the per-lane partial row sums accumulate the rounded values.
+template <int QT>
+__device__ __forceinline__ void exp_pack(const float4_t (&s)[QT][4], float xs, const float (&m)[QT],
+                                         float (&lsum)[QT], bf16x8_t (&pb)[QT][2]) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float negm = -m[qt];
+    float ps = lsum[qt];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x2_t h[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i0 = 8 * kc + 2 * u;   // element index within the 16 held values
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][i0 >> 2][i0 & 3], xs, negm));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][(i0 + 1) >> 2][(i0 + 1) & 3], xs, negm));
+        h[u] = __builtin_convertvector((float2_t){x0, x1}, bf16x2_t);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(h[u], kOnes2, ps, false);
+      }
+      pb[qt][kc] = __builtin_bit_cast(bf16x8_t, (bf16x2x4_t){h[0], h[1], h[2], h[3]});
+    }
+    lsum[qt] = ps;
+  }
+}
+
+// O^T += V^T P^T for the 64 keys of the LDS tile at `vb`.
+template <int D, int QT>
+__device__ __forceinline__ void pv_tile(const char* vb, const bf16x8_t (&pb)[QT][2],
+                                        float4_t (&o)[QT][D / 16], int g, int c16) {
+  constexpr int VSTR = 2 * D + 32;
+  const int tr_row = 4 * g + (c16 >> 2);
+  const int tr_col = 4 * (c16 & 3);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const short4_t lo = lds_read_tr(vb + (32 * kc + tr_row) * VSTR + (16 * dt + tr_col) * 2);
+      const short4_t hi = lds_read_tr(vb + (32 * kc + 16 + tr_row) * VSTR + (16 * dt + tr_col) * 2);
+      const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qt][kc], o[qt][dt], 0, 0, 0);
+    }
+  }
+}
+
+template <int D, int MODE, int QT, int NWAVES, bool PIPE>
 __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
   constexpr int NT = NWAVES * 64;
   constexpr int KSTR = 2 * D + 16;
@@ -184,9 +320,10 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
   static_assert(CH >= 1 && (kKeyTile * CPR) % NT == 0, "tile split");
   static_assert(NT % CPR == 0, "chunk column must be fixed per thread");
 
+  constexpr int NVB = PIPE ? 3 : 2;         // V / logit-offset buffers
   __shared__ __attribute__((aligned(16))) char k_lds[2][kKeyTile * KSTR];
-  __shared__ __attribute__((aligned(16))) char v_lds[2][kKeyTile * VSTR];
-  __shared__ float bias_lds[2][kKeyTile];
+  __shared__ __attribute__((aligned(16))) char v_lds[NVB][kKeyTile * VSTR];
+  __shared__ __attribute__((aligned(16))) float bias_lds[NVB][kKeyTile];
   // Sharp path: token range of every kept block, packed (start << 7) | n_j,
   // indexed by position in J. Flat path (dynamic LDS): the same for E_i, then
   // (j << 8) | (n_j << 1) | in_E for every position of J.
@@ -243,11 +380,21 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
   int* etab = dyn_lds;                            // flat: [k_ns]
   int* ptab = dyn_lds + (MODE == kFlat ? s.k_ns : 0);   // flat: [N_kv]
   if (MODE == kSharp) {
+    // Kept blocks in J order, except that the (at most two) partial blocks
+    // move to the end: the last source block and, if kept, the last context
+    // block, whose positions in J are N_src-1 and N_kv-1.
+    const int p1 = (s.L_src % b) ? s.N_src - 1 : -1;
+    const int p2 = (s.L_ctx % b && s.k_ctx > 0 && ctx_row[s.k_ctx - 1] == s.N - 1) ? s.N_kv - 1 : -1;
+    const int npart = (p1 >= 0) + (p2 >= 0);
     for (int q = tid; q < s.N_kv; q += NT) {
       const int j = kept_id(s, ctx_row, q);
       int st = 0, n = 0;
       if (j >= 0) isa_block_range(s, j, st, n);
-      jtab[q] = (st << 7) | n;
+      int dest;
+      if (q == p1) dest = s.N_kv - npart;
+      else if (q == p2) dest = s.N_kv - 1;
+      else dest = q - ((p1 >= 0 && q > p1) ? 1 : 0);
+      jtab[dest] = (st << 7) | n;
     }
     __syncthreads();
   } else if (MODE == kFlat) {
@@ -313,15 +460,15 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
     kr[i] = *reinterpret_cast<const uint4*>(ss.k + c8 * 8);                     \
     vr[i] = *reinterpret_cast<const uint4*>(ss.v + c8 * 8);                     \
   }
-#define ISA_STORE_TILE(BUF)                                                     \
+#define ISA_STORE_TILE(KB, VB)                                                  \
   _Pragma("unroll") for (int i = 0; i < CH; ++i) {                              \
     const int slot = (tid + i * NT) / CPR;                                      \
     const uint32_t m = vmask[i];                                                \
-    *reinterpret_cast<uint4*>(&k_lds[(BUF)][slot * KSTR + c8 * 16]) =           \
+    *reinterpret_cast<uint4*>(&k_lds[(KB)][slot * KSTR + c8 * 16]) =            \
         make_uint4(kr[i].x & m, kr[i].y & m, kr[i].z & m, kr[i].w & m);         \
-    *reinterpret_cast<uint4*>(&v_lds[(BUF)][slot * VSTR + c8 * 16]) =           \
+    *reinterpret_cast<uint4*>(&v_lds[(VB)][slot * VSTR + c8 * 16]) =            \
         make_uint4(vr[i].x & m, vr[i].y & m, vr[i].z & m, vr[i].w & m);         \
-    if (c8 == 0) bias_lds[(BUF)][slot] = br[i];                                 \
+    if (c8 == 0) bias_lds[(VB)][slot] = br[i];                                  \
   }
 
   const float cscale = kLog2e / sqrtf((float)D);
@@ -334,113 +481,97 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
-
-  ISA_LOAD_TILE(0)
-  ISA_STORE_TILE(0)
   const int ntiles = a.ntiles;
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < ntiles;
-    if (more) { ISA_LOAD_TILE(t + 1) }
-    const bool has_bias = tile_has_bias<MODE>(tc, t);
-    __syncthreads();
-    const char* kb = k_lds[buf];
-    const char* vb = v_lds[buf];
+  bf16x8_t pb[QT][2];
 
-    float4_t sacc[QT][4];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) sacc[qt][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-    // The first wave of each SIMD takes the matrix core first, so the second
-    // one runs its softmax while the first multiplies, and vice versa.
-    const bool lead = wave < NWAVES / 2;
-    if (NWAVES >= 8 && lead) {
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(2);
-      __builtin_amdgcn_sched_barrier(0);
+  if (!PIPE) {
+    ISA_LOAD_TILE(0)
+    ISA_STORE_TILE(0, 0)
+    for (int t = 0; t < ntiles; ++t) {
+      const int buf = t & 1;
+      const bool more = t + 1 < ntiles;
+      if (more) { ISA_LOAD_TILE(t + 1) }
+      const bool hb = tile_has_bias<MODE>(tc, t);
+      __syncthreads();
+      float4_t sc[QT][4];
+      qk_tile<D, QT>(k_lds[buf], qf, sc, g, c16);
+      if (hb) apply_logit_offsets<QT>(sc, bias_lds[buf], cscale, g);
+      float mx[QT];
+      row_max<QT>(sc, hb ? 1.0f : cscale, mx);
+      rescale<D, QT>(mx, m, lsum, oacc);
+      exp_pack<QT>(sc, hb ? 1.0f : cscale, m, lsum, pb);
+      pv_tile<D, QT>(v_lds[buf], pb, oacc, g, c16);
+      if (more) { ISA_STORE_TILE(buf ^ 1, buf ^ 1) }
     }
+  } else {
+    // Steady state: the leading tiles, which carry no additive logits.
+    const int P = a.ntiles_plain;
+    if (P > 0) {
+      // Prologue: tiles 0 and 1 in LDS, scores of tile 0 in registers.
+      ISA_LOAD_TILE(0)
+      ISA_STORE_TILE(0, 0)
+      if (P > 1) {
+        ISA_LOAD_TILE(1)
+        ISA_STORE_TILE(1, 1)
+      }
+      __syncthreads();
+      float4_t scur[QT][4], snext[QT][4];
+      qk_tile<D, QT>(k_lds[0], qf, scur, g, c16);
+      float mx[QT];
+      row_max<QT>(scur, cscale, mx);
+      int vb_cur = 0, vb_load = 2;   // t % 3 and (t + 2) % 3
+      for (int t = 0; t < P; ++t) {
+        __syncthreads();
+        const bool more2 = t + 2 < P;
+        if (more2) { ISA_LOAD_TILE(t + 2) }
+        rescale<D, QT>(mx, m, lsum, oacc);
+        // matrix cores: scores of tile t+1 (stale data on the last tile,
+        // unused); vector ALUs meanwhile: probabilities of tile t. The group
+        // barriers interleave them: per step one K read, two MFMAs, six VALU
+        // ops.
+        qk_tile<D, QT>(k_lds[(t + 1) & 1], qf, snext, g, c16);
+        exp_pack<QT>(scur, cscale, m, lsum, pb);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+        // matrix cores: O += V P of tile t; vector ALUs: row max of tile t+1.
+        pv_tile<D, QT>(v_lds[vb_cur], pb, oacc, g, c16);
+        row_max<QT>(snext, cscale, mx);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kb + (16 * mt + c16) * KSTR + (32 * kk + 8 * g) * 2);
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
+        }
+        if (more2) { ISA_STORE_TILE(t & 1, vb_load) }
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          sacc[qt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qt][kk], sacc[qt][mt], 0, 0, 0);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) scur[qt][mt] = snext[qt][mt];
+        vb_cur = vb_cur == 2 ? 0 : vb_cur + 1;
+        vb_load = vb_load == 2 ? 0 : vb_load + 1;
       }
+      __syncthreads();
     }
-
-    if (NWAVES >= 8 && lead) {
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
-      __builtin_amdgcn_sched_barrier(0);
+    // Tail: the few tiles with padding or partial blocks, one at a time.
+    for (int t = P; t < ntiles; ++t) {
+      ISA_LOAD_TILE(t)
+      ISA_STORE_TILE(0, 0)
+      __syncthreads();
+      float4_t sc[QT][4];
+      qk_tile<D, QT>(k_lds[0], qf, sc, g, c16);
+      apply_logit_offsets<QT>(sc, bias_lds[0], cscale, g);
+      float mx[QT];
+      row_max<QT>(sc, 1.0f, mx);
+      rescale<D, QT>(mx, m, lsum, oacc);
+      exp_pack<QT>(sc, 1.0f, m, lsum, pb);
+      pv_tile<D, QT>(v_lds[0], pb, oacc, g, c16);
+      __syncthreads();
     }
-
-    bf16x8_t pb[QT][2];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float x[16];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[4 * mt + j] = sacc[qt][mt][j] * cscale;
-      if (has_bias) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) x[4 * mt + j] += bias_lds[buf][16 * mt + 4 * g + j];
-      }
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-      mx = xor16_max(mx);
-      mx = xor32_max(mx);
-      if (__ballot(mx > m[qt] + kRescaleSlack)) {
-        const float mn = fmaxf(m[qt], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
-        lsum[qt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= alpha;
-        m[qt] = mn;
-      }
-      float ps = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = __builtin_amdgcn_exp2f(x[i] - m[qt]);
-        ps += x[i];
-      }
-      lsum[qt] += ps;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        uint4 w;
-        w.x = pack_bf16x2(x[8 * kc + 0], x[8 * kc + 1]);
-        w.y = pack_bf16x2(x[8 * kc + 2], x[8 * kc + 3]);
-        w.z = pack_bf16x2(x[8 * kc + 4], x[8 * kc + 5]);
-        w.w = pack_bf16x2(x[8 * kc + 6], x[8 * kc + 7]);
-        pb[qt][kc] = __builtin_bit_cast(bf16x8_t, w);
-      }
-    }
-
-    const int tr_row = 4 * g + (c16 >> 2);
-    const int tr_col = 4 * (c16 & 3);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const short4_t lo = lds_read_tr(vb + (32 * kc + tr_row) * VSTR + (16 * dt + tr_col) * 2);
-        const short4_t hi = lds_read_tr(vb + (32 * kc + 16 + tr_row) * VSTR + (16 * dt + tr_col) * 2);
-        const bf16x8_t va = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qt][kc], oacc[qt][dt], 0, 0, 0);
-      }
-    }
-
-    if (more) { ISA_STORE_TILE(buf ^ 1) }
   }
-
 #undef ISA_LOAD_TILE
 #undef ISA_STORE_TILE
 
@@ -462,18 +593,18 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int MODE, int QT, int NWAVES>
+template <int D, int MODE, int QT, int NWAVES, bool PIPE>
 hipError_t launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
   size_t dyn = 0;
   if (MODE == kFlat) {
     dyn = (size_t)(a.s.k_ns + a.s.N_kv) * sizeof(int);
     // Raise the dynamic LDS limit once per instantiation (host-side only).
     static hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&attn_kernel<D, MODE, QT, NWAVES>),
+        reinterpret_cast<const void*>(&attn_kernel<D, MODE, QT, NWAVES, PIPE>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * ISA_MAX_NKV * sizeof(int)));
     if (attr != hipSuccess) return attr;
   }
-  attn_kernel<D, MODE, QT, NWAVES><<<grid, NWAVES * 64, dyn, st>>>(a);
+  attn_kernel<D, MODE, QT, NWAVES, PIPE><<<grid, NWAVES * 64, dyn, st>>>(a);
   return hipGetLastError();
 }
 
@@ -499,10 +630,17 @@ hipError_t isa_launch_sharp_attn(const IsaShape& s, const uint16_t* Q, const uin
   a.qlist = sharp_idx;
   a.n_q = s.n_sharp;
   a.ntiles = (s.N_kv * s.b + kKeyTile - 1) / kKeyTile;
+  {
+    // tiles made only of full kept blocks (partial blocks are ordered last)
+    int npart = (s.L_src % s.b) ? 1 : 0;
+    if (s.L_ctx % s.b) npart += 1;   // conservative: the last context block may be kept
+    a.ntiles_plain = (s.N_kv - npart) * s.b / kKeyTile;
+  }
   const int rows = 8 * 32;
   const int blocks_per_wg = rows / s.b;
   dim3 grid((s.n_sharp + blocks_per_wg - 1) / blocks_per_wg, s.B * s.H);
-  return s.D == 128 ? launch<128, kSharp, 2, 8>(a, grid, st) : launch<64, kSharp, 2, 8>(a, grid, st);
+  return s.D == 128 ? launch<128, kSharp, 2, 8, true>(a, grid, st)
+                    : launch<64, kSharp, 2, 8, true>(a, grid, st);
 }
 
 hipError_t isa_launch_flat_attn(const IsaShape& s, const uint16_t* Q, const uint16_t* K,
@@ -523,8 +661,10 @@ hipError_t isa_launch_flat_attn(const IsaShape& s, const uint16_t* Q, const uint
   a.ntiles = a.ntiles_exact + pooled;
   dim3 grid(s.n_flat, s.B * s.H);
   if (s.b == 64)
-    return s.D == 128 ? launch<128, kFlat, 1, 4>(a, grid, st) : launch<64, kFlat, 1, 4>(a, grid, st);
-  return s.D == 128 ? launch<128, kFlat, 1, 2>(a, grid, st) : launch<64, kFlat, 1, 2>(a, grid, st);
+    return s.D == 128 ? launch<128, kFlat, 1, 4, false>(a, grid, st)
+                      : launch<64, kFlat, 1, 4, false>(a, grid, st);
+  return s.D == 128 ? launch<128, kFlat, 1, 2, false>(a, grid, st)
+                    : launch<64, kFlat, 1, 2, false>(a, grid, st);
 }
 
 hipError_t isa_launch_dense_attn(int B, int H, int L, int D, const uint16_t* Q,
@@ -539,6 +679,8 @@ hipError_t isa_launch_dense_attn(int B, int H, int L, int D, const uint16_t* Q,
   s.b = kKeyTile;
   AttnArgs a = base_args(s, Q, K, V, O);
   a.ntiles = (L + kKeyTile - 1) / kKeyTile;
+  a.ntiles_plain = L / kKeyTile;
   dim3 grid((L + 255) / 256, B * H);
-  return D == 128 ? launch<128, kDense, 2, 8>(a, grid, st) : launch<64, kDense, 2, 8>(a, grid, st);
+  return D == 128 ? launch<128, kDense, 2, 8, true>(a, grid, st)
+                  : launch<64, kDense, 2, 8, true>(a, grid, st);
 }
