@@ -307,7 +307,8 @@ __device__ __forceinline__ void pv_tile(const char* vb, const bf16x8_t (&pb)[QT]
 }
 
 template <int D, int MODE, int QT, int NWAVES, bool PIPE>
-__global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(PIPE ? 2 : 3)))
+void attn_kernel(AttnArgs a) {
   constexpr int NT = NWAVES * 64;
   constexpr int KSTR = 2 * D + 16;
   constexpr int VSTR = 2 * D + 32;
@@ -320,8 +321,9 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
   static_assert(CH >= 1 && (kKeyTile * CPR) % NT == 0, "tile split");
   static_assert(NT % CPR == 0, "chunk column must be fixed per thread");
 
-  constexpr int NVB = PIPE ? 3 : 2;         // V / logit-offset buffers
-  __shared__ __attribute__((aligned(16))) char k_lds[2][kKeyTile * KSTR];
+  constexpr int NKB = PIPE ? 2 : 1;         // K buffers
+  constexpr int NVB = PIPE ? 3 : 1;         // V / logit-offset buffers
+  __shared__ __attribute__((aligned(16))) char k_lds[NKB][kKeyTile * KSTR];
   __shared__ __attribute__((aligned(16))) char v_lds[NVB][kKeyTile * VSTR];
   __shared__ __attribute__((aligned(16))) float bias_lds[NVB][kKeyTile];
   // Sharp path: token range of every kept block, packed (start << 7) | n_j,
@@ -485,23 +487,22 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_kernel(AttnArgs a) {
   bf16x8_t pb[QT][2];
 
   if (!PIPE) {
-    ISA_LOAD_TILE(0)
-    ISA_STORE_TILE(0, 0)
+    // One LDS buffer; latency is hidden by the other workgroups resident on
+    // the compute unit (small register and LDS footprint).
     for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
-      const bool more = t + 1 < ntiles;
-      if (more) { ISA_LOAD_TILE(t + 1) }
+      ISA_LOAD_TILE(t)
       const bool hb = tile_has_bias<MODE>(tc, t);
+      if (t > 0) __syncthreads();   // previous tile fully consumed
+      ISA_STORE_TILE(0, 0)
       __syncthreads();
       float4_t sc[QT][4];
-      qk_tile<D, QT>(k_lds[buf], qf, sc, g, c16);
-      if (hb) apply_logit_offsets<QT>(sc, bias_lds[buf], cscale, g);
+      qk_tile<D, QT>(k_lds[0], qf, sc, g, c16);
+      if (hb) apply_logit_offsets<QT>(sc, bias_lds[0], cscale, g);
       float mx[QT];
       row_max<QT>(sc, hb ? 1.0f : cscale, mx);
       rescale<D, QT>(mx, m, lsum, oacc);
       exp_pack<QT>(sc, hb ? 1.0f : cscale, m, lsum, pb);
-      pv_tile<D, QT>(v_lds[buf], pb, oacc, g, c16);
-      if (more) { ISA_STORE_TILE(buf ^ 1, buf ^ 1) }
+      pv_tile<D, QT>(v_lds[0], pb, oacc, g, c16);
     }
   } else {
     // Steady state: the leading tiles, which carry no additive logits.

@@ -180,7 +180,9 @@ __global__ __launch_bounds__(kCtxThreads) void ctx_topk_kernel(IsaShape s, const
 }
 
 // ------------------------------------------------- step (1) coarse rows
-constexpr int kCoarseRows = 16, kCoarseCols = 64, kCoarseDc = 32;
+// S[i, p] = Qc_i . Kc_{J[p]} / sqrt(D) in fp64 for a 64 x 64 tile per
+// workgroup; each thread accumulates a 4 x 4 block from LDS-staged slices.
+constexpr int kCoarseRows = 64, kCoarseCols = 64, kCoarseDc = 16;
 
 __global__ __launch_bounds__(256) void coarse_rows_kernel(IsaShape s, const double* __restrict__ qc,
                                                           const double* __restrict__ kc,
@@ -188,8 +190,8 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(IsaShape s, const doub
                                                           double* __restrict__ srows) {
   const int i0 = blockIdx.x * kCoarseRows, p0 = blockIdx.y * kCoarseCols, bh = blockIdx.z;
   const int D = s.D;
-  __shared__ double qs[kCoarseRows][kCoarseDc + 1];
-  __shared__ double ks[kCoarseCols][kCoarseDc + 1];
+  __shared__ double qs[kCoarseDc][kCoarseRows + 1];
+  __shared__ double ks[kCoarseDc][kCoarseCols + 1];
   __shared__ int gid[kCoarseCols];
   const int32_t* ctx_row = ctx_idx + (size_t)bh * s.k_ctx;
   if (threadIdx.x < kCoarseCols) {
@@ -197,34 +199,48 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(IsaShape s, const doub
     int g = p < s.N_kv ? kept_block_id(s, ctx_row, p) : -1;
     gid[threadIdx.x] = (g >= 0 && g < s.N) ? g : -1;   // ids outside [0, N) read as zero rows
   }
-  const int col = threadIdx.x % kCoarseCols, rg = threadIdx.x / kCoarseCols;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;   // rows 4tr.., cols tc + 16c
+  double acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
   __syncthreads();
+  const int lr = threadIdx.x >> 2, ld = (threadIdx.x & 3) * 4;   // loader: row, 4 dims
   for (int d0 = 0; d0 < D; d0 += kCoarseDc) {
-    for (int t = threadIdx.x; t < kCoarseRows * kCoarseDc; t += 256) {
-      const int r = t / kCoarseDc, dd = t % kCoarseDc, i = i0 + r;
-      qs[r][dd] = i < s.N ? qc[((size_t)bh * s.N + i) * D + d0 + dd] : 0.0;
-    }
-    for (int t = threadIdx.x; t < kCoarseCols * kCoarseDc; t += 256) {
-      const int c = t / kCoarseDc, dd = t % kCoarseDc, g = gid[c];
-      ks[c][dd] = g >= 0 ? kc[((size_t)bh * s.N + g) * D + d0 + dd] : 0.0;
+    {
+      const int i = i0 + lr;
+      const int g = gid[lr];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        qs[ld + x][lr] = i < s.N ? qc[((size_t)bh * s.N + i) * D + d0 + ld + x] : 0.0;
+        ks[ld + x][lr] = g >= 0 ? kc[((size_t)bh * s.N + g) * D + d0 + ld + x] : 0.0;
+      }
     }
     __syncthreads();
-#pragma unroll 8
-    for (int dd = 0; dd < kCoarseDc; ++dd) {
-      const double kv = ks[col][dd];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = fma(qs[rg * 4 + r][dd], kv, acc[r]);
+    for (int dd = 0; dd < kCoarseDc; ++dd) {
+      double a[4], bv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = qs[dd][4 * tr + r];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bv[c] = ks[dd][tc + 16 * c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = fma(a[r], bv[c], acc[r][c]);
     }
     __syncthreads();
   }
   const double sq = sqrt((double)D);
-  const int p = p0 + col;
-  if (p < s.N_kv) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + rg * 4 + r;
-      if (i < s.N) srows[((size_t)bh * s.N + i) * s.N_kv + p] = acc[r] / sq;
+  for (int r = 0; r < 4; ++r) {
+    const int i = i0 + 4 * tr + r;
+    if (i >= s.N) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int p = p0 + tc + 16 * c;
+      if (p < s.N_kv) srows[((size_t)bh * s.N + i) * s.N_kv + p] = acc[r][c] / sq;
     }
   }
 }
@@ -281,31 +297,68 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(IsaShape s, const 
 }
 
 // --------------------------------------------- step (5) exact set per block
-constexpr int kFlatTopkThreads = 256;
-constexpr int kFlatTopkIPT = ISA_MAX_NKV / kFlatTopkThreads;
+// One wave selects the k largest of the n keys it holds (lower index wins
+// ties). Lane l holds items p = l + 64u, so index order is u-major,
+// lane-minor. Counting uses ballots (scalar popcounts), no workgroup barrier.
+template <int IPL>
+__device__ inline void wave_topk(const unsigned long long (&key)[IPL], int n, int k,
+                                 bool (&sel)[IPL]) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  unsigned long long T = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const unsigned long long trial = T | (1ull << bit);
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < IPL; ++u) c += __popcll(__ballot(lane + 64 * u < n && key[u] >= trial));
+    if (c >= k) T = trial;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int u = 0; u < IPL; ++u) gt += __popcll(__ballot(lane + 64 * u < n && key[u] > T));
+  const int need = k - gt;
+  int before = 0;
+#pragma unroll
+  for (int u = 0; u < IPL; ++u) {
+    const bool valid = lane + 64 * u < n;
+    const bool tie = valid && key[u] == T;
+    const unsigned long long m = __ballot(tie);
+    const int rank = before + __popcll(m & below);
+    sel[u] = (valid && key[u] > T) || (tie && rank < need);
+    before += __popcll(m);
+  }
+}
 
-__global__ __launch_bounds__(kFlatTopkThreads) void flat_topk_kernel(IsaShape s, const double* __restrict__ srows,
-                                                                     const int32_t* __restrict__ ctx_idx,
-                                                                     const int32_t* __restrict__ flat_idx,
-                                                                     int32_t* __restrict__ exact) {
-  const int r = blockIdx.x, bh = blockIdx.y;
-  __shared__ int scratch[kFlatTopkThreads / 64];
+constexpr int kFlatTopkWaves = 4;
+
+template <int IPL>
+__global__ __launch_bounds__(64 * kFlatTopkWaves) void flat_topk_kernel(IsaShape s, const double* __restrict__ srows,
+                                                                        const int32_t* __restrict__ ctx_idx,
+                                                                        const int32_t* __restrict__ flat_idx,
+                                                                        int32_t* __restrict__ exact) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * kFlatTopkWaves + (threadIdx.x >> 6), bh = blockIdx.y;
+  if (r >= s.n_flat) return;   // whole wave; no workgroup barrier below
   const int i = flat_idx[(size_t)bh * s.n_flat + r];
   const double* row = srows + ((size_t)bh * s.N + i) * s.N_kv;
-  unsigned long long key[kFlatTopkIPT];
-  bool valid[kFlatTopkIPT], sel[kFlatTopkIPT];
+  unsigned long long key[IPL];
+  bool sel[IPL];
 #pragma unroll
-  for (int u = 0; u < kFlatTopkIPT; ++u) {
-    const int p = threadIdx.x * kFlatTopkIPT + u;
-    valid[u] = p < s.N_kv;
-    key[u] = valid[u] ? order_key(row[p]) : 0;
+  for (int u = 0; u < IPL; ++u) {
+    const int p = lane + 64 * u;
+    key[u] = p < s.N_kv ? order_key(row[p]) : 0ull;
   }
-  block_topk<kFlatTopkThreads, kFlatTopkIPT>(key, valid, s.k_ns, sel, scratch);
+  wave_topk<IPL>(key, s.N_kv, s.k_ns, sel);
   const int32_t* ctx_row = ctx_idx + (size_t)bh * s.k_ctx;
-  const IsaShape sh = s;
-  block_compact<kFlatTopkThreads, kFlatTopkIPT>(
-      sel, valid, true, exact + ((size_t)bh * s.n_flat + r) * s.k_ns,
-      [sh, ctx_row](int p) { return kept_block_id(sh, ctx_row, p); }, scratch);
+  int32_t* out = exact + ((size_t)bh * s.n_flat + r) * s.k_ns;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int u = 0; u < IPL; ++u) {
+    const unsigned long long m = __ballot(sel[u]);
+    if (sel[u]) out[base + __popcll(m & below)] = kept_block_id(s, ctx_row, lane + 64 * u);
+    base += __popcll(m);
+  }
 }
 
 }  // namespace
@@ -342,7 +395,18 @@ hipError_t isa_launch_flat_topk(const IsaShape& s, const double* srows, const in
                                 const int32_t* flat_idx, int32_t* flat_exact_idx,
                                 hipStream_t st) {
   if (s.n_flat == 0 || s.k_ns == 0) return hipSuccess;
-  dim3 grid(s.n_flat, s.B * s.H);
-  flat_topk_kernel<<<grid, kFlatTopkThreads, 0, st>>>(s, srows, ctx_idx, flat_idx, flat_exact_idx);
+  dim3 grid((s.n_flat + kFlatTopkWaves - 1) / kFlatTopkWaves, s.B * s.H);
+  const int ipl = (s.N_kv + 63) / 64;
+  const int nt = 64 * kFlatTopkWaves;
+  if (ipl <= 4)
+    flat_topk_kernel<4><<<grid, nt, 0, st>>>(s, srows, ctx_idx, flat_idx, flat_exact_idx);
+  else if (ipl <= 8)
+    flat_topk_kernel<8><<<grid, nt, 0, st>>>(s, srows, ctx_idx, flat_idx, flat_exact_idx);
+  else if (ipl <= 16)
+    flat_topk_kernel<16><<<grid, nt, 0, st>>>(s, srows, ctx_idx, flat_idx, flat_exact_idx);
+  else if (ipl <= 32)
+    flat_topk_kernel<32><<<grid, nt, 0, st>>>(s, srows, ctx_idx, flat_idx, flat_exact_idx);
+  else
+    flat_topk_kernel<64><<<grid, nt, 0, st>>>(s, srows, ctx_idx, flat_idx, flat_exact_idx);
   return hipGetLastError();
 }
