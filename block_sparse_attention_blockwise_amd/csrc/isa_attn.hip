@@ -35,8 +35,8 @@
 // buffered in LDS, one workgroup barrier per tile). Tiles that need additive
 // logits (padding, partial blocks) are ordered last so the steady state runs
 // without them.
-// K rows are padded to 2D+16 bytes and V rows to 2D+32 bytes in LDS so the
-// 16-byte K reads and the 8-byte transposing V reads are bank-conflict free.
+// K and V rows are padded to 2D+32 bytes in LDS; with that stride the 16-byte
+// K reads and the 8-byte transposing V reads measure free of bank conflicts.
 #include "isa_internal.h"
 
 namespace {
@@ -188,7 +188,7 @@ __device__ inline bool tile_has_bias(const TileCtx& c, int t) {
 template <int D, int QT>
 __device__ __forceinline__ void qk_tile(const char* kb, const bf16x8_t (&qf)[QT][D / 32],
                                         float4_t (&s)[QT][4], int g, int c16) {
-  constexpr int KSTR = 2 * D + 16;
+  constexpr int KSTR = 2 * D + 32;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -310,7 +310,7 @@ template <int D, int MODE, int QT, int NWAVES, bool PIPE>
 __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(PIPE ? 2 : 3)))
 void attn_kernel(AttnArgs a) {
   constexpr int NT = NWAVES * 64;
-  constexpr int KSTR = 2 * D + 16;
+  constexpr int KSTR = 2 * D + 32;
   constexpr int VSTR = 2 * D + 32;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int CH = kKeyTile * CPR / NT;    // chunks per thread per tensor
@@ -661,6 +661,7 @@ hipError_t isa_launch_flat_attn(const IsaShape& s, const uint16_t* Q, const uint
   const int pooled = s.k_ns < s.N_kv ? (s.N_kv + kKeyTile - 1) / kKeyTile : 0;
   a.ntiles = a.ntiles_exact + pooled;
   dim3 grid(s.n_flat, s.B * s.H);
+  // one flat block per workgroup, 16 query rows per wave
   if (s.b == 64)
     return s.D == 128 ? launch<128, kFlat, 1, 4, false>(a, grid, st)
                       : launch<64, kFlat, 1, 4, false>(a, grid, st);
