@@ -51,6 +51,10 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=["sharp"], default=None,
+                    help="launch only this kernel --steps times (for counter collection)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -173,6 +177,15 @@ def main():
     import block_sparse_attention_blockwise_amd as isa
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 29   # 2^29 bf16 = 1 GiB
+        src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 2 * n, "launches": max(args.steps, 1)}))
+        return
     lib = isa.lib()
     w = WORKLOAD
     p = isa.Params(w["B"], w["H"], w["L_src"], w["L_ctx"], w["D"], w["b"], w["alpha_s"],
@@ -230,6 +243,13 @@ def main():
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
+    if args.only == "sharp":
+        for _ in range(args.steps):
+            chk("sharp", lib.isa_sharp_attn(pr, Q.data_ptr(), K.data_ptr(), V.data_ptr(), ctx.data_ptr(),
+                                            si.data_ptr(), O.data_ptr(), sp))
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "sharp", "launches": args.steps}))
+        return
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()

@@ -335,7 +335,20 @@ void attn_kernel(AttnArgs a) {
   const IsaShape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int bh = blockIdx.y;
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2). For the sharp and dense paths, whose workgroups of one head stream
+  // the same K/V, the dispatch index is remapped so that each XCD receives a
+  // contiguous run of tiles, i.e. mostly one head at a time.
+  int tile_x = blockIdx.x, bh = blockIdx.y;
+  if (MODE != kFlat) {
+    const int total = gridDim.x * gridDim.y;
+    if ((total & 7) == 0) {
+      const int id = blockIdx.x + gridDim.x * blockIdx.y;
+      const int logical = (id & 7) * (total >> 3) + (id >> 3);
+      tile_x = logical % gridDim.x;
+      bh = logical / gridDim.x;
+    }
+  }
   const size_t head = (size_t)bh * s.L;     // first token row of this (batch, head)
   const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
   const int b = s.b;
@@ -350,11 +363,11 @@ void attn_kernel(AttnArgs a) {
     qval[qt] = false;
     qtok[qt] = 0;
     if (MODE == kDense) {
-      const int tok = blockIdx.x * ROWS + lr;
+      const int tok = tile_x * ROWS + lr;
       qval[qt] = tok < s.L;
       qtok[qt] = tok;
     } else {
-      const int e = (MODE == kSharp) ? blockIdx.x * (ROWS >> lb) + (lr >> lb) : blockIdx.x;
+      const int e = (MODE == kSharp) ? tile_x * (ROWS >> lb) + (lr >> lb) : tile_x;
       const int o = (MODE == kSharp) ? (lr & (b - 1)) : lr;
       if (e < a.n_q) {
         const int j = a.qlist[(size_t)bh * a.n_q + e];
@@ -400,7 +413,7 @@ void attn_kernel(AttnArgs a) {
     }
     __syncthreads();
   } else if (MODE == kFlat) {
-    const int32_t* exact_row = a.exact + ((size_t)bh * s.n_flat + blockIdx.x) * s.k_ns;
+    const int32_t* exact_row = a.exact + ((size_t)bh * s.n_flat + tile_x) * s.k_ns;
     for (int q = tid; q < s.k_ns; q += NT) {
       const int j = exact_row[q];
       int st = 0, n = 0;
