@@ -33,13 +33,17 @@ def hipcc() -> str:
 def compile_flags() -> list[str]:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-fno-honor-nans", "-mno-amdgpu-ieee",
             "-fvisibility=hidden", f"-I{INCLUDE}", f"-I{CSRC}", "-Wno-unused-result"]
+
+
+# The attention kernels take max/min of finite or -inf logits only; without
+# NaN semantics the compiler emits v_max3 without quieting operands.
+EXTRA_FLAGS = {"isa_attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + compile_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + compile_flags() + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
