@@ -565,22 +565,34 @@ void attn_kernel(AttnArgs a) {
         rescale<D, QT>(mx, m, lsum, oacc);
         // matrix cores: scores of tile t+1 (stale data on the last tile,
         // unused); vector ALUs meanwhile: probabilities of tile t. The group
-        // barriers interleave them: per step one K read, two MFMAs, six VALU
-        // ops.
+        // barriers interleave them: per step two MFMAs, six VALU ops and one
+        // K read issued two steps ahead of its use.
         qk_tile<D, QT>(k_lds[(t + 1) & 1], qf, snext, g, c16);
         exp_pack<QT>(scur, cscale, m, lsum, pb);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two K reads ahead
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 14; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
         }
         // matrix cores: O += V P of tile t; vector ALUs: row max of tile t+1.
         pv_tile<D, QT>(v_lds[vb_cur], pb, oacc, g, c16);
         row_max<QT>(snext, cscale, mx);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);   // two V operands ahead
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 14; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
           __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
         }

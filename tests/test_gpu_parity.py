@@ -151,6 +151,21 @@ def test_small_shapes_all_rows(dev, D, b):
     _check(p, inp, res, {(0, 0), (0, 1)}, None)
 
 
+@pytest.mark.parametrize("B,H", [(2, 3), (3, 5)])
+def test_batch_and_odd_head_counts(dev, B, H):
+    """B > 1 and head counts that do not fill the XCD remap evenly."""
+    p = isa.Params(B, H, 640, 520, 128, 64, 0.25, 0.5, 0.125)
+    inp = _inputs(2, p)
+    res = _run(p, inp, dev)
+    _check(p, inp, res, {(B - 1, H - 1), (0, 1)}, None)
+    Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
+    Od = isa.dense_attn(Q, K, V).float().cpu().numpy()
+    for (bi, h) in ((0, 0), (B - 1, H - 1)):
+        ref = isa_oracle.dense_attention(inp["Q"][1][bi, h], inp["K"][1][bi, h], inp["V"][1][bi, h])
+        e = np.abs(Od[bi, h] - ref)
+        assert e.max() <= 2e-2 and e.mean() <= 2e-3
+
+
 def test_dense_equality_and_dense_kernel(dev):
     for D in (64, 128):
         p, inp, res = _small(dev, 333, 410, D, 64, 1.0, 0.0, 0.0625)
