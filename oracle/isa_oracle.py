@@ -39,8 +39,11 @@ R7  the sharp and the flat path both see only the kept KV blocks J (all
 R8  the exact set E_i of a flat block is the top k_ns of its coarse row over
     J; the Taylor weight of block j is n_j (the step (5) factor L_K), applied
     to numerator and denominator.
-R9  the low-frequency residual gamma*O_coarse of step (6) is omitted
-    (gamma = 0; the pages never give gamma).
+R9  the low-frequency residual of step (6) is gamma * O_coarse, with
+    O_coarse_i = softmax over the kept blocks J of the coarse row S[i, J]
+    applied to Vc[J] (the pooled attention of step (1) at block resolution,
+    unweighted), broadcast to every token of block i. The pages never give
+    gamma; the default is 0 (residual off).
 R10 ties: the lower index wins in every top-k; in the split a lower index
     counts as sharper.
 """
@@ -241,8 +244,17 @@ class HeadResult:
     exact_gaps: np.ndarray      # [n_flat]
 
 
+def coarse_output(S: np.ndarray, Vc: np.ndarray, J: np.ndarray) -> np.ndarray:
+    """O_coarse [N, D]: for query block i, softmax(S[i, J]) applied to Vc[J]
+    ([RB] "Method steps" step (6), reading R9)."""
+    x = S[:, J]
+    x = x - x.max(axis=1, keepdims=True)
+    w = np.exp(x)
+    return (w @ Vc[J]) / w.sum(axis=1, keepdims=True)
+
+
 def isa_head(Q, K, V, plan: Plan, selections: dict | None = None, rows=None,
-             compute_output: bool = True) -> HeadResult:
+             compute_output: bool = True, gamma: float = 0.0) -> HeadResult:
     """ISA forward for one (batch, head). Q, K, V: [L, D] arrays.
 
     `selections` may inject ctx_idx / sharp_idx / flat_idx / flat_exact_idx
@@ -301,12 +313,17 @@ def isa_head(Q, K, V, plan: Plan, selections: dict | None = None, rows=None,
             exact_tok = (np.concatenate([_token_range(plan, j) for j in Ei])
                          if Ei.size else np.zeros(0, dtype=np.int64))
             O[tok] = _flat_block_out(Q[tok], K, V, Kc, Vc, exact_tok, Ti, counts[Ti], D)
+        if gamma != 0.0:
+            Oc = coarse_output(S, Vc, J)
+            for i in range(plan.N):
+                tok = _token_range(plan, i)
+                O[tok] += gamma * Oc[i][None, :]
 
     return HeadResult(O, ctx_idx, sharp_idx, flat_idx, E, r, M, S, Qc, Kc, Vc,
                       _topk_gap(r, plan.k_ctx), split_gap, exact_gaps)
 
 
-def isa_forward(Q, K, V, L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns, heads=None):
+def isa_forward(Q, K, V, L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns, heads=None, gamma=0.0):
     """ISA over [B, H, L, D] inputs; returns (O [B,H,L,D] float64, results
     dict keyed by (b_idx, h)). `heads` restricts the work to listed heads."""
     plan = make_plan(L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns)
@@ -314,7 +331,7 @@ def isa_forward(Q, K, V, L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns, heads=None
     O = np.full((Bn, Hn, L, D), np.nan)
     res = {}
     for (bi, h) in (heads if heads is not None else [(x, y) for x in range(Bn) for y in range(Hn)]):
-        hr = isa_head(Q[bi, h], K[bi, h], V[bi, h], plan)
+        hr = isa_head(Q[bi, h], K[bi, h], V[bi, h], plan, gamma=gamma)
         O[bi, h] = hr.O
         res[(bi, h)] = hr
     return O, res

@@ -346,3 +346,36 @@ def test_generator_is_seeded_and_structured():
     Q, K, V = a
     # context keys are scaled down
     assert np.abs(K[256:]).mean() < 0.7 * np.abs(K[:256]).mean()
+
+
+# ------------------------------------------------- step (6) residual
+def test_residual_off_by_default_and_linear_in_gamma():
+    Q, K, V = _rand_head(40, 230, 170, 8)
+    p = O.make_plan(230, 170, 32, 0.5, 0.5, 0.25)
+    o0 = O.isa_head(Q, K, V, p).O
+    assert np.array_equal(O.isa_head(Q, K, V, p, gamma=0.0).O, o0)
+    o1 = O.isa_head(Q, K, V, p, gamma=0.3).O
+    o2 = O.isa_head(Q, K, V, p, gamma=-0.6).O
+    assert np.abs((o2 - o0) + 2.0 * (o1 - o0)).max() < 1e-12
+    # the residual is constant over the tokens of a block
+    d = o1 - o0
+    for s_, n in zip(p.starts, p.counts):
+        assert np.abs(d[s_:s_ + n] - d[s_]).max() < 1e-12
+
+
+def test_coarse_output_is_pooled_sdpa_over_kept_blocks():
+    Q, K, V = _rand_head(41, 256, 224, 8)
+    p = O.make_plan(256, 224, 32, 0.5, 0.5, 0.25)
+    r = O.isa_head(Q, K, V, p)
+    J = O.kept_blocks(r.ctx_idx, p)
+    ref = _sdpa(r.Qc, r.Kc[J], r.Vc[J])
+    assert np.abs(O.coarse_output(r.S, r.Vc, J) - ref).max() < 1e-12
+
+
+def test_residual_with_unit_blocks_scales_dense_attention():
+    # b = 1, all context kept, all sharp: pooling is the identity, so the
+    # coarse output is dense attention and O = (1 + gamma) * dense.
+    Q, K, V = _rand_head(42, 48, 40, 8)
+    p = O.make_plan(48, 40, 1, 1.0, 0.0, 0.5)
+    o = O.isa_head(Q, K, V, p, gamma=0.25).O
+    assert np.abs(o - 1.25 * _sdpa(Q, K, V)).max() < 1e-12
