@@ -23,15 +23,15 @@ ISA_ERR_WORKSPACE = -3
 ISA_ERR_HIP = -4
 
 EXPORTED = ("isa_plan", "isa_pool_coarse", "isa_ctx_topk", "isa_sharpness_split",
-            "isa_sharp_attn", "isa_flat_taylor_attn", "isa_forward", "isa_dense_attn",
-            "isa_strerror")
+            "isa_sharp_attn", "isa_flat_taylor_attn", "isa_coarse_residual", "isa_forward",
+            "isa_dense_attn", "isa_strerror")
 
 
 class IsaParams(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L_src", ctypes.c_int32),
                 ("L_ctx", ctypes.c_int32), ("D", ctypes.c_int32), ("b", ctypes.c_int32),
                 ("alpha_s", ctypes.c_double), ("alpha_f", ctypes.c_double),
-                ("alpha_ns", ctypes.c_double)]
+                ("alpha_ns", ctypes.c_double), ("gamma", ctypes.c_double)]
 
 
 class IsaPlan(ctypes.Structure):
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.isa_sharpness_split.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.isa_sharp_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.isa_flat_taylor_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.isa_coarse_residual.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
         L.isa_forward.argtypes = [P, vp, vp, vp, vp, vp, sz, ctypes.POINTER(IsaDebug), vp]
         L.isa_dense_attn.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.isa_strerror.argtypes = [ctypes.c_int]
@@ -102,10 +103,11 @@ class Params:
     alpha_s: float = 0.125
     alpha_f: float = 0.5
     alpha_ns: float = 0.0625
+    gamma: float = 0.0
 
     def c(self) -> IsaParams:
         return IsaParams(self.B, self.H, self.L_src, self.L_ctx, self.D, self.b,
-                         self.alpha_s, self.alpha_f, self.alpha_ns)
+                         self.alpha_s, self.alpha_f, self.alpha_ns, self.gamma)
 
 
 def plan(p: Params) -> dict:
@@ -246,6 +248,18 @@ def flat_taylor_attn(Q, K, V, kc_bf16, vc_bf16, ctx_idx, flat_idx, flat_exact_id
         ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(), V.data_ptr(), kc_bf16.data_ptr(),
         vc_bf16.data_ptr(), nz(ctx_idx), nz(flat_idx), nz(flat_exact_idx), O.data_ptr(),
         _stream(Q.device)))
+    return O
+
+
+def coarse_residual(qc, kc, vc_bf16, ctx_idx, O, p: Params):
+    """Step (6): adds gamma * O_coarse to every token row of O in place."""
+    torch = _torch()
+    pl = plan(p)
+    ws = _empty((pl["scores_bytes"],), torch.uint8, O.device)
+    nz = lambda t: t.data_ptr() if t.numel() else None
+    _check("isa_coarse_residual", lib().isa_coarse_residual(
+        ctypes.byref(p.c()), qc.data_ptr(), kc.data_ptr(), vc_bf16.data_ptr(), nz(ctx_idx),
+        O.data_ptr(), ws.data_ptr(), ws.numel(), _stream(O.device)))
     return O
 
 

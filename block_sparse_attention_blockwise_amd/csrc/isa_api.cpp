@@ -65,6 +65,7 @@ int make_shape(const isa_params_t* p, IsaShape* s) {
   if (p->B < 1 || p->H < 1 || p->L_src < 1 || p->L_ctx < 0 || p->D < 1 || p->b < 1)
     return ISA_ERR_ARG;
   if (!ratio_ok(p->alpha_s) || !ratio_ok(p->alpha_f) || !ratio_ok(p->alpha_ns)) return ISA_ERR_ARG;
+  if (!std::isfinite(p->gamma)) return ISA_ERR_ARG;
   if (p->D != 64 && p->D != 128) return ISA_ERR_UNSUPPORTED;
   if (p->b != 32 && p->b != 64) return ISA_ERR_UNSUPPORTED;
   const int64_t N_src = ((int64_t)p->L_src + p->b - 1) / p->b;
@@ -83,6 +84,7 @@ int make_shape(const isa_params_t* p, IsaShape* s) {
   r.n_sharp = r.N - r.n_flat;
   r.k_ns = ceil_count(p->alpha_ns * r.N_kv);
   if (r.k_ns > r.N_kv) r.k_ns = r.N_kv;
+  r.gamma = (float)p->gamma;
   *s = r;
   return ISA_OK;
 }
@@ -176,6 +178,23 @@ int isa_flat_taylor_attn(const isa_params_t* p, const void* Q, const void* K, co
                                          flat_exact_idx, (uint16_t*)O, as_stream(stream)));
 }
 
+int isa_coarse_residual(const isa_params_t* p, const double* qc, const double* kc,
+                        const void* vc_bf16, const int32_t* ctx_idx, void* O, void* ws,
+                        size_t ws_bytes, void* stream) {
+  IsaShape s;
+  int rc = make_shape(p, &s);
+  if (rc != ISA_OK) return rc;
+  if (!qc || !kc || !vc_bf16 || (!ctx_idx && s.k_ctx > 0) || !O || !ws) return ISA_ERR_ARG;
+  if (ws_bytes < scores_rows_bytes(s)) return ISA_ERR_WORKSPACE;
+  if (s.gamma == 0.0f) return ISA_OK;
+  hipStream_t st = as_stream(stream);
+  double* srows = (double*)ws;
+  hipError_t e = isa_launch_coarse_rows(s, qc, kc, ctx_idx, srows, st);
+  if (e == hipSuccess)
+    e = isa_launch_coarse_residual(s, srows, (const uint16_t*)vc_bf16, ctx_idx, (uint16_t*)O, st);
+  return hip_status(e);
+}
+
 int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void* V, void* O,
                 void* ws, size_t ws_bytes, const isa_debug_t* dbg, void* stream) {
   IsaShape s;
@@ -210,6 +229,8 @@ int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void*
   if (e == hipSuccess) e = isa_launch_sharp_attn(s, q, k, v, ctx_idx, sharp_idx, (uint16_t*)O, st);
   if (e == hipSuccess)
     e = isa_launch_flat_attn(s, q, k, v, kcb, vcb, ctx_idx, flat_idx, exact, (uint16_t*)O, st);
+  if (e == hipSuccess && s.gamma != 0.0f)
+    e = isa_launch_coarse_residual(s, srows, vcb, ctx_idx, (uint16_t*)O, st);
   if (e == hipSuccess && dbg) {
     const size_t bh = (size_t)s.B * s.H;
     struct { void* dst; const void* src; size_t n; } cp[] = {

@@ -11,6 +11,7 @@
 struct IsaShape {
   int B, H, L_src, L_ctx, L, D, b;
   int N_src, N_ctx, N, k_ctx, N_kv, n_flat, n_sharp, k_ns;
+  float gamma;
 };
 
 // Token range [start, start + n) of global block j (source blocks first,
@@ -47,6 +48,9 @@ hipError_t isa_launch_split(const IsaShape& s, const double* sharp, int32_t* sha
 hipError_t isa_launch_flat_topk(const IsaShape& s, const double* srows, const int32_t* ctx_idx,
                                 const int32_t* flat_idx, int32_t* flat_exact_idx,
                                 hipStream_t st);
+hipError_t isa_launch_coarse_residual(const IsaShape& s, const double* srows,
+                                      const uint16_t* vc_bf16, const int32_t* ctx_idx,
+                                      uint16_t* O, hipStream_t st);
 hipError_t isa_launch_sharp_attn(const IsaShape& s, const uint16_t* Q, const uint16_t* K,
                                  const uint16_t* V, const int32_t* ctx_idx,
                                  const int32_t* sharp_idx, uint16_t* O, hipStream_t st);

@@ -361,7 +361,89 @@ __global__ __launch_bounds__(64 * kFlatTopkWaves) void flat_topk_kernel(IsaShape
   }
 }
 
+// ------------------------------------------------ step (6) coarse residual
+// One workgroup per query block i: softmax of the coarse row S[i, J] (fp64),
+// O_coarse_i = sum_p w_p Vc[J[p]] / sum_p w_p, then gamma * O_coarse_i is
+// added to every token row of block i (bf16 read-modify-write).
+constexpr int kResThreads = 256;
+
+__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ inline uint16_t f32_to_bf16_rne_sel(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__global__ __launch_bounds__(kResThreads) void coarse_residual_kernel(IsaShape s, const double* __restrict__ srows,
+                                                                      const uint16_t* __restrict__ vcb,
+                                                                      const int32_t* __restrict__ ctx_idx,
+                                                                      uint16_t* __restrict__ O) {
+  const int i = blockIdx.x, bh = blockIdx.y;
+  __shared__ double w[ISA_MAX_NKV];
+  __shared__ double red[kResThreads / 64];
+  __shared__ float part[kResThreads / 128][128];
+  __shared__ float oc[128];
+  const double* row = srows + ((size_t)bh * s.N + i) * s.N_kv;
+  const int32_t* ctx_row = ctx_idx + (size_t)bh * s.k_ctx;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double mx = -INFINITY;
+  for (int p = threadIdx.x; p < s.N_kv; p += kResThreads) mx = fmax(mx, row[p]);
+  mx = wave_max_f64(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = red[0];
+  for (int x = 1; x < kResThreads / 64; ++x) mx = fmax(mx, red[x]);
+  __syncthreads();
+  double z = 0.0;
+  for (int p = threadIdx.x; p < s.N_kv; p += kResThreads) {
+    const double e = exp(row[p] - mx);
+    w[p] = e;
+    z += e;
+  }
+  z = wave_sum_f64(z);
+  if (lane == 0) red[wave] = z;
+  __syncthreads();
+  z = 0.0;
+  for (int x = 0; x < kResThreads / 64; ++x) z += red[x];
+  // weighted sum of the bf16 block means of V: thread (half, d)
+  const int D = s.D;
+  const int d = threadIdx.x % 128, half = threadIdx.x / 128;
+  float acc = 0.0f;
+  if (d < D) {
+    for (int p = half; p < s.N_kv; p += kResThreads / 128) {
+      const int j = kept_block_id(s, ctx_row, p);
+      if (j >= 0 && j < s.N)
+        acc += (float)w[p] * bf16_to_f32(vcb[((size_t)bh * s.N + j) * D + d]);
+    }
+  }
+  part[half][d] = acc;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float t = 0.0f;
+    for (int x = 0; x < kResThreads / 128; ++x) t += part[x][threadIdx.x];
+    oc[threadIdx.x] = s.gamma * (float)((double)t / z);
+  }
+  __syncthreads();
+  int start, n;
+  isa_block_range(s, i, start, n);
+  uint16_t* base = O + ((size_t)bh * s.L + start) * D;
+  for (int x = threadIdx.x; x < n * D; x += kResThreads) {
+    const float v = bf16_to_f32(base[x]) + oc[x % D];
+    base[x] = f32_to_bf16_rne_sel(v);
+  }
+}
+
 }  // namespace
+
+hipError_t isa_launch_coarse_residual(const IsaShape& s, const double* srows,
+                                      const uint16_t* vc_bf16, const int32_t* ctx_idx,
+                                      uint16_t* O, hipStream_t st) {
+  if (s.gamma == 0.0f) return hipSuccess;
+  dim3 grid(s.N, s.B * s.H);
+  coarse_residual_kernel<<<grid, kResThreads, 0, st>>>(s, srows, vc_bf16, ctx_idx, O);
+  return hipGetLastError();
+}
 
 hipError_t isa_launch_ctx_topk(const IsaShape& s, const double* qc, const double* kc,
                                int32_t* ctx_idx, double* ctx_score, hipStream_t st) {

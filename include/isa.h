@@ -20,8 +20,11 @@
  *       n_j * exp(q.Kc_j / sqrt(D)) in the denominator and that weight times
  *       Vc_j in the numerator (n_j = valid tokens of block j); one softmax
  *       accumulator merges both;
- *   (6) outputs land at their token positions (the gamma * O_coarse residual
- *       is not applied: gamma = 0).
+ *   (6) outputs land at their token positions, plus gamma * O_coarse_i on
+ *       every token of block i, where O_coarse_i is the pooled attention at
+ *       block resolution over the kept blocks: softmax_j(S[i, j], j in J)
+ *       applied to Vc_j. The pages leave gamma open; gamma = 0 (the default)
+ *       skips the residual.
  *
  * Conventions shared by every entry point
  *   Layout:    Q, K, V, O are dense row-major [B, H, L, D] bf16 (raw 16-bit
@@ -56,7 +59,7 @@
  *              identical outputs and selections.
  *   Limits:    D in {64, 128}; b in {32, 64}; L_src >= 1; L_ctx >= 0;
  *              B, H >= 1; N_src <= 4096; N_ctx <= 4096; N_kv <= 4096;
- *              ratios in [0, 1] (NaN rejected).
+ *              ratios in [0, 1] (NaN rejected); gamma finite.
  */
 #ifndef ISA_H
 #define ISA_H
@@ -89,6 +92,7 @@ typedef struct {
   double alpha_s;      /* fraction of context blocks kept (step 2) */
   double alpha_f;      /* fraction of query blocks on the flat path (step 3) */
   double alpha_ns;     /* fraction of J computed exactly per flat block (step 5) */
+  double gamma;        /* weight of the low-frequency residual (step 6); 0 = off */
 } isa_params_t;
 
 typedef struct {
@@ -148,6 +152,15 @@ ISA_API int isa_flat_taylor_attn(const isa_params_t* p, const void* Q, const voi
                          const void* kc_bf16, const void* vc_bf16, const int32_t* ctx_idx,
                          const int32_t* flat_idx, const int32_t* flat_exact_idx, void* O,
                          void* stream);
+
+/* Step (6) residual: adds gamma * O_coarse_i (see above) to every token row
+ * of block i of O, in place (bf16, rounded to nearest even). Needs qc, kc
+ * from isa_pool_coarse, vc_bf16 (the bf16 V means) and ctx_idx. `ws` must
+ * hold plan.scores_bytes bytes of device memory (the coarse rows are
+ * recomputed there). Does nothing when gamma == 0. */
+ISA_API int isa_coarse_residual(const isa_params_t* p, const double* qc, const double* kc,
+                                const void* vc_bf16, const int32_t* ctx_idx, void* O, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /* Steps (1)-(6) enqueued back to back with no host synchronisation. `ws`
  * must hold plan.workspace_bytes of device memory; `dbg` may be NULL. */

@@ -272,3 +272,28 @@ def test_step_entry_points_compose_to_forward(dev):
         np.testing.assert_allclose(sharp[0, h].cpu().numpy(), M, rtol=1e-10, atol=0)
         r = isa_oracle.context_scores(S, plan)
         np.testing.assert_allclose(score[0, h].cpu().numpy(), r, rtol=1e-10, atol=1e-10)
+
+
+@pytest.mark.parametrize("gamma", [0.5, -0.25])
+def test_coarse_residual_gamma(dev, gamma):
+    """Step (6) residual: forward with gamma matches the oracle, and the
+    residual entry point composes with the other steps."""
+    p = isa.Params(1, 2, 700, 451, 128, 64, 0.25, 0.5, 0.125, gamma)
+    inp = _inputs(1, p)
+    res = _run(p, inp, dev)
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    for h in range(p.H):
+        r = isa_oracle.isa_head(inp["Q"][1][0, h], inp["K"][1][0, h], inp["V"][1][0, h], plan, gamma=gamma)
+        assert np.array_equal(res["sharp_idx"][0, h], r.sharp_idx)
+        e = np.abs(res["O"][0, h] - r.O)
+        log(f"residual gamma={gamma} h={h}: max-abs {e.max():.2e} mean-abs {e.mean():.2e}")
+        assert e.max() <= 2e-2 and e.mean() <= 2e-3
+    Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
+    p0 = isa.Params(1, 2, 700, 451, 128, 64, 0.25, 0.5, 0.125, 0.0)
+    O0 = isa.forward(Q, K, V, p0)
+    qc, kc, kcb, vcb = isa.pool_coarse(Q, K, V, p)
+    ctx, _ = isa.ctx_topk(qc, kc, p)
+    isa.coarse_residual(qc, kc, vcb, ctx, O0, p)
+    Og = isa.forward(Q, K, V, p)
+    torch.cuda.synchronize()
+    assert torch.equal(O0.view(torch.int16), Og.view(torch.int16))

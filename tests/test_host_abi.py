@@ -63,7 +63,7 @@ def test_plan_matches_oracle_counts(isa):
 
 def _params(isa, **kw):
     base = dict(B=1, H=2, L_src=1024, L_ctx=1024, D=128, b=64, alpha_s=0.125, alpha_f=0.5,
-                alpha_ns=0.0625)
+                alpha_ns=0.0625, gamma=0.0)
     base.update(kw)
     return isa.IsaParams(**base)
 
@@ -72,6 +72,7 @@ def _params(isa, **kw):
     (dict(L_src=0), -1), (dict(L_ctx=-1), -1), (dict(B=0), -1), (dict(H=0), -1),
     (dict(D=0), -1), (dict(b=0), -1),
     (dict(alpha_s=float("nan")), -1), (dict(alpha_f=1.5), -1), (dict(alpha_ns=-0.1), -1),
+    (dict(gamma=float("nan")), -1), (dict(gamma=float("inf")), -1),
     (dict(D=96), -2), (dict(D=256), -2), (dict(b=16), -2), (dict(b=128), -2),
     (dict(L_src=64 * 4097), -2), (dict(L_ctx=64 * 4097), -2),
     (dict(L_src=64 * 4000, L_ctx=64 * 4000, alpha_s=0.05), -2),   # N_kv > 4096
@@ -98,6 +99,8 @@ def test_calls_fail_before_launch(isa):
     assert L.isa_sharp_attn(ctypes.byref(p), fake, fake, fake, None, fake, fake, None) == -1
     assert L.isa_flat_taylor_attn(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake,
                                   fake, fake, None) == -1
+    assert L.isa_coarse_residual(ctypes.byref(p), fake, fake, fake, fake, None, fake, 1 << 40, None) == -1
+    assert L.isa_coarse_residual(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 16, None) == -3
     assert L.isa_dense_attn(1, 1, 0, 128, fake, fake, fake, fake, None) == -1
     assert L.isa_dense_attn(1, 1, 16, 96, fake, fake, fake, fake, None) == -2
     assert L.isa_dense_attn(1, 1, 16, 128, None, fake, fake, fake, None) == -1
