@@ -55,6 +55,9 @@ def parse():
                     help="launch only this kernel --steps times (for counter collection)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--fig6", action="store_true",
+                    help="pure 0th-order Taylor variant (alpha_f=1, alpha_ns=0) vs exact "
+                         "attention over J: latencies and the error/sharpness rank correlation")
     return ap.parse_args()
 
 
@@ -167,6 +170,51 @@ def cpu_baseline(host, budget_s):
                        f"blocks and heads, numpy fp64 with {threads} BLAS threads")}
 
 
+def fig6(isa, torch, p, Q, K, V, args):
+    """Sharpness as an error predictor (Fig. 6 of the paper) and the speed of
+    the all-Taylor variant (Fig. 8), on the GPU at the benchmark workload.
+    Exact reference: alpha_f = 0 (every block exact over J). Taylor variant:
+    alpha_f = 1, alpha_ns = 0 (every block on the pooled keys only)."""
+    import dataclasses
+    from scipy.stats import spearmanr
+    from oracle.isa_oracle import make_plan   # block boundaries only
+    pe = dataclasses.replace(p, alpha_f=0.0)
+    pt = dataclasses.replace(p, alpha_f=1.0, alpha_ns=0.0)
+    times = {}
+    outs = {}
+    for name, q in (("default", p), ("exact_over_J", pe), ("all_taylor", pt)):
+        O, dbg = isa.forward(Q, K, V, q, debug=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(max(args.steps // 4, 2)):
+            isa.forward(Q, K, V, q, out=O)
+        e1.record()
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / max(args.steps // 4, 2)
+        outs[name] = (O.float(), dbg["sharpness"])
+    plan = make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    starts = torch.tensor(plan.starts, device=Q.device)
+    counts = torch.tensor(plan.counts, device=Q.device)
+    tok_block = torch.repeat_interleave(torch.arange(plan.N, device=Q.device), counts)
+    diff = (outs["all_taylor"][0] - outs["exact_over_J"][0]).abs().mean(dim=-1)   # [B,H,L]
+    rhos = []
+    for bi in range(p.B):
+        for h in range(p.H):
+            err = torch.zeros(plan.N, device=Q.device, dtype=torch.float32)
+            err.index_add_(0, tok_block, diff[bi, h])
+            err = (err / counts).cpu().numpy()
+            rhos.append(spearmanr(outs["all_taylor"][1][bi, h].cpu().numpy(), err).correlation)
+    rhos = np.asarray(rhos)
+    print(json.dumps({"fig6": {"spearman_sharpness_vs_taylor_error": {
+        "mean": float(rhos.mean()), "min": float(rhos.min()), "max": float(rhos.max()),
+        "heads": int(rhos.size)},
+        "latency_ms": times,
+        "speedup_vs_exact_over_J": {"default": times["exact_over_J"] / times["default"],
+                                    "all_taylor": times["exact_over_J"] / times["all_taylor"]},
+        "config": {"workload": "isa_fwd_64k_tokens_h40_d128", "alpha_s": p.alpha_s}}}), flush=True)
+    del starts
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -196,6 +244,9 @@ def main():
     log("generating inputs")
     T, host = make_inputs(dev)
     Q, K, V = T["Q"], T["K"], T["V"]
+    if args.fig6:
+        fig6(isa, torch, p, Q, K, V, args)
+        return
     O = torch.empty_like(Q)
     BH = p.B * p.H
     e = lambda *s, dt: torch.empty(s, dtype=dt, device=dev)

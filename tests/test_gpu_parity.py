@@ -297,3 +297,28 @@ def test_coarse_residual_gamma(dev, gamma):
     Og = isa.forward(Q, K, V, p)
     torch.cuda.synchronize()
     assert torch.equal(O0.view(torch.int16), Og.view(torch.int16))
+
+
+def test_pure_taylor_flat_path_at_16k(dev):
+    """alpha_ns = 0: every flat block uses only the 0th-order Taylor terms
+    (the variant the pages report as fastest). Full-size launch, selections of
+    every head, sampled rows of three heads; then the Fig. 6 property on the
+    GPU outputs: per-block Taylor error rises with sharpness."""
+    from scipy.stats import spearmanr
+    c = isa_inputs.CONFIGS[2]
+    p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"], 0.125, 1.0, 0.0)
+    inp = _inputs(2, p)
+    log("pure Taylor 16k: forward")
+    res = _run(p, inp, dev)
+    assert res["sharp_idx"].size == 0
+    _check(p, inp, res, {(0, 0), (0, 21), (0, p.H - 1)}, 256, seed=7)
+    pe = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"], 0.125, 0.0, 0.0)
+    exact = _run(pe, inp, dev)
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, 0.125, 1.0, 0.0)
+    rhos = []
+    for h in (0, 13, 39):
+        err = [np.abs(res["O"][0, h, s_:s_ + n] - exact["O"][0, h, s_:s_ + n]).mean()
+               for s_, n in zip(plan.starts, plan.counts)]
+        rhos.append(spearmanr(res["sharpness"][0, h], err).correlation)
+    log(f"Fig. 6 on GPU outputs: Spearman(sharpness, Taylor error) = {rhos}")
+    assert min(rhos) > 0.5
