@@ -46,6 +46,15 @@ R9  the low-frequency residual of step (6) is gamma * O_coarse, with
     gamma; the default is 0 (residual off).
 R10 ties: the lower index wins in every top-k; in the split a lower index
     counts as sharper.
+R11 decoupled RoPE (the step before (1), [RB] "Novelty"; [TW] section 6):
+    standard rotary embedding of Q and K on interleaved pairs (2i, 2i+1)
+    with angle pos * base^(-2i/D), where source tokens take positions
+    0..L_src-1 and context tokens restart at 0. The pages give no base and
+    no precision; the rotated tensors are the attention inputs, so they are
+    stored as bf16: cos/sin are computed in fp64 and rounded to fp32, the
+    rotation is done in fp32 with each product and sum rounded, and the
+    result is rounded to bf16 (the arithmetic of the kernel, so both sides
+    produce the same bf16 values).
 """
 from __future__ import annotations
 
@@ -115,6 +124,38 @@ def make_plan(L_src: int, L_ctx: int, b: int, alpha_s: float, alpha_f: float,
         counts.append(min(b, L_ctx - j * b))
     return Plan(L_src, L_ctx, b, N_src, N_ctx, N, k_ctx, N_kv, n_flat, N - n_flat,
                 k_ns, tuple(starts), tuple(counts))
+
+
+# ------------------------------------------------------ decoupled RoPE (R11)
+def rope_positions(L_src: int, L_ctx: int) -> np.ndarray:
+    """Source tokens 0..L_src-1, context tokens restarting at 0."""
+    return np.concatenate([np.arange(L_src), np.arange(L_ctx)]).astype(np.float64)
+
+
+def rope_tables(pos: np.ndarray, D: int, base: float):
+    """cos/sin of pos * base^(-2i/D) for i < D/2: fp64, then rounded to fp32."""
+    inv = base ** (-(2.0 * np.arange(D // 2)) / D)
+    ang = pos[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def _bf16_rne(x: np.ndarray) -> np.ndarray:
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def rope(X: np.ndarray, L_src: int, L_ctx: int, base: float) -> np.ndarray:
+    """Rotates X [L, D] pairwise (R11); returns the bf16 result as float64."""
+    X = np.asarray(X, dtype=np.float32)
+    c, s = rope_tables(rope_positions(L_src, L_ctx), X.shape[1], base)
+    x, y = X[:, 0::2], X[:, 1::2]
+    xr = (x * c).astype(np.float32) - (y * s).astype(np.float32)
+    yr = (x * s).astype(np.float32) + (y * c).astype(np.float32)
+    out = np.empty_like(X)
+    out[:, 0::2] = xr
+    out[:, 1::2] = yr
+    return _bf16_rne(out).astype(np.float64)
 
 
 # ------------------------------------------------------------ selection steps

@@ -379,3 +379,47 @@ def test_residual_with_unit_blocks_scales_dense_attention():
     p = O.make_plan(48, 40, 1, 1.0, 0.0, 0.5)
     o = O.isa_head(Q, K, V, p, gamma=0.25).O
     assert np.abs(o - 1.25 * _sdpa(Q, K, V)).max() < 1e-12
+
+
+# --------------------------------------------------------- decoupled RoPE
+def _rope64(X, pos, base):
+    """Plain fp64 rotary embedding as complex multiplication (no rounding)."""
+    D = X.shape[1]
+    z = X[:, 0::2] + 1j * X[:, 1::2]
+    ang = pos[:, None] * base ** (-(2.0 * np.arange(D // 2)) / D)[None, :]
+    r = z * np.exp(1j * ang)
+    out = np.empty_like(X)
+    out[:, 0::2], out[:, 1::2] = r.real, r.imag
+    return out
+
+
+def test_rope_matches_complex_rotation_and_restarts_per_segment():
+    rng = np.random.default_rng(50)
+    Ls, Lc, D = 40, 30, 16
+    X = isa_inputs.round_to_bf16(rng.standard_normal((Ls + Lc, D)).astype(np.float32))[1]
+    pos = O.rope_positions(Ls, Lc)
+    assert pos[0] == 0 and pos[Ls] == 0 and pos[-1] == Lc - 1
+    R = O.rope(X, Ls, Lc, 10000.0)
+    ref = _rope64(X.astype(np.float64), pos, 10000.0)
+    assert np.abs(R - ref).max() <= 2 ** -7 * np.abs(ref).max()   # bf16 rounding only
+    # identical tokens at equal source/context positions rotate identically
+    X2 = X.copy()
+    X2[Ls:Ls + 10] = X2[:10]
+    R2 = O.rope(X2, Ls, Lc, 10000.0)
+    assert np.array_equal(R2[Ls:Ls + 10], R2[:10])
+    # position 0 is the identity (bf16 inputs are already representable)
+    assert np.array_equal(R[0], X[0].astype(np.float64))
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    rng = np.random.default_rng(51)
+    D = 32
+    q = rng.standard_normal((1, D))
+    k = rng.standard_normal((1, D))
+    base = 500.0
+    dots = []
+    for m, n in ((3, 1), (10, 8), (107, 105)):
+        qm = _rope64(q, np.array([m], dtype=np.float64), base)
+        kn = _rope64(k, np.array([n], dtype=np.float64), base)
+        dots.append(float((qm @ kn.T)[0, 0]))
+    assert np.allclose(dots, dots[0], rtol=0, atol=1e-12)
