@@ -22,7 +22,7 @@ ISA_ERR_UNSUPPORTED = -2
 ISA_ERR_WORKSPACE = -3
 ISA_ERR_HIP = -4
 
-EXPORTED = ("isa_plan", "isa_pool_coarse", "isa_ctx_topk", "isa_sharpness_split",
+EXPORTED = ("isa_plan", "isa_pool_coarse", "isa_rope_pool_coarse", "isa_ctx_topk", "isa_sharpness_split",
             "isa_sharp_attn", "isa_flat_taylor_attn", "isa_coarse_residual", "isa_forward",
             "isa_dense_attn", "isa_strerror")
 
@@ -31,14 +31,16 @@ class IsaParams(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L_src", ctypes.c_int32),
                 ("L_ctx", ctypes.c_int32), ("D", ctypes.c_int32), ("b", ctypes.c_int32),
                 ("alpha_s", ctypes.c_double), ("alpha_f", ctypes.c_double),
-                ("alpha_ns", ctypes.c_double), ("gamma", ctypes.c_double)]
+                ("alpha_ns", ctypes.c_double), ("gamma", ctypes.c_double),
+                ("rope_base", ctypes.c_double)]
 
 
 class IsaPlan(ctypes.Structure):
     _fields_ = [("N_src", ctypes.c_int32), ("N_ctx", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("k_ctx", ctypes.c_int32), ("N_kv", ctypes.c_int32), ("n_flat", ctypes.c_int32),
                 ("n_sharp", ctypes.c_int32), ("k_ns", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t), ("scores_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("scores_bytes", ctypes.c_size_t),
+                ("rope_bytes", ctypes.c_size_t)]
 
 
 class IsaDebug(ctypes.Structure):
@@ -68,6 +70,7 @@ def lib() -> ctypes.CDLL:
         P = ctypes.POINTER(IsaParams)
         L.isa_plan.argtypes = [P, ctypes.POINTER(IsaPlan)]
         L.isa_pool_coarse.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.isa_rope_pool_coarse.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.isa_ctx_topk.argtypes = [P, vp, vp, vp, vp, vp]
         L.isa_sharpness_split.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.isa_sharp_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
@@ -104,10 +107,11 @@ class Params:
     alpha_f: float = 0.5
     alpha_ns: float = 0.0625
     gamma: float = 0.0
+    rope_base: float = 0.0
 
     def c(self) -> IsaParams:
         return IsaParams(self.B, self.H, self.L_src, self.L_ctx, self.D, self.b,
-                         self.alpha_s, self.alpha_f, self.alpha_ns, self.gamma)
+                         self.alpha_s, self.alpha_f, self.alpha_ns, self.gamma, self.rope_base)
 
 
 def plan(p: Params) -> dict:
@@ -192,6 +196,26 @@ def pool_coarse(Q, K, V, p: Params):
                                                     V.data_ptr(), qc.data_ptr(), kc.data_ptr(),
                                                     kcb.data_ptr(), vcb.data_ptr(), _stream(dev)))
     return qc, kc, kcb, vcb
+
+
+def rope_pool_coarse(Q, K, V, p: Params):
+    """Decoupled RoPE fused with step (1): returns (Qr, Kr, qc, kc, kc_bf16, vc_bf16)."""
+    torch = _torch()
+    _check_qkv(p, Q, K, V)
+    pl = plan(p)
+    dev = Q.device
+    Qr = _empty(tuple(Q.shape), torch.bfloat16, dev)
+    Kr = _empty(tuple(K.shape), torch.bfloat16, dev)
+    qc = _empty((p.B, p.H, pl["N"], p.D), torch.float64, dev)
+    kc = _empty((p.B, p.H, pl["N"], p.D), torch.float64, dev)
+    kcb = _empty((p.B, p.H, pl["N"], p.D), torch.bfloat16, dev)
+    vcb = _empty((p.B, p.H, pl["N"], p.D), torch.bfloat16, dev)
+    ws = _empty((max(pl["rope_bytes"], 1),), torch.uint8, dev)
+    _check("isa_rope_pool_coarse", lib().isa_rope_pool_coarse(
+        ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(), V.data_ptr(), Qr.data_ptr(),
+        Kr.data_ptr(), qc.data_ptr(), kc.data_ptr(), kcb.data_ptr(), vcb.data_ptr(),
+        ws.data_ptr(), ws.numel(), _stream(dev)))
+    return Qr, Kr, qc, kc, kcb, vcb
 
 
 def ctx_topk(qc, kc, p: Params):

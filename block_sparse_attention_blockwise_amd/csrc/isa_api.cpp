@@ -26,8 +26,16 @@ bool ratio_ok(double a) { return !std::isnan(a) && a >= 0.0 && a <= 1.0; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t qc, kc, kcb, vcb, ctx_idx, ctx_score, sharp, sharp_idx, flat_idx, exact, srows, total;
+  size_t qc, kc, kcb, vcb, ctx_idx, ctx_score, sharp, sharp_idx, flat_idx, exact, srows;
+  size_t qr, kr, rope, total;   // RoPE buffers (only when rope_base > 0)
 };
+
+// cos/sin table of the decoupled RoPE: one float2 per (position, pair).
+size_t rope_table_bytes(const IsaShape& s) {
+  if (s.rope_base == 0.0) return 0;
+  const size_t P = s.L_src > s.L_ctx ? s.L_src : s.L_ctx;
+  return align256(P * (size_t)(s.D / 2) * sizeof(float2));
+}
 
 Layout make_layout(const IsaShape& s) {
   const size_t bh = (size_t)s.B * s.H;
@@ -46,6 +54,10 @@ Layout make_layout(const IsaShape& s) {
   l.flat_idx = o;  o = align256(o + at_least1(bh * s.n_flat) * 4);
   l.exact = o;     o = align256(o + at_least1(bh * s.n_flat * (size_t)s.k_ns) * 4);
   l.srows = o;     o = align256(o + bh * s.N * (size_t)s.N_kv * 8);
+  const size_t qkr = s.rope_base != 0.0 ? bh * (size_t)s.L * s.D * 2 : 0;
+  l.qr = o;        o = align256(o + qkr);
+  l.kr = o;        o = align256(o + qkr);
+  l.rope = o;      o = align256(o + rope_table_bytes(s));
   l.total = o;
   return l;
 }
@@ -66,6 +78,7 @@ int make_shape(const isa_params_t* p, IsaShape* s) {
     return ISA_ERR_ARG;
   if (!ratio_ok(p->alpha_s) || !ratio_ok(p->alpha_f) || !ratio_ok(p->alpha_ns)) return ISA_ERR_ARG;
   if (!std::isfinite(p->gamma)) return ISA_ERR_ARG;
+  if (!(p->rope_base == 0.0 || (std::isfinite(p->rope_base) && p->rope_base > 1.0))) return ISA_ERR_ARG;
   if (p->D != 64 && p->D != 128) return ISA_ERR_UNSUPPORTED;
   if (p->b != 32 && p->b != 64) return ISA_ERR_UNSUPPORTED;
   const int64_t N_src = ((int64_t)p->L_src + p->b - 1) / p->b;
@@ -85,6 +98,7 @@ int make_shape(const isa_params_t* p, IsaShape* s) {
   r.k_ns = ceil_count(p->alpha_ns * r.N_kv);
   if (r.k_ns > r.N_kv) r.k_ns = r.N_kv;
   r.gamma = (float)p->gamma;
+  r.rope_base = p->rope_base;
   *s = r;
   return ISA_OK;
 }
@@ -106,6 +120,7 @@ int isa_plan(const isa_params_t* p, isa_plan_t* out) {
   out->N_kv = s.N_kv; out->n_flat = s.n_flat; out->n_sharp = s.n_sharp; out->k_ns = s.k_ns;
   out->workspace_bytes = make_layout(s).total;
   out->scores_bytes = scores_bytes(s);
+  out->rope_bytes = rope_table_bytes(s);
   return ISA_OK;
 }
 
@@ -118,6 +133,24 @@ int isa_pool_coarse(const isa_params_t* p, const void* Q, const void* K, const v
   return hip_status(isa_launch_pool(s, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V,
                                     qc, kc, (uint16_t*)kc_bf16, (uint16_t*)vc_bf16,
                                     as_stream(stream)));
+}
+
+int isa_rope_pool_coarse(const isa_params_t* p, const void* Q, const void* K, const void* V,
+                         void* Qr, void* Kr, double* qc, double* kc, void* kc_bf16, void* vc_bf16,
+                         void* ws, size_t ws_bytes, void* stream) {
+  IsaShape s;
+  int rc = make_shape(p, &s);
+  if (rc != ISA_OK) return rc;
+  if (!Q || !K || !V || !Qr || !Kr || !qc || !kc || !ws || s.rope_base == 0.0) return ISA_ERR_ARG;
+  if (ws_bytes < rope_table_bytes(s)) return ISA_ERR_WORKSPACE;
+  hipStream_t st = as_stream(stream);
+  float2* table = (float2*)ws;
+  hipError_t e = isa_launch_rope_table(s, table, st);
+  if (e == hipSuccess)
+    e = isa_launch_rope_pool(s, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, table,
+                             (uint16_t*)Qr, (uint16_t*)Kr, qc, kc, (uint16_t*)kc_bf16,
+                             (uint16_t*)vc_bf16, st);
+  return hip_status(e);
 }
 
 int isa_ctx_topk(const isa_params_t* p, const double* qc, const double* kc, int32_t* ctx_idx,
@@ -220,7 +253,18 @@ int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void*
   const uint16_t* k = (const uint16_t*)K;
   const uint16_t* v = (const uint16_t*)V;
 
-  hipError_t e = isa_launch_pool(s, q, k, v, qc, kc, kcb, vcb, st);
+  hipError_t e = hipSuccess;
+  if (s.rope_base != 0.0) {
+    uint16_t* qr = (uint16_t*)(w + l.qr);
+    uint16_t* kr = (uint16_t*)(w + l.kr);
+    float2* table = (float2*)(w + l.rope);
+    e = isa_launch_rope_table(s, table, st);
+    if (e == hipSuccess) e = isa_launch_rope_pool(s, q, k, v, table, qr, kr, qc, kc, kcb, vcb, st);
+    q = qr;   // every later step reads the rotated tensors
+    k = kr;
+  } else {
+    e = isa_launch_pool(s, q, k, v, qc, kc, kcb, vcb, st);
+  }
   if (e == hipSuccess) e = isa_launch_ctx_topk(s, qc, kc, ctx_idx, ctx_score, st);
   if (e == hipSuccess) e = isa_launch_coarse_rows(s, qc, kc, ctx_idx, srows, st);
   if (e == hipSuccess) e = isa_launch_sharpness(s, srows, sharp, st);

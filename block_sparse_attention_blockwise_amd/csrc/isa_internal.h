@@ -12,6 +12,7 @@ struct IsaShape {
   int B, H, L_src, L_ctx, L, D, b;
   int N_src, N_ctx, N, k_ctx, N_kv, n_flat, n_sharp, k_ns;
   float gamma;
+  double rope_base;
 };
 
 // Token range [start, start + n) of global block j (source blocks first,
@@ -37,6 +38,11 @@ constexpr int ISA_MAX_NKV = 4096;
 hipError_t isa_launch_pool(const IsaShape& s, const uint16_t* Q, const uint16_t* K,
                            const uint16_t* V, double* qc, double* kc, uint16_t* kc_bf16,
                            uint16_t* vc_bf16, hipStream_t st);
+hipError_t isa_launch_rope_table(const IsaShape& s, float2* table, hipStream_t st);
+hipError_t isa_launch_rope_pool(const IsaShape& s, const uint16_t* Q, const uint16_t* K,
+                                const uint16_t* V, const float2* table, uint16_t* Qr,
+                                uint16_t* Kr, double* qc, double* kc, uint16_t* kc_bf16,
+                                uint16_t* vc_bf16, hipStream_t st);
 hipError_t isa_launch_ctx_topk(const IsaShape& s, const double* qc, const double* kc,
                                int32_t* ctx_idx, double* ctx_score, hipStream_t st);
 hipError_t isa_launch_coarse_rows(const IsaShape& s, const double* qc, const double* kc,

@@ -59,7 +59,8 @@
  *              identical outputs and selections.
  *   Limits:    D in {64, 128}; b in {32, 64}; L_src >= 1; L_ctx >= 0;
  *              B, H >= 1; N_src <= 4096; N_ctx <= 4096; N_kv <= 4096;
- *              ratios in [0, 1] (NaN rejected); gamma finite.
+ *              ratios in [0, 1] (NaN rejected); gamma finite; rope_base 0 or
+ *              finite and > 1.
  */
 #ifndef ISA_H
 #define ISA_H
@@ -93,12 +94,17 @@ typedef struct {
   double alpha_f;      /* fraction of query blocks on the flat path (step 3) */
   double alpha_ns;     /* fraction of J computed exactly per flat block (step 5) */
   double gamma;        /* weight of the low-frequency residual (step 6); 0 = off */
+  double rope_base;    /* > 1: decoupled RoPE on Q and K before step 1 (read by
+                          isa_forward and isa_rope_pool_coarse; the other step
+                          entry points take Q and K as given, so pass them the
+                          rotated tensors); 0 = off */
 } isa_params_t;
 
 typedef struct {
   int32_t N_src, N_ctx, N, k_ctx, N_kv, n_flat, n_sharp, k_ns;
   size_t workspace_bytes; /* device workspace isa_forward needs */
   size_t scores_bytes;    /* workspace isa_sharpness_split needs */
+  size_t rope_bytes;      /* workspace isa_rope_pool_coarse needs (0 if RoPE off) */
 } isa_plan_t;
 
 /* Optional device buffers isa_forward fills when non-NULL (debug and tests). */
@@ -122,6 +128,21 @@ ISA_API int isa_plan(const isa_params_t* p, isa_plan_t* out);
  * kc may be NULL. */
 ISA_API int isa_pool_coarse(const isa_params_t* p, const void* Q, const void* K, const void* V,
                     double* qc, double* kc, void* kc_bf16, void* vc_bf16, void* stream);
+
+/* Decoupled RoPE fused with step (1). Rotary embedding of Q and K on
+ * interleaved pairs (2i, 2i+1) with angle pos * rope_base^(-2i/D), where
+ * source tokens take positions 0..L_src-1 and context tokens restart at 0
+ * (source and context positions are encoded independently: rainbus.top
+ * summary, Novelty; techwalker article, section 6). cos/sin are computed in
+ * fp64 and rounded to fp32; the rotation is fp32 (each product and sum
+ * rounded); the rotated values are rounded to bf16 and written to Qr, Kr
+ * ([B,H,L,D] bf16, caller-owned). The block means of Qr, Kr and V are written
+ * as in isa_pool_coarse. `ws` must hold plan.rope_bytes bytes of device
+ * memory. Requires rope_base != 0 (ISA_ERR_ARG otherwise). */
+ISA_API int isa_rope_pool_coarse(const isa_params_t* p, const void* Q, const void* K,
+                                 const void* V, void* Qr, void* Kr, double* qc, double* kc,
+                                 void* kc_bf16, void* vc_bf16, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* Step (2): context importance r_j = sum over source query blocks i of
  * S[i, N_src + j] (computed as s * (sum_i Qc_i) . Kc_{N_src+j}) and the
@@ -162,8 +183,9 @@ ISA_API int isa_coarse_residual(const isa_params_t* p, const double* qc, const d
                                 const void* vc_bf16, const int32_t* ctx_idx, void* O, void* ws,
                                 size_t ws_bytes, void* stream);
 
-/* Steps (1)-(6) enqueued back to back with no host synchronisation. `ws`
- * must hold plan.workspace_bytes of device memory; `dbg` may be NULL. */
+/* Steps (1)-(6) enqueued back to back with no host synchronisation (with
+ * the decoupled RoPE first when rope_base > 0). `ws` must hold
+ * plan.workspace_bytes of device memory; `dbg` may be NULL. */
 ISA_API int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void* V, void* O,
                 void* ws, size_t ws_bytes, const isa_debug_t* dbg, void* stream);
 

@@ -322,3 +322,98 @@ def test_pure_taylor_flat_path_at_16k(dev):
         rhos.append(spearmanr(res["sharpness"][0, h], err).correlation)
     log(f"Fig. 6 on GPU outputs: Spearman(sharpness, Taylor error) = {rhos}")
     assert min(rhos) > 0.5
+
+
+# ------------------------------------------------------------ decoupled RoPE
+def _bf16_bits_of(x):
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _rope_mismatch(got_bits, want, X):
+    """Counts rotated bf16 elements that differ from the oracle's. cos/sin
+    come from different fp64 libms on the two sides (each within about an
+    ulp), which can very rarely move an fp32 rounding of a table entry; such
+    a difference stays within one bf16 ulp of the result plus one fp32 ulp of
+    the pair's magnitude (the products can nearly cancel)."""
+    w = _bf16_bits_of(want)
+    bad = got_bits.astype(np.uint16) != w
+    if bad.any():
+        got = (got_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        X = np.asarray(X, dtype=np.float64)
+        mag = np.repeat(np.abs(X[:, 0::2]) + np.abs(X[:, 1::2]), 2, axis=1)
+        bound = 2.0 ** -7 * np.abs(want) + 2.0 ** -22 * mag
+        assert (np.abs(got - want)[bad] <= bound[bad]).all()
+    return int(bad.sum())
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_rope_pool_matches_oracle(dev, D):
+    """Rotated Q, K against the oracle's rotation (R11), element by element,
+    and the pooled means of the rotated tensors."""
+    base = 10000.0
+    p = isa.Params(2, 3, 700, 451, D, 64, rope_base=base)
+    inp = _inputs(1, p)
+    Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
+    Qr, Kr, qc, kc, kcb, vcb = isa.rope_pool_coarse(Q, K, V, p)
+    torch.cuda.synchronize()
+    Qr_b = Qr.view(torch.int16).cpu().numpy().view(np.uint16)
+    Kr_b = Kr.view(torch.int16).cpu().numpy().view(np.uint16)
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    bad = 0
+    for bi in range(p.B):
+        for h in range(p.H):
+            qr = isa_oracle.rope(inp["Q"][1][bi, h], p.L_src, p.L_ctx, base)
+            kr = isa_oracle.rope(inp["K"][1][bi, h], p.L_src, p.L_ctx, base)
+            bad += (_rope_mismatch(Qr_b[bi, h], qr, inp["Q"][1][bi, h])
+                    + _rope_mismatch(Kr_b[bi, h], kr, inp["K"][1][bi, h]))
+            np.testing.assert_allclose(qc[bi, h].cpu().numpy(), isa_oracle.pool(qr, plan),
+                                       rtol=0, atol=1e-3)
+            np.testing.assert_allclose(kc[bi, h].cpu().numpy(), isa_oracle.pool(kr, plan),
+                                       rtol=0, atol=1e-3)
+    total = 2 * p.B * p.H * (p.L_src + p.L_ctx) * D
+    log(f"rope D={D}: {bad} of {total} rotated bf16 values differ from the oracle")
+    assert bad <= total * 1e-5
+
+
+def test_rope_forward_small_all_rows(dev):
+    """Forward with RoPE against the oracle (rotation, then the method),
+    every row; and bitwise equal to the forward without RoPE fed the rotated
+    tensors of the RoPE entry point."""
+    base = 10000.0
+    p = isa.Params(1, 2, 700, 451, 128, 64, 0.25, 0.5, 0.125, rope_base=base)
+    inp = _inputs(1, p)
+    res = _run(p, inp, dev)
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    for h in range(p.H):
+        qr = isa_oracle.rope(inp["Q"][1][0, h], p.L_src, p.L_ctx, base)
+        kr = isa_oracle.rope(inp["K"][1][0, h], p.L_src, p.L_ctx, base)
+        rep = compare_head(plan, qr, kr, inp["V"][1][0, h], _gpu_head(res, 0, h))
+        log(f"rope forward h={h}: max-abs {rep['max_abs']:.2e} excused {rep['excused']}")
+    Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
+    Qr, Kr, *_ = isa.rope_pool_coarse(Q, K, V, p)
+    p0 = isa.Params(1, 2, 700, 451, 128, 64, 0.25, 0.5, 0.125)
+    O0 = isa.forward(Qr, Kr, V, p0)
+    Og = isa.forward(Q, K, V, p)
+    torch.cuda.synchronize()
+    assert torch.equal(O0.view(torch.int16), Og.view(torch.int16))
+
+
+def test_rope_forward_ragged_workload(dev):
+    """RoPE on the ragged 11884 + 11884-token workload (both segments end in
+    a partial block; positions restart at the context segment): every
+    selection of every head, sampled rows of two heads."""
+    c = isa_inputs.CONFIGS[3]
+    base = 10000.0
+    p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"], rope_base=base)
+    inp = _inputs(3, p)
+    log("rope ragged workload: forward")
+    res = _run(p, inp, dev)
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    for h in range(p.H):
+        qr = isa_oracle.rope(inp["Q"][1][0, h], p.L_src, p.L_ctx, base)
+        kr = isa_oracle.rope(inp["K"][1][0, h], p.L_src, p.L_ctx, base)
+        rows = _sample_rows(plan, 192, 11 + h) if h in (0, p.H - 1) else np.zeros(0, dtype=np.int64)
+        rep = compare_head(plan, qr, kr, inp["V"][1][0, h], _gpu_head(res, 0, h), rows=rows)
+        if rows.size:
+            log(f"  head {h}: max-abs {rep['max_abs']:.2e} mean-abs {rep['mean_abs']:.2e} "
+                f"excused {rep['excused']}")

@@ -38,6 +38,17 @@ def test_exports_every_declared_symbol(isa):
         assert getattr(isa.lib(), n) is not None
 
 
+def test_binding_declares_every_signature(isa):
+    """Every entry point has its argument types declared in the binding (an
+    undeclared one would pass pointers as C ints), matching the header's
+    parameter count."""
+    txt = open(os.path.join(ROOT, "include", "isa.h")).read()
+    for name, args in re.findall(r"ISA_API\s+[\w\s\*]+?\b(isa_\w+)\s*\(([^)]*)\)", txt):
+        fn = getattr(isa.lib(), name)
+        assert fn.argtypes is not None, name
+        assert len(fn.argtypes) == len([a for a in args.split(",") if a.strip()]), name
+
+
 def test_plan_matches_oracle_counts(isa):
     from oracle import isa_oracle
     import isa_inputs
@@ -59,11 +70,22 @@ def test_plan_matches_oracle_counts(isa):
             assert pl[k] == getattr(o, k), (k, Ls, Lc, b, a_s, a_f, a_ns)
         assert pl["workspace_bytes"] >= 40 * o.N * o.N_kv * 8
         assert pl["scores_bytes"] >= 40 * o.N * o.N_kv * 8
+        assert pl["rope_bytes"] == 0
+
+
+def test_plan_rope_workspace(isa):
+    """RoPE adds the rotated Q and K and the cos/sin table to the forward
+    workspace; the table covers max(L_src, L_ctx) positions."""
+    for (Ls, Lc, D) in ((1024, 1024, 64), (777, 333, 128), (100, 0, 64), (333, 777, 128)):
+        off = isa.plan(isa.Params(2, 3, Ls, Lc, D, 64))
+        on = isa.plan(isa.Params(2, 3, Ls, Lc, D, 64, rope_base=10000.0))
+        assert on["rope_bytes"] >= max(Ls, Lc) * (D // 2) * 8
+        assert on["workspace_bytes"] >= off["workspace_bytes"] + 2 * 6 * (Ls + Lc) * D * 2 + on["rope_bytes"]
 
 
 def _params(isa, **kw):
     base = dict(B=1, H=2, L_src=1024, L_ctx=1024, D=128, b=64, alpha_s=0.125, alpha_f=0.5,
-                alpha_ns=0.0625, gamma=0.0)
+                alpha_ns=0.0625, gamma=0.0, rope_base=0.0)
     base.update(kw)
     return isa.IsaParams(**base)
 
@@ -73,6 +95,8 @@ def _params(isa, **kw):
     (dict(D=0), -1), (dict(b=0), -1),
     (dict(alpha_s=float("nan")), -1), (dict(alpha_f=1.5), -1), (dict(alpha_ns=-0.1), -1),
     (dict(gamma=float("nan")), -1), (dict(gamma=float("inf")), -1),
+    (dict(rope_base=float("nan")), -1), (dict(rope_base=float("inf")), -1),
+    (dict(rope_base=-10000.0), -1), (dict(rope_base=1.0), -1), (dict(rope_base=0.5), -1),
     (dict(D=96), -2), (dict(D=256), -2), (dict(b=16), -2), (dict(b=128), -2),
     (dict(L_src=64 * 4097), -2), (dict(L_ctx=64 * 4097), -2),
     (dict(L_src=64 * 4000, L_ctx=64 * 4000, alpha_s=0.05), -2),   # N_kv > 4096
@@ -101,6 +125,13 @@ def test_calls_fail_before_launch(isa):
                                   fake, fake, None) == -1
     assert L.isa_coarse_residual(ctypes.byref(p), fake, fake, fake, fake, None, fake, 1 << 40, None) == -1
     assert L.isa_coarse_residual(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 16, None) == -3
+    rp = _params(isa, rope_base=10000.0)
+    assert L.isa_rope_pool_coarse(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
+                                  fake, fake, 1 << 40, None) == -1      # RoPE off
+    assert L.isa_rope_pool_coarse(ctypes.byref(rp), fake, fake, fake, None, fake, fake, fake, fake,
+                                  fake, fake, 1 << 40, None) == -1
+    assert L.isa_rope_pool_coarse(ctypes.byref(rp), fake, fake, fake, fake, fake, fake, fake, fake,
+                                  fake, fake, 16, None) == -3
     assert L.isa_dense_attn(1, 1, 0, 128, fake, fake, fake, fake, None) == -1
     assert L.isa_dense_attn(1, 1, 16, 96, fake, fake, fake, fake, None) == -2
     assert L.isa_dense_attn(1, 1, 16, 128, None, fake, fake, fake, None) == -1
