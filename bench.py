@@ -334,6 +334,28 @@ def main():
     torch.cuda.synchronize()
     same = bool(torch.equal(O_fwd.view(torch.int16), O.view(torch.int16)))
 
+    # decoupled RoPE fused with pooling (same workload, base 10000): reads Q, K, V
+    # once, writes the rotated Q and K and the block means
+    pr_rope = isa.Params(p.B, p.H, p.L_src, p.L_ctx, p.D, p.b, p.alpha_s, p.alpha_f, p.alpha_ns,
+                         rope_base=10000.0)
+    prc = pr_rope.c()
+    Qr, Kr = torch.empty_like(Q), torch.empty_like(K)
+    ws_r = e(max(isa.plan(pr_rope)["rope_bytes"], 1), dt=torch.uint8)
+
+    def rope_pool():
+        chk("rope", lib.isa_rope_pool_coarse(ctypes.byref(prc), Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                                             Qr.data_ptr(), Kr.data_ptr(), qc.data_ptr(), kc.data_ptr(),
+                                             kcb.data_ptr(), vcb.data_ptr(), ws_r.data_ptr(),
+                                             ws_r.numel(), sp))
+    rope_pool()
+    e0.record(stream)
+    for _ in range(args.steps):
+        rope_pool()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rope_ms = e0.elapsed_time(e1) / args.steps
+    del Qr, Kr, ws_r
+
     flops = algorithmic_flops(p, pl, ctx.view(p.B, p.H, -1).cpu().numpy(),
                               si.view(p.B, p.H, -1).cpu().numpy(), fi.view(p.B, p.H, -1).cpu().numpy(),
                               ei.view(p.B, p.H, pl["n_flat"], pl["k_ns"]).cpu().numpy())
@@ -379,6 +401,9 @@ def main():
                       "flat_taylor_attn": (flops["flat_exact"] + flops["taylor"]) /
                       (per["flat_taylor_attn"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "pool_hbm_frac": pool_bytes / (per["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "rope_pool_ms": rope_ms,
+        "rope_pool_hbm_frac": (pool_bytes + 2 * BH * (p.L_src + p.L_ctx) * p.D * 2) /
+                              (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "algorithmic_tflop": {k: v / 1e12 for k, v in flops.items()},
         "dense_ms": dense_ms,
         "dense_tflops": (flops["dense"] / (dense_ms * 1e-3) / 1e12) if dense_ms else None,
