@@ -55,6 +55,15 @@ R11 decoupled RoPE (the step before (1), [RB] "Novelty"; [TW] section 6):
     rotation is done in fp32 with each product and sum rounded, and the
     result is rounded to bf16 (the arithmetic of the kernel, so both sides
     produce the same bf16 values).
+R12 backward (trainable ISA, [RB] "Core method" and Novelty (c): the
+    operator is trained end to end): the selections are piecewise constant
+    in Q, K, V, so gradients flow only through the attention terms with the
+    selections held fixed; the exact terms give the usual softmax-attention
+    gradients, the Taylor terms reach K and V through the block means
+    (each token of block j receives 1/n_j of the gradient of Kc_j, Vc_j),
+    and, when gamma != 0, the residual reaches Q, K, V through Qc, Kc, Vc.
+    The bf16 roundings of the forward (rotated Q/K, the Taylor operands) are
+    taken as the identity.
 """
 from __future__ import annotations
 
@@ -362,6 +371,87 @@ def isa_head(Q, K, V, plan: Plan, selections: dict | None = None, rows=None,
 
     return HeadResult(O, ctx_idx, sharp_idx, flat_idx, E, r, M, S, Qc, Kc, Vc,
                       _topk_gap(r, plan.k_ctx), split_gap, exact_gaps)
+
+
+# ---------------------------------------------------------------- backward
+def _attn_rows_backward(Qi, dOi, Kx, Vx, bias, scale):
+    """Gradients of o = softmax(scale * Qi Kx^T + bias) Vx for one set of
+    query rows against its key rows (bias: additive logit per key row).
+    Returns (dQi, dKx, dVx) with the softmax Jacobian written out:
+    dS = P * (dO Vx^T - rowsum(dO * o))."""
+    logits = (Qi @ Kx.T) * scale + bias[None, :]
+    m = logits.max(axis=1, keepdims=True)
+    w = np.exp(logits - m)
+    P = w / w.sum(axis=1, keepdims=True)
+    O = P @ Vx
+    dS = P * (dOi @ Vx.T - (dOi * O).sum(axis=1, keepdims=True))
+    return (dS @ Kx) * scale, (dS.T @ Qi) * scale, P.T @ dOi
+
+
+def isa_head_backward(Q, K, V, dO, plan: Plan, selections: dict | None = None,
+                      gamma: float = 0.0):
+    """Gradients (dQ, dK, dV) [L, D] fp64 of sum(dO * O) for one (batch,
+    head), O the ISA output of isa_head with the same selections (R12)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    L, D = Q.shape
+    scale = 1.0 / math.sqrt(D)
+    f = isa_head(Q, K, V, plan, selections=selections, compute_output=False)
+    J = kept_blocks(f.ctx_idx, plan)
+    counts = np.asarray(plan.counts, dtype=np.float64)
+    dQ, dK, dV = np.zeros((L, D)), np.zeros((L, D)), np.zeros((L, D))
+    dQc, dKc, dVc = np.zeros((plan.N, D)), np.zeros((plan.N, D)), np.zeros((plan.N, D))
+    J_tok = np.concatenate([_token_range(plan, j) for j in J])
+    for i in f.sharp_idx:                       # step (4): exact over the tokens of J
+        tok = _token_range(plan, i)
+        gq, gk, gv = _attn_rows_backward(Q[tok], dO[tok], K[J_tok], V[J_tok],
+                                         np.zeros(J_tok.size), scale)
+        dQ[tok] += gq
+        dK[J_tok] += gk
+        dV[J_tok] += gv
+    for r, i in enumerate(f.flat_idx):          # step (5): exact over E_i, Taylor over J \ E_i
+        tok = _token_range(plan, i)
+        Ei = f.flat_exact_idx[r]
+        Ti = np.setdiff1d(J, Ei)
+        ex = (np.concatenate([_token_range(plan, j) for j in Ei]) if Ei.size
+              else np.zeros(0, dtype=np.int64))
+        Kx = np.vstack([K[ex], f.Kc[Ti]])
+        Vx = np.vstack([V[ex], f.Vc[Ti]])
+        bias = np.concatenate([np.zeros(ex.size), np.log(counts[Ti])])
+        gq, gk, gv = _attn_rows_backward(Q[tok], dO[tok], Kx, Vx, bias, scale)
+        dQ[tok] += gq
+        dK[ex] += gk[:ex.size]
+        dV[ex] += gv[:ex.size]
+        dKc[Ti] += gk[ex.size:]
+        dVc[Ti] += gv[ex.size:]
+    if gamma != 0.0:                            # step (6) residual on the pooled rows
+        dOc = np.stack([dO[_token_range(plan, i)].sum(axis=0) for i in range(plan.N)]) * gamma
+        gq, gk, gv = _attn_rows_backward(f.Qc, dOc, f.Kc[J], f.Vc[J], np.zeros(J.size), scale)
+        dQc += gq
+        dKc[J] += gk
+        dVc[J] += gv
+    for j in range(plan.N):                     # through the block means of step (1)
+        tok = _token_range(plan, j)
+        dQ[tok] += dQc[j] / counts[j]
+        dK[tok] += dKc[j] / counts[j]
+        dV[tok] += dVc[j] / counts[j]
+    return dQ, dK, dV
+
+
+def rope_backward(dXr: np.ndarray, L_src: int, L_ctx: int, base: float) -> np.ndarray:
+    """Gradient through the rotation of R11 (the transpose of each 2x2
+    rotation, with the same fp32 cos/sin values), fp64, rounding taken as
+    the identity (R12)."""
+    dXr = np.asarray(dXr, dtype=np.float64)
+    c, s = rope_tables(rope_positions(L_src, L_ctx), dXr.shape[1], base)
+    c, s = c.astype(np.float64), s.astype(np.float64)
+    gx, gy = dXr[:, 0::2], dXr[:, 1::2]
+    out = np.empty_like(dXr)
+    out[:, 0::2] = gx * c + gy * s
+    out[:, 1::2] = gy * c - gx * s
+    return out
 
 
 def isa_forward(Q, K, V, L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns, heads=None, gamma=0.0):
