@@ -24,7 +24,7 @@ ISA_ERR_HIP = -4
 
 EXPORTED = ("isa_plan", "isa_pool_coarse", "isa_rope_pool_coarse", "isa_ctx_topk", "isa_sharpness_split",
             "isa_sharp_attn", "isa_flat_taylor_attn", "isa_coarse_residual", "isa_forward",
-            "isa_dense_attn", "isa_strerror")
+            "isa_backward", "isa_dense_attn", "isa_strerror")
 
 
 class IsaParams(ctypes.Structure):
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
         L.isa_flat_taylor_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.isa_coarse_residual.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
         L.isa_forward.argtypes = [P, vp, vp, vp, vp, vp, sz, ctypes.POINTER(IsaDebug), vp]
+        L.isa_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.isa_dense_attn.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.isa_strerror.argtypes = [ctypes.c_int]
         L.isa_strerror.restype = ctypes.c_char_p
@@ -180,6 +181,28 @@ def forward(Q, K, V, p: Params, debug: bool = False, out=None, workspace=None):
                            ctypes.byref(dbg_c) if dbg_c is not None else None, _stream(dev))
     _check("isa_forward", rc)
     return (O, dbg_t) if debug else O
+
+
+def workspace(p: Params, device):
+    """A workspace for forward() and backward() (plan()["workspace_bytes"] bytes)."""
+    torch = _torch()
+    return _empty((plan(p)["workspace_bytes"],), torch.uint8, device)
+
+
+def backward(Q, K, V, O, dO, p: Params, workspace, out=None):
+    """Gradients (dQ, dK, dV) of sum(dO * O), selections held fixed. Q, K, V, O
+    and `workspace` must be those of the forward() call that produced O (its
+    workspace argument, unmodified since)."""
+    torch = _torch()
+    _check_qkv(p, Q, K, V, O, dO)
+    if workspace.numel() < plan(p)["workspace_bytes"]:
+        raise ValueError("workspace smaller than plan()['workspace_bytes']")
+    dQ, dK, dV = out if out is not None else (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    _check("isa_backward", lib().isa_backward(
+        ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), dO.data_ptr(),
+        dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        _stream(Q.device)))
+    return dQ, dK, dV
 
 
 def pool_coarse(Q, K, V, p: Params):

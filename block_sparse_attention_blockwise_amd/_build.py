@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libisa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["isa_api.cpp", "isa_pool.hip", "isa_select.hip", "isa_attn.hip"]
+SOURCES = ["isa_api.cpp", "isa_pool.hip", "isa_select.hip", "isa_attn.hip", "isa_attn_bwd.hip"]
 ARCH = "gfx950"
 
 
@@ -38,7 +38,8 @@ def compile_flags() -> list[str]:
 
 # The attention kernels take max/min of finite or -inf logits only; without
 # NaN semantics the compiler emits v_max3 without quieting operands.
-EXTRA_FLAGS = {"isa_attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+EXTRA_FLAGS = {"isa_attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+               "isa_attn_bwd.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _compile(src: str) -> str:

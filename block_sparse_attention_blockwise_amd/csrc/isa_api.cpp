@@ -27,7 +27,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   size_t qc, kc, kcb, vcb, ctx_idx, ctx_score, sharp, sharp_idx, flat_idx, exact, srows;
-  size_t qr, kr, rope, total;   // RoPE buffers (only when rope_base > 0)
+  size_t qr, kr, rope;          // RoPE buffers (only when rope_base > 0)
+  size_t lse;                   // saved by isa_forward for isa_backward
+  size_t delta, dkc, dvc, ebits, inv_off, inv_list;   // backward scratch
+  size_t total;
 };
 
 // cos/sin table of the decoupled RoPE: one float2 per (position, pair).
@@ -58,6 +61,13 @@ Layout make_layout(const IsaShape& s) {
   l.qr = o;        o = align256(o + qkr);
   l.kr = o;        o = align256(o + qkr);
   l.rope = o;      o = align256(o + rope_table_bytes(s));
+  l.lse = o;       o = align256(o + bh * s.L * 4);
+  l.delta = o;     o = align256(o + bh * s.L * 4);
+  l.dkc = o;       o = align256(o + bh * s.N * s.D * 4);
+  l.dvc = o;       o = align256(o + bh * s.N * s.D * 4);
+  l.ebits = o;     o = align256(o + bh * s.n_flat * (size_t)((s.N_kv + 63) / 64) * 8);
+  l.inv_off = o;   o = align256(o + bh * (size_t)(s.N_kv + 1) * 4);
+  l.inv_list = o;  o = align256(o + bh * s.n_flat * (size_t)s.k_ns * 4);
   l.total = o;
   return l;
 }
@@ -191,7 +201,7 @@ int isa_sharp_attn(const isa_params_t* p, const void* Q, const void* K, const vo
   if (!Q || !K || !V || !O || (!ctx_idx && s.k_ctx > 0) || (!sharp_idx && s.n_sharp > 0))
     return ISA_ERR_ARG;
   return hip_status(isa_launch_sharp_attn(s, (const uint16_t*)Q, (const uint16_t*)K,
-                                          (const uint16_t*)V, ctx_idx, sharp_idx, (uint16_t*)O,
+                                          (const uint16_t*)V, ctx_idx, sharp_idx, (uint16_t*)O, nullptr,
                                           as_stream(stream)));
 }
 
@@ -208,7 +218,8 @@ int isa_flat_taylor_attn(const isa_params_t* p, const void* Q, const void* K, co
   return hip_status(isa_launch_flat_attn(s, (const uint16_t*)Q, (const uint16_t*)K,
                                          (const uint16_t*)V, (const uint16_t*)kc_bf16,
                                          (const uint16_t*)vc_bf16, ctx_idx, flat_idx,
-                                         flat_exact_idx, (uint16_t*)O, as_stream(stream)));
+                                         flat_exact_idx, (uint16_t*)O, nullptr,
+                                         as_stream(stream)));
 }
 
 int isa_coarse_residual(const isa_params_t* p, const double* qc, const double* kc,
@@ -270,9 +281,10 @@ int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void*
   if (e == hipSuccess) e = isa_launch_sharpness(s, srows, sharp, st);
   if (e == hipSuccess) e = isa_launch_split(s, sharp, sharp_idx, flat_idx, st);
   if (e == hipSuccess) e = isa_launch_flat_topk(s, srows, ctx_idx, flat_idx, exact, st);
-  if (e == hipSuccess) e = isa_launch_sharp_attn(s, q, k, v, ctx_idx, sharp_idx, (uint16_t*)O, st);
+  float* lse = (float*)(w + l.lse);
+  if (e == hipSuccess) e = isa_launch_sharp_attn(s, q, k, v, ctx_idx, sharp_idx, (uint16_t*)O, lse, st);
   if (e == hipSuccess)
-    e = isa_launch_flat_attn(s, q, k, v, kcb, vcb, ctx_idx, flat_idx, exact, (uint16_t*)O, st);
+    e = isa_launch_flat_attn(s, q, k, v, kcb, vcb, ctx_idx, flat_idx, exact, (uint16_t*)O, lse, st);
   if (e == hipSuccess && s.gamma != 0.0f)
     e = isa_launch_coarse_residual(s, srows, vcb, ctx_idx, (uint16_t*)O, st);
   if (e == hipSuccess && dbg) {
@@ -293,6 +305,44 @@ int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void*
     }
   }
   return hip_status(e);
+}
+
+int isa_backward(const isa_params_t* p, const void* Q, const void* K, const void* V,
+                 const void* O, const void* dO, void* dQ, void* dK, void* dV, void* ws,
+                 size_t ws_bytes, void* stream) {
+  IsaShape s;
+  int rc = make_shape(p, &s);
+  if (rc != ISA_OK) return rc;
+  if (!Q || !K || !V || !O || !dO || !dQ || !dK || !dV || !ws) return ISA_ERR_ARG;
+  if (s.gamma != 0.0f) return ISA_ERR_UNSUPPORTED;
+  const Layout l = make_layout(s);
+  if (ws_bytes < l.total) return ISA_ERR_WORKSPACE;
+  char* w = (char*)ws;
+  IsaBwdBuffers b{};
+  const bool rope = s.rope_base != 0.0;
+  b.Q = rope ? (const uint16_t*)(w + l.qr) : (const uint16_t*)Q;
+  b.K = rope ? (const uint16_t*)(w + l.kr) : (const uint16_t*)K;
+  b.V = (const uint16_t*)V;
+  b.O = (const uint16_t*)O;
+  b.dO = (const uint16_t*)dO;
+  b.lse = (const float*)(w + l.lse);
+  b.delta = (float*)(w + l.delta);
+  b.kcb = (const uint16_t*)(w + l.kcb);
+  b.vcb = (const uint16_t*)(w + l.vcb);
+  b.ctx_idx = (const int32_t*)(w + l.ctx_idx);
+  b.sharp_idx = (const int32_t*)(w + l.sharp_idx);
+  b.flat_idx = (const int32_t*)(w + l.flat_idx);
+  b.exact = (const int32_t*)(w + l.exact);
+  b.ebits = (uint64_t*)(w + l.ebits);
+  b.inv_off = (int32_t*)(w + l.inv_off);
+  b.inv_list = (int32_t*)(w + l.inv_list);
+  b.dkc = (float*)(w + l.dkc);
+  b.dvc = (float*)(w + l.dvc);
+  b.rope = rope ? (const float2*)(w + l.rope) : nullptr;
+  b.dQ = (uint16_t*)dQ;
+  b.dK = (uint16_t*)dK;
+  b.dV = (uint16_t*)dV;
+  return hip_status(isa_launch_backward(s, b, as_stream(stream)));
 }
 
 int isa_dense_attn(int32_t B, int32_t H, int32_t L, int32_t D, const void* Q, const void* K,

@@ -67,6 +67,7 @@ struct AttnArgs {
   const int32_t* ctx_idx;    // [B,H,k_ctx] kept context blocks (global ids)
   const int32_t* qlist;      // sharp_idx or flat_idx [B,H,n_q]
   const int32_t* exact;      // flat: [B,H,n_flat,k_ns]
+  float* lse;                // optional [B,H,L]: log2 of each row's softmax denominator
   int n_q;
   int ntiles_exact;
   int ntiles;
@@ -631,6 +632,9 @@ void attn_kernel(AttnArgs a) {
     float lt = xor16_sum(lsum[qt]);
     lt = xor32_sum(lt);
     if (!qval[qt]) continue;
+    // log2-domain log-sum-exp of the row (m is the running reference of the
+    // logits in log2 units), kept for the backward pass
+    if (a.lse != nullptr && g == 0) a.lse[head + qtok[qt]] = m[qt] + __log2f(lt);
     const float inv = 1.0f / lt;
     uint16_t* orow = a.O + (head + qtok[qt]) * D;
 #pragma unroll
@@ -673,9 +677,11 @@ AttnArgs base_args(const IsaShape& s, const uint16_t* Q, const uint16_t* K, cons
 
 hipError_t isa_launch_sharp_attn(const IsaShape& s, const uint16_t* Q, const uint16_t* K,
                                  const uint16_t* V, const int32_t* ctx_idx,
-                                 const int32_t* sharp_idx, uint16_t* O, hipStream_t st) {
+                                 const int32_t* sharp_idx, uint16_t* O, float* lse,
+                                 hipStream_t st) {
   if (s.n_sharp == 0) return hipSuccess;
   AttnArgs a = base_args(s, Q, K, V, O);
+  a.lse = lse;
   a.ctx_idx = ctx_idx;
   a.qlist = sharp_idx;
   a.n_q = s.n_sharp;
@@ -701,9 +707,10 @@ hipError_t isa_launch_flat_attn(const IsaShape& s, const uint16_t* Q, const uint
                                 const uint16_t* V, const uint16_t* kc_bf16,
                                 const uint16_t* vc_bf16, const int32_t* ctx_idx,
                                 const int32_t* flat_idx, const int32_t* flat_exact_idx,
-                                uint16_t* O, hipStream_t st) {
+                                uint16_t* O, float* lse, hipStream_t st) {
   if (s.n_flat == 0) return hipSuccess;
   AttnArgs a = base_args(s, Q, K, V, O);
+  a.lse = lse;
   a.kcb = kc_bf16;
   a.vcb = vc_bf16;
   a.ctx_idx = ctx_idx;

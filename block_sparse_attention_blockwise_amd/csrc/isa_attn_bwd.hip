@@ -1,0 +1,794 @@
+// Backward pass of In-context Sparse Attention on gfx950 (the operator is
+// trained end to end: paper.rainbus.top summary of arXiv 2605.04569, "Core
+// method" and "Novelty" (c)).
+//
+// The selections of the forward pass are piecewise constant, so the
+// gradients flow through the attention terms with J, the sharp/flat split
+// and every E_i held fixed. For a query row t with key rows u (exact tokens,
+// and for a flat block also the pooled keys Kc_j with logit offset ln n_j):
+//   P = softmax over u,   Delta_t = dO_t . O_t,   dS_tu = P_tu (dO_t . v_u - Delta_t),
+//   dq_t = sum_u dS_tu k_u / sqrt(D),   dk_u += dS_tu q_t / sqrt(D),   dv_u += P_tu dO_t.
+// The pooled keys pass their gradients to the tokens of their block through
+// the mean of step (1): each token of block j receives dKc_j / n_j and
+// dVc_j / n_j.
+//
+// Kernels (all deterministic: every sum has a fixed order, no float atomics):
+//   * bwd_prep_kernel: per head, a bitmap of E_i over the positions of J and,
+//     for every kept block, the ascending list of flat blocks whose E_i holds it;
+//   * delta_kernel: Delta_t for every row;
+//   * dq_kernel (query-major, as the forward): per query block, over the key
+//     tiles the forward used; S^T = K Q^T and dP^T = V dO^T on the matrix
+//     cores, P recomputed from the saved log-sum-exp, dQ^T += K^T dS^T;
+//   * dkv_kernel (key-major): per kept block j, its keys held in registers,
+//     over every query block that reads j exactly (all sharp blocks and the
+//     flat blocks listing j in E_i); S = Q K^T, dP = dO V^T, dV^T += dO^T P,
+//     dK^T += Q^T dS; the pooled gradients dKc_j / n_j, dVc_j / n_j are added
+//     before the rows are written; blocks outside J get zero gradients;
+//   * dkv_pooled_kernel (key-major over the pooled keys): per 64 positions of
+//     J, over every flat block; writes dKc, dVc (fp32).
+// With decoupled RoPE the gradients of the rotated Q and K are turned back by
+// the transposed rotation in the epilogues.
+#include "isa_internal.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef short short4_t __attribute__((__vector_size__(8)));
+typedef float float4_t __attribute__((__vector_size__(16)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+struct bf16x2x4_t { bf16x2_t a, b, c, d; };
+
+constexpr int kKeyTile = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdArgs {
+  IsaShape s;
+  const uint16_t* Q;          // the attention inputs (rotated when RoPE is on)
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* dO;
+  const float* lse;           // [B,H,L] log2-domain log-sum-exp from the forward
+  const float* delta;         // [B,H,L]
+  const uint16_t* kcb;        // [B,H,N,D] bf16 block means (the forward's Taylor operands)
+  const uint16_t* vcb;
+  const int32_t* ctx_idx;     // [B,H,k_ctx]
+  const int32_t* qlist;       // dq: sharp_idx or flat_idx
+  const int32_t* sharp_idx;   // [B,H,n_sharp]
+  const int32_t* flat_idx;    // [B,H,n_flat]
+  const int32_t* exact;       // [B,H,n_flat,k_ns]
+  const uint64_t* ebits;      // [B,H,n_flat,W] bit p of row r: position p of J is in E_r
+  const int32_t* inv_off;     // [B,H,N_kv+1]
+  const int32_t* inv_list;    // [B,H,n_flat*k_ns] flat block ids reading each position exactly
+  const float* dkc;           // [B,H,N,D] pooled-key gradients (nullable)
+  const float* dvc;
+  float* dkc_out;
+  float* dvc_out;
+  const float2* rope;         // cos/sin table (nullable: no RoPE)
+  uint16_t* dQ;
+  uint16_t* dK;
+  uint16_t* dV;
+  int n_q;
+  int ntiles_exact;
+  int ntiles;
+  int W;                      // 64-bit words per bitmap row
+};
+
+__device__ inline short4_t lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(p));
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Position of global block j in the kept list J, or -1.
+__device__ inline int kept_pos(const IsaShape& s, const int32_t* ctx_row, int j) {
+  if (j >= 0 && j < s.N_src) return j;
+  if (j < s.N_src || j >= s.N) return -1;
+  int lo = 0, hi = s.k_ctx;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (ctx_row[mid] < j) lo = mid + 1; else hi = mid;
+  }
+  return (lo < s.k_ctx && ctx_row[lo] == j) ? s.N_src + lo : -1;
+}
+
+// Global block id at position q of J, or -1.
+__device__ inline int kept_id(const IsaShape& s, const int32_t* ctx_row, int q) {
+  if (q < s.N_src) return q;
+  if (q >= s.N_kv) return -1;
+  const int j = ctx_row[q - s.N_src];
+  return (j >= s.N_src && j < s.N) ? j : -1;
+}
+
+// ---------------------------------------------------------------- tile math
+// s[nf][mt] = A rows (16 mt + 4g + e of the LDS tile) . B fragment nf
+// (column c16); A is read from LDS rows of stride 2D+32 bytes.
+template <int D, int MT, int NF>
+__device__ __forceinline__ void mm_rows(const char* lds, const bf16x8_t (&f)[NF][D / 32],
+                                        float4_t (&s)[NF][MT], int g, int c16) {
+  constexpr int STR = 2 * D + 32;
+#pragma unroll
+  for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) s[nf][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(lds + (16 * mt + c16) * STR + (32 * kk + 8 * g) * 2);
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf)
+        s[nf][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, f[nf][kk], s[nf][mt], 0, 0, 0);
+    }
+  }
+}
+
+// acc[nf][dt] += (LDS rows)^T . pk[nf]: the LDS tile (16*MT rows) is read
+// transposed, its rows being the contraction index in the order pack_bf16
+// produces.
+template <int D, int MT, int NF>
+__device__ __forceinline__ void mm_tr(const char* lds, const bf16x8_t (&pk)[NF][MT / 2],
+                                      float4_t (&acc)[NF][D / 16], int g, int c16) {
+  constexpr int STR = 2 * D + 32;
+  const int tr_row = 4 * g + (c16 >> 2);
+  const int tr_col = 4 * (c16 & 3);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+    for (int kc = 0; kc < MT / 2; ++kc) {
+      const short4_t lo = lds_read_tr(lds + (32 * kc + tr_row) * STR + (16 * dt + tr_col) * 2);
+      const short4_t hi = lds_read_tr(lds + (32 * kc + 16 + tr_row) * STR + (16 * dt + tr_col) * 2);
+      const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf)
+        acc[nf][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[nf][kc], acc[nf][dt], 0, 0, 0);
+    }
+  }
+}
+
+// Rounds an mm_rows result to bf16 in the operand layout mm_tr expects.
+template <int MT, int NF>
+__device__ __forceinline__ void pack_bf16(const float4_t (&x)[NF][MT], bf16x8_t (&pk)[NF][MT / 2]) {
+#pragma unroll
+  for (int nf = 0; nf < NF; ++nf) {
+#pragma unroll
+    for (int kc = 0; kc < MT / 2; ++kc) {
+      bf16x2_t h[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i0 = 8 * kc + 2 * u;
+        h[u] = __builtin_convertvector((float2_t){x[nf][i0 >> 2][i0 & 3], x[nf][(i0 + 1) >> 2][(i0 + 1) & 3]},
+                                       bf16x2_t);
+      }
+      pk[nf][kc] = __builtin_bit_cast(bf16x8_t, (bf16x2x4_t){h[0], h[1], h[2], h[3]});
+    }
+  }
+}
+
+// Transposed RoPE rotation of one gradient pair (gx, gy) at position `pos`,
+// pair index `i` (the inverse of the forward rotation by angle pos*f_i).
+__device__ inline void rope_back(const float2* tab, int half, int pos, int i, float& gx, float& gy) {
+  const float2 cs = tab[(size_t)pos * half + i];
+  const float x = gx * cs.x + gy * cs.y;
+  const float y = gy * cs.x - gx * cs.y;
+  gx = x;
+  gy = y;
+}
+
+// Writes 4 consecutive gradient values (d0..d0+3 of one token row) as bf16,
+// after the optional RoPE transpose (pairs (d0, d0+1) and (d0+2, d0+3)).
+__device__ inline void store4(uint16_t* row, int d0, float4_t v, const float2* rope, int half, int pos) {
+  float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+  if (rope != nullptr) {
+    rope_back(rope, half, pos, d0 >> 1, x0, x1);
+    rope_back(rope, half, pos, (d0 >> 1) + 1, x2, x3);
+  }
+  uint2 w;
+  w.x = pack_bf16x2(x0, x1);
+  w.y = pack_bf16x2(x2, x3);
+  *reinterpret_cast<uint2*>(row + d0) = w;
+}
+
+// ---------------------------------------------------------------- prep
+// One workgroup per head: E bitmap, then the per-position lists of flat
+// blocks that read a kept block exactly (ascending block ids).
+constexpr int kPrepThreads = 1024;
+
+__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
+  const IsaShape& s = a.s;
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
+  const int32_t* ex = a.exact + (size_t)bh * s.n_flat * s.k_ns;
+  const int32_t* frow = a.flat_idx + (size_t)bh * s.n_flat;
+  uint64_t* bits = const_cast<uint64_t*>(a.ebits) + (size_t)bh * s.n_flat * a.W;
+  int32_t* off = const_cast<int32_t*>(a.inv_off) + (size_t)bh * (s.N_kv + 1);
+  int32_t* lst = const_cast<int32_t*>(a.inv_list) + (size_t)bh * s.n_flat * s.k_ns;
+  __shared__ int cnt[ISA_MAX_NKV + 1];
+  __shared__ int cur[ISA_MAX_NKV];
+  __shared__ int part[kPrepThreads];
+  for (int p = tid; p <= s.N_kv; p += kPrepThreads) cnt[p] = 0;
+  __syncthreads();
+  for (int r = tid; r < s.n_flat; r += kPrepThreads) {
+    uint64_t* brow = bits + (size_t)r * a.W;
+    for (int w = 0; w < a.W; ++w) brow[w] = 0;
+    int cw = -1;
+    uint64_t word = 0;
+    for (int q = 0; q < s.k_ns; ++q) {
+      const int p = kept_pos(s, ctx_row, ex[(size_t)r * s.k_ns + q]);
+      if (p < 0) continue;
+      atomicAdd(&cnt[p], 1);
+      if ((p >> 6) != cw) {
+        if (cw >= 0) brow[cw] = word;
+        cw = p >> 6;
+        word = 0;
+      }
+      word |= 1ull << (p & 63);
+    }
+    if (cw >= 0) brow[cw] = word;
+  }
+  __syncthreads();
+  // exclusive scan of cnt[0..N_kv) in contiguous chunks
+  const int per = (s.N_kv + kPrepThreads - 1) / kPrepThreads;
+  const int p0 = tid * per, p1 = min(p0 + per, s.N_kv);
+  int sum = 0;
+  for (int p = p0; p < p1; ++p) sum += cnt[p];
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int t = 0; t < kPrepThreads; ++t) {
+      const int v = part[t];
+      part[t] = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  int acc = part[tid];
+  for (int p = p0; p < p1; ++p) {
+    const int v = cnt[p];
+    off[p] = acc;
+    cur[p] = acc;
+    acc += v;
+  }
+  if (tid == kPrepThreads - 1) off[s.N_kv] = part[tid] + sum;
+  __syncthreads();
+  for (int r = tid; r < s.n_flat; r += kPrepThreads) {
+    for (int q = 0; q < s.k_ns; ++q) {
+      const int p = kept_pos(s, ctx_row, ex[(size_t)r * s.k_ns + q]);
+      if (p < 0) continue;
+      const int slot = atomicAdd(&cur[p], 1);
+      lst[slot] = frow[r];
+    }
+  }
+  __syncthreads();
+  // the slots were taken in arbitrary order: sort each list ascending
+  for (int p = tid; p < s.N_kv; p += kPrepThreads) {
+    const int b0 = off[p], b1 = cur[p];
+    for (int x = b0 + 1; x < b1; ++x) {
+      const int v = lst[x];
+      int y = x - 1;
+      while (y >= b0 && lst[y] > v) {
+        lst[y + 1] = lst[y];
+        --y;
+      }
+      lst[y + 1] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- Delta
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ dO,
+                                                    const uint16_t* __restrict__ O,
+                                                    float* __restrict__ delta, size_t rows) {
+  constexpr int TPR = D / 8;
+  const size_t row = ((size_t)blockIdx.x * 256 + threadIdx.x) / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 x = *reinterpret_cast<const uint4*>(dO + row * D + c * 8);
+    const uint4 y = *reinterpret_cast<const uint4*>(O + row * D + c * 8);
+    const uint32_t xu[4] = {x.x, x.y, x.z, x.w}, yu[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc += __uint_as_float(xu[i] << 16) * __uint_as_float(yu[i] << 16);
+      acc += __uint_as_float(xu[i] & 0xffff0000u) * __uint_as_float(yu[i] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+  if (row < rows && c == 0) delta[row] = acc;
+}
+
+// ---------------------------------------------------------------- dQ
+// One query block per workgroup (NWAVES = b/16 waves, 16 rows each); key
+// tiles of 64 keys as in the forward: sharp blocks over the tokens of J,
+// flat blocks over the tokens of E_i and then the pooled keys of J.
+enum : int { kSharp = 1, kFlat = 2 };
+
+template <int D, int MODE, int NWAVES>
+__global__ __launch_bounds__(NWAVES * 64) void dq_kernel(BwdArgs a) {
+  constexpr int NT = NWAVES * 64;
+  constexpr int STR = 2 * D + 32;
+  constexpr int CPR = D / 8;
+  constexpr int CH = kKeyTile * CPR / NT;
+  constexpr int KK = D / 32;
+  constexpr int DT = D / 16;
+  static_assert(CH >= 1 && NT % CPR == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) char k_lds[kKeyTile * STR];
+  __shared__ __attribute__((aligned(16))) char v_lds[kKeyTile * STR];
+  __shared__ __attribute__((aligned(16))) float bias_lds[kKeyTile];
+  extern __shared__ int tabs[];   // sharp: [N_kv]; flat: [k_ns] then [N_kv]
+
+  const IsaShape& s = a.s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y;
+  const size_t head = (size_t)bh * s.L;
+  const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
+  const int b = s.b, lb = b == 64 ? 6 : 5;
+
+  // this lane's query row
+  const int jq = a.qlist[(size_t)bh * a.n_q + blockIdx.x];
+  int qst, qn;
+  isa_block_range(s, jq, qst, qn);
+  const int lr = wave * 16 + c16;
+  const bool qval = lr < qn;
+  const int qtok = qst + (qval ? lr : 0);
+  bf16x8_t qf[1][KK], df[1][KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    uint4 wq = make_uint4(0, 0, 0, 0), wd = make_uint4(0, 0, 0, 0);
+    if (qval) {
+      wq = *reinterpret_cast<const uint4*>(a.Q + (head + qtok) * D + 32 * kk + 8 * g);
+      wd = *reinterpret_cast<const uint4*>(a.dO + (head + qtok) * D + 32 * kk + 8 * g);
+    }
+    qf[0][kk] = __builtin_bit_cast(bf16x8_t, wq);
+    df[0][kk] = __builtin_bit_cast(bf16x8_t, wd);
+  }
+  const float lse2 = qval ? a.lse[head + qtok] : INFINITY;
+  const float dl = qval ? a.delta[head + qtok] : 0.0f;
+
+  // key tables: (start << 7) | n per listed block; pooled: (j << 8) | (n << 1) | in_E
+  int* jtab = tabs;
+  int* ptab = tabs + (MODE == kFlat ? s.k_ns : 0);
+  int ntab;
+  if (MODE == kSharp) {
+    ntab = s.N_kv;
+    for (int q = tid; q < s.N_kv; q += NT) {
+      const int j = kept_id(s, ctx_row, q);
+      int st = 0, n = 0;
+      if (j >= 0) isa_block_range(s, j, st, n);
+      jtab[q] = (st << 7) | n;
+    }
+  } else {
+    ntab = s.k_ns;
+    const int32_t* ex = a.exact + ((size_t)bh * s.n_flat + blockIdx.x) * s.k_ns;
+    for (int q = tid; q < s.k_ns; q += NT) {
+      const int j = ex[q];
+      int st = 0, n = 0;
+      if (j >= 0 && j < s.N) isa_block_range(s, j, st, n);
+      jtab[q] = (st << 7) | n;
+    }
+    for (int p = tid; p < s.N_kv; p += NT) {
+      const int j = kept_id(s, ctx_row, p);
+      int st = 0, n = 0;
+      if (j >= 0) isa_block_range(s, j, st, n);
+      ptab[p] = j >= 0 ? ((j << 8) | (n << 1)) : 1;
+    }
+    __syncthreads();
+    for (int q = tid; q < s.k_ns; q += NT) {
+      const int p = kept_pos(s, ctx_row, ex[q]);
+      if (p >= 0) ptab[p] |= 1;
+    }
+  }
+  __syncthreads();
+
+  const int per = kKeyTile >> lb;
+  const uint16_t* Kh = a.K + head * D;
+  const uint16_t* Vh = a.V + head * D;
+  const uint16_t* kch = MODE == kFlat ? a.kcb + (size_t)bh * s.N * D : nullptr;
+  const uint16_t* vch = MODE == kFlat ? a.vcb + (size_t)bh * s.N * D : nullptr;
+  const int c8 = tid % CPR;
+  const float cscale = kLog2e / sqrtf((float)D);
+  float4_t dq[1][DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[0][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int t = 0; t < a.ntiles; ++t) {
+    uint4 kr[CH], vr[CH];
+    float br[CH];
+    uint32_t vm[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int slot = (tid + i * NT) / CPR;
+      const uint16_t *kp, *vp;
+      bool valid;
+      float bias;
+      if (MODE == kFlat && t >= a.ntiles_exact) {
+        const int p = (t - a.ntiles_exact) * kKeyTile + slot;
+        const int e = p < s.N_kv ? ptab[p] : 1;
+        const int n = (e >> 1) & 127;
+        valid = !(e & 1) && n > 0;
+        const size_t row = (size_t)(valid ? (e >> 8) : 0) * D;
+        kp = kch + row;
+        vp = vch + row;
+        bias = valid ? __log2f((float)n) : -INFINITY;
+      } else {
+        const int q = t * per + (slot >> lb), o = slot & (b - 1);
+        const int e = q < ntab ? jtab[q] : 0;
+        valid = o < (e & 127);
+        const size_t row = (size_t)(valid ? (e >> 7) + o : 0) * D;
+        kp = Kh + row;
+        vp = Vh + row;
+        bias = valid ? 0.0f : -INFINITY;
+      }
+      vm[i] = valid ? 0xffffffffu : 0u;
+      br[i] = bias;
+      kr[i] = *reinterpret_cast<const uint4*>(kp + c8 * 8);
+      vr[i] = *reinterpret_cast<const uint4*>(vp + c8 * 8);
+    }
+    if (t > 0) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int slot = (tid + i * NT) / CPR;
+      const uint32_t m = vm[i];
+      *reinterpret_cast<uint4*>(&k_lds[slot * STR + c8 * 16]) =
+          make_uint4(kr[i].x & m, kr[i].y & m, kr[i].z & m, kr[i].w & m);
+      *reinterpret_cast<uint4*>(&v_lds[slot * STR + c8 * 16]) =
+          make_uint4(vr[i].x & m, vr[i].y & m, vr[i].z & m, vr[i].w & m);
+      if (c8 == 0) bias_lds[slot] = br[i];
+    }
+    __syncthreads();
+    float4_t sc[1][4], dp[1][4];
+    mm_rows<D, 4, 1>(k_lds, qf, sc, g, c16);
+    mm_rows<D, 4, 1>(v_lds, df, dp, g, c16);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const float4_t bv = *reinterpret_cast<const float4_t*>(bias_lds + 16 * mt + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][mt][e], cscale, bv[e]) - lse2);
+        sc[0][mt][e] = p * (dp[0][mt][e] - dl);
+      }
+    }
+    bf16x8_t pk[1][2];
+    pack_bf16<4, 1>(sc, pk);
+    mm_tr<D, 4, 1>(k_lds, pk, dq, g, c16);
+  }
+
+  if (!qval) return;
+  const float rs = 1.0f / sqrtf((float)D);
+  const int pos = qtok - (jq < s.N_src ? 0 : s.L_src);
+  uint16_t* row = a.dQ + (head + qtok) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) store4(row, 16 * dt + 4 * g, dq[0][dt] * rs, a.rope, D / 2, pos);
+}
+
+// ---------------------------------------------------------------- dK, dV
+// Loads the b token rows of query block jq (Q and dO) into LDS, zero rows
+// past its n valid tokens, and the rows' log-sum-exp and Delta (+inf and 0
+// for the padding, so those rows get zero probability).
+template <int D, int NT, int BR>
+__device__ __forceinline__ void load_query_block(const BwdArgs& a, size_t head, int jq, char* q_lds,
+                                                 char* d_lds, float* l_lds, float* dl_lds, int tid) {
+  constexpr int STR = 2 * D + 32;
+  constexpr int CPR = D / 8;
+  constexpr int CHQ = BR * CPR / NT;
+  static_assert(CHQ >= 1 && (BR * CPR) % NT == 0, "query tile split");
+  int st, n;
+  isa_block_range(a.s, jq, st, n);
+  uint4 qr[CHQ], dr[CHQ];
+#pragma unroll
+  for (int i = 0; i < CHQ; ++i) {
+    const int ch = tid + i * NT, r = ch / CPR, c = ch % CPR;
+    qr[i] = make_uint4(0, 0, 0, 0);
+    dr[i] = make_uint4(0, 0, 0, 0);
+    if (r < n) {
+      qr[i] = *reinterpret_cast<const uint4*>(a.Q + (head + st + r) * D + c * 8);
+      dr[i] = *reinterpret_cast<const uint4*>(a.dO + (head + st + r) * D + c * 8);
+    }
+  }
+  float lv = INFINITY, dv = 0.0f;
+  if (tid < BR && tid < n) {
+    lv = a.lse[head + st + tid];
+    dv = a.delta[head + st + tid];
+  }
+  __syncthreads();   // previous block fully consumed
+#pragma unroll
+  for (int i = 0; i < CHQ; ++i) {
+    const int ch = tid + i * NT, r = ch / CPR, c = ch % CPR;
+    *reinterpret_cast<uint4*>(q_lds + r * STR + c * 16) = qr[i];
+    *reinterpret_cast<uint4*>(d_lds + r * STR + c * 16) = dr[i];
+  }
+  if (tid < BR) {
+    l_lds[tid] = lv;
+    dl_lds[tid] = dv;
+  }
+  __syncthreads();
+}
+
+// One query block against this wave's 16 keys (kf, vf in registers, per-lane
+// additive logit kbias in log2 units): accumulates dK^T (raw, before the
+// 1/sqrt(D) scale) and dV^T.
+template <int D, int MT>
+__device__ __forceinline__ void kv_block(const char* q_lds, const char* d_lds, const float* l_lds,
+                                         const float* dl_lds, const bf16x8_t (&kf)[1][D / 32],
+                                         const bf16x8_t (&vf)[1][D / 32], float kbias, float cscale,
+                                         float4_t (&dk)[1][D / 16], float4_t (&dv)[1][D / 16],
+                                         int g, int c16) {
+  float4_t sc[1][MT], dp[1][MT];
+  mm_rows<D, MT, 1>(q_lds, kf, sc, g, c16);
+  mm_rows<D, MT, 1>(d_lds, vf, dp, g, c16);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const float4_t lv = *reinterpret_cast<const float4_t*>(l_lds + 16 * mt + 4 * g);
+    const float4_t dl = *reinterpret_cast<const float4_t*>(dl_lds + 16 * mt + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][mt][e], cscale, kbias) - lv[e]);
+      sc[0][mt][e] = p;
+      dp[0][mt][e] = p * (dp[0][mt][e] - dl[e]);
+    }
+  }
+  bf16x8_t pp[1][MT / 2], pd[1][MT / 2];
+  pack_bf16<MT, 1>(sc, pp);
+  pack_bf16<MT, 1>(dp, pd);
+  mm_tr<D, MT, 1>(d_lds, pp, dv, g, c16);
+  mm_tr<D, MT, 1>(q_lds, pd, dk, g, c16);
+}
+
+// Exact keys: one workgroup per global key block j (NWAVES = b/16 waves of
+// 16 keys), over every query block that reads j exactly.
+template <int D, int NWAVES>
+__global__ __launch_bounds__(NWAVES * 64) void dkv_kernel(BwdArgs a) {
+  constexpr int NT = NWAVES * 64;
+  constexpr int BR = NWAVES * 16;   // block size b
+  constexpr int MT = BR / 16;
+  constexpr int STR = 2 * D + 32;
+  constexpr int KK = D / 32;
+  constexpr int DT = D / 16;
+  __shared__ __attribute__((aligned(16))) char q_lds[BR * STR];
+  __shared__ __attribute__((aligned(16))) char d_lds[BR * STR];
+  __shared__ __attribute__((aligned(16))) float l_lds[BR];
+  __shared__ __attribute__((aligned(16))) float dl_lds[BR];
+
+  const IsaShape& s = a.s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  // heads vary fastest, so neighbouring workgroups share the query blocks
+  const int bh = blockIdx.x, j = blockIdx.y;
+  const size_t head = (size_t)bh * s.L;
+  const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
+  int kst, kn;
+  isa_block_range(s, j, kst, kn);
+  const int p = kept_pos(s, ctx_row, j);
+  const int kr = wave * 16 + c16;
+  const bool kval = kr < kn;
+  const int ktok = kst + (kval ? kr : 0);
+  const int pos = ktok - (j < s.N_src ? 0 : s.L_src);
+  const float rs = 1.0f / sqrtf((float)D);
+
+  float4_t dk[1][DT], dv[1][DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dk[0][dt] = dv[0][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (p >= 0) {
+    bf16x8_t kf[1][KK], vf[1][KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      uint4 wk = make_uint4(0, 0, 0, 0), wv = make_uint4(0, 0, 0, 0);
+      if (kval) {
+        wk = *reinterpret_cast<const uint4*>(a.K + (head + ktok) * D + 32 * kk + 8 * g);
+        wv = *reinterpret_cast<const uint4*>(a.V + (head + ktok) * D + 32 * kk + 8 * g);
+      }
+      kf[0][kk] = __builtin_bit_cast(bf16x8_t, wk);
+      vf[0][kk] = __builtin_bit_cast(bf16x8_t, wv);
+    }
+    const float kbias = kval ? 0.0f : -INFINITY;
+    const float cscale = kLog2e / sqrtf((float)D);
+    const int32_t* srow = a.sharp_idx + (size_t)bh * s.n_sharp;
+    const int32_t* off = a.inv_off + (size_t)bh * (s.N_kv + 1);
+    const int32_t* lst = a.inv_list + (size_t)bh * s.n_flat * s.k_ns;
+    const int f0 = s.n_flat > 0 ? off[p] : 0;
+    const int nf = s.n_flat > 0 ? off[p + 1] - f0 : 0;
+    const int total = s.n_sharp + nf;
+    for (int qi = 0; qi < total; ++qi) {
+      const int jq = qi < s.n_sharp ? srow[qi] : lst[f0 + qi - s.n_sharp];
+      load_query_block<D, NT, BR>(a, head, jq, q_lds, d_lds, l_lds, dl_lds, tid);
+      kv_block<D, MT>(q_lds, d_lds, l_lds, dl_lds, kf, vf, kbias, cscale, dk, dv, g, c16);
+    }
+  }
+  if (!kval) return;
+  // pooled-key gradients reach every token of the block through the mean
+  const float* gk = (p >= 0 && a.dkc) ? a.dkc + ((size_t)bh * s.N + j) * D : nullptr;
+  const float* gv = (p >= 0 && a.dvc) ? a.dvc + ((size_t)bh * s.N + j) * D : nullptr;
+  const float inv_n = 1.0f / (float)kn;
+  uint16_t* krow = a.dK + (head + ktok) * D;
+  uint16_t* vrow = a.dV + (head + ktok) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int d0 = 16 * dt + 4 * g;
+    float4_t xk = dk[0][dt] * rs, xv = dv[0][dt];
+    if (gk) xk += *reinterpret_cast<const float4_t*>(gk + d0) * inv_n;
+    if (gv) xv += *reinterpret_cast<const float4_t*>(gv + d0) * inv_n;
+    store4(krow, d0, xk, a.rope, D / 2, pos);
+    store4(vrow, d0, xv, nullptr, 0, 0);
+  }
+}
+
+// Pooled keys: one workgroup per 64 positions of J (4 waves of 16), over
+// every flat block; writes dKc (scaled) and dVc in fp32 by global block id.
+template <int D, int MT>
+__global__ __launch_bounds__(256) void dkv_pooled_kernel(BwdArgs a) {
+  constexpr int NT = 256;
+  constexpr int BR = MT * 16;
+  constexpr int STR = 2 * D + 32;
+  constexpr int KK = D / 32;
+  constexpr int DT = D / 16;
+  __shared__ __attribute__((aligned(16))) char q_lds[BR * STR];
+  __shared__ __attribute__((aligned(16))) char d_lds[BR * STR];
+  __shared__ __attribute__((aligned(16))) float l_lds[BR];
+  __shared__ __attribute__((aligned(16))) float dl_lds[BR];
+
+  const IsaShape& s = a.s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.x, p0 = blockIdx.y * kKeyTile;
+  const size_t head = (size_t)bh * s.L;
+  const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
+  const int kp = p0 + wave * 16 + c16;
+  const int jg = kp < s.N_kv ? kept_id(s, ctx_row, kp) : -1;
+  int kst = 0, kn = 0;
+  if (jg >= 0) isa_block_range(s, jg, kst, kn);
+  const bool kval = jg >= 0 && kn > 0;
+  bf16x8_t kf[1][KK], vf[1][KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    uint4 wk = make_uint4(0, 0, 0, 0), wv = make_uint4(0, 0, 0, 0);
+    if (kval) {
+      wk = *reinterpret_cast<const uint4*>(a.kcb + ((size_t)bh * s.N + jg) * D + 32 * kk + 8 * g);
+      wv = *reinterpret_cast<const uint4*>(a.vcb + ((size_t)bh * s.N + jg) * D + 32 * kk + 8 * g);
+    }
+    kf[0][kk] = __builtin_bit_cast(bf16x8_t, wk);
+    vf[0][kk] = __builtin_bit_cast(bf16x8_t, wv);
+  }
+  const float kb0 = kval ? __log2f((float)kn) : -INFINITY;
+  const float cscale = kLog2e / sqrtf((float)D);
+  const int32_t* frow = a.flat_idx + (size_t)bh * s.n_flat;
+  const uint64_t* bits = a.ebits + (size_t)bh * s.n_flat * a.W + (p0 >> 6);
+  float4_t dk[1][DT], dv[1][DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dk[0][dt] = dv[0][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < s.n_flat; ++r) {
+    const uint64_t w = bits[(size_t)r * a.W];
+    const float kbias = ((w >> (kp - p0)) & 1ull) ? -INFINITY : kb0;
+    load_query_block<D, NT, BR>(a, head, frow[r], q_lds, d_lds, l_lds, dl_lds, tid);
+    kv_block<D, MT>(q_lds, d_lds, l_lds, dl_lds, kf, vf, kbias, cscale, dk, dv, g, c16);
+  }
+  if (!kval) return;
+  const float rs = 1.0f / sqrtf((float)D);
+  float* ok = a.dkc_out + ((size_t)bh * s.N + jg) * D;
+  float* ov = a.dvc_out + ((size_t)bh * s.N + jg) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int d0 = 16 * dt + 4 * g;
+    *reinterpret_cast<float4_t*>(ok + d0) = dk[0][dt] * rs;
+    *reinterpret_cast<float4_t*>(ov + d0) = dv[0][dt];
+  }
+}
+
+template <typename F>
+hipError_t set_dyn_lds(F* kernel, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int D>
+hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream_t st) {
+  const int BH = s.B * s.H;
+  hipError_t e = hipSuccess;
+  if (s.n_flat > 0) {
+    bwd_prep_kernel<<<BH, kPrepThreads, 0, st>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const size_t rows = (size_t)BH * s.L;
+    const size_t threads = rows * (D / 8);
+    delta_kernel<D><<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(a.dO, O, const_cast<float*>(a.delta), rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const bool pooled = s.n_flat > 0 && s.k_ns < s.N_kv;
+  if (pooled) {
+    dim3 grid(BH, (s.N_kv + kKeyTile - 1) / kKeyTile);
+    if (s.b == 64) dkv_pooled_kernel<D, 4><<<grid, 256, 0, st>>>(a);
+    else dkv_pooled_kernel<D, 2><<<grid, 256, 0, st>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    BwdArgs k = a;
+    if (!pooled) k.dkc = k.dvc = nullptr;
+    dim3 grid(BH, s.N);
+    if (s.b == 64) dkv_kernel<D, 4><<<grid, 256, 0, st>>>(k);
+    else dkv_kernel<D, 2><<<grid, 128, 0, st>>>(k);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int max_dyn = 2 * ISA_MAX_NKV * (int)sizeof(int);
+  if (s.n_sharp > 0) {
+    BwdArgs q = a;
+    q.qlist = a.sharp_idx;
+    q.n_q = s.n_sharp;
+    q.ntiles_exact = q.ntiles = (s.N_kv * s.b + kKeyTile - 1) / kKeyTile;
+    dim3 grid(s.n_sharp, BH);
+    const size_t dyn = (size_t)s.N_kv * sizeof(int);
+    if (s.b == 64) {
+      static hipError_t attr = set_dyn_lds(&dq_kernel<D, kSharp, 4>, max_dyn);
+      if (attr != hipSuccess) return attr;
+      dq_kernel<D, kSharp, 4><<<grid, 256, dyn, st>>>(q);
+    } else {
+      static hipError_t attr = set_dyn_lds(&dq_kernel<D, kSharp, 2>, max_dyn);
+      if (attr != hipSuccess) return attr;
+      dq_kernel<D, kSharp, 2><<<grid, 128, dyn, st>>>(q);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (s.n_flat > 0) {
+    BwdArgs q = a;
+    q.qlist = a.flat_idx;
+    q.n_q = s.n_flat;
+    q.ntiles_exact = (s.k_ns * s.b + kKeyTile - 1) / kKeyTile;
+    q.ntiles = q.ntiles_exact + (s.k_ns < s.N_kv ? (s.N_kv + kKeyTile - 1) / kKeyTile : 0);
+    dim3 grid(s.n_flat, BH);
+    const size_t dyn = (size_t)(s.k_ns + s.N_kv) * sizeof(int);
+    if (s.b == 64) {
+      static hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 4>, max_dyn);
+      if (attr != hipSuccess) return attr;
+      dq_kernel<D, kFlat, 4><<<grid, 256, dyn, st>>>(q);
+    } else {
+      static hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 2>, max_dyn);
+      if (attr != hipSuccess) return attr;
+      dq_kernel<D, kFlat, 2><<<grid, 128, dyn, st>>>(q);
+    }
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+hipError_t isa_launch_backward(const IsaShape& s, const IsaBwdBuffers& w, hipStream_t st) {
+  BwdArgs a{};
+  a.s = s;
+  a.Q = w.Q;
+  a.K = w.K;
+  a.V = w.V;
+  a.dO = w.dO;
+  a.lse = w.lse;
+  a.delta = w.delta;
+  a.kcb = w.kcb;
+  a.vcb = w.vcb;
+  a.ctx_idx = w.ctx_idx;
+  a.sharp_idx = w.sharp_idx;
+  a.flat_idx = w.flat_idx;
+  a.exact = w.exact;
+  a.ebits = w.ebits;
+  a.inv_off = w.inv_off;
+  a.inv_list = w.inv_list;
+  a.dkc = a.dkc_out = w.dkc;
+  a.dvc = a.dvc_out = w.dvc;
+  a.rope = w.rope;
+  a.dQ = w.dQ;
+  a.dK = w.dK;
+  a.dV = w.dV;
+  a.W = (s.N_kv + 63) / 64;
+  return s.D == 128 ? launch_all<128>(s, a, w.O, st) : launch_all<64>(s, a, w.O, st);
+}

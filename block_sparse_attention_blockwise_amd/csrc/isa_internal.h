@@ -57,14 +57,44 @@ hipError_t isa_launch_flat_topk(const IsaShape& s, const double* srows, const in
 hipError_t isa_launch_coarse_residual(const IsaShape& s, const double* srows,
                                       const uint16_t* vc_bf16, const int32_t* ctx_idx,
                                       uint16_t* O, hipStream_t st);
+// `lse` (nullable, [B,H,L] fp32): log2-domain log-sum-exp of every written
+// row, saved for the backward pass.
 hipError_t isa_launch_sharp_attn(const IsaShape& s, const uint16_t* Q, const uint16_t* K,
                                  const uint16_t* V, const int32_t* ctx_idx,
-                                 const int32_t* sharp_idx, uint16_t* O, hipStream_t st);
+                                 const int32_t* sharp_idx, uint16_t* O, float* lse,
+                                 hipStream_t st);
 hipError_t isa_launch_flat_attn(const IsaShape& s, const uint16_t* Q, const uint16_t* K,
                                 const uint16_t* V, const uint16_t* kc_bf16,
                                 const uint16_t* vc_bf16, const int32_t* ctx_idx,
                                 const int32_t* flat_idx, const int32_t* flat_exact_idx,
-                                uint16_t* O, hipStream_t st);
+                                uint16_t* O, float* lse, hipStream_t st);
+// Buffers of the backward pass (device pointers; the forward's saved state
+// and the backward's scratch live in the forward workspace).
+struct IsaBwdBuffers {
+  const uint16_t* Q;          // attention inputs (the rotated Q, K when RoPE is on)
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* O;
+  const uint16_t* dO;
+  const float* lse;
+  float* delta;
+  const uint16_t* kcb;
+  const uint16_t* vcb;
+  const int32_t* ctx_idx;
+  const int32_t* sharp_idx;
+  const int32_t* flat_idx;
+  const int32_t* exact;
+  uint64_t* ebits;
+  int32_t* inv_off;
+  int32_t* inv_list;
+  float* dkc;
+  float* dvc;
+  const float2* rope;         // nullable
+  uint16_t* dQ;
+  uint16_t* dK;
+  uint16_t* dV;
+};
+hipError_t isa_launch_backward(const IsaShape& s, const IsaBwdBuffers& w, hipStream_t st);
 hipError_t isa_launch_dense_attn(int B, int H, int L, int D, const uint16_t* Q,
                                  const uint16_t* K, const uint16_t* V, uint16_t* O,
                                  hipStream_t st);

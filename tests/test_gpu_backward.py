@@ -1,0 +1,172 @@
+"""GPU parity of the ISA backward pass (isa_backward through the C ABI)
+against the oracle's fp64 gradients with the selections held fixed.
+
+Tolerance, from the arithmetic: the kernels round the probabilities and the
+score gradients dS to bf16 before the matrix-core products (relative error
+2^-9 each), accumulate in fp32, and round the gradients to bf16 (2^-9); the
+forward's Taylor operands Kc, Vc are bf16 while the oracle's are fp64. Each
+gradient element is a sum of many such terms with cancellation (the rows of
+dS sum to zero), so the bound is taken relative to the tensor's RMS: the
+rounding errors add like a random walk, ||gpu - oracle|| <= 0.02 * ||oracle||
+(about ten times the per-term 2^-9), and the largest single deviation, a
+several-sigma tail over ~10^5 elements, max |gpu - oracle| <= 0.3 * rms(oracle)."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import isa_inputs
+from oracle import isa_oracle
+from parity_util import bf16_tensor
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+isa = pytest.importorskip("block_sparse_attention_blockwise_amd")
+
+MAX_RMS = 0.3
+REL_L2 = 0.02
+
+
+def log(msg):
+    print(f"[gpu-bwd {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    isa.lib()
+    return torch.device("cuda:0")
+
+
+def _dO(p, seed):
+    """Seeded output gradient ~N(0, 1), rounded to bf16 (bits, values)."""
+    rng = np.random.default_rng([99, seed])
+    x = rng.standard_normal((p.B, p.H, p.L_src + p.L_ctx, p.D)).astype(np.float32)
+    return isa_inputs.round_to_bf16(x)
+
+
+def _run(p, inp, dO_bits, dev):
+    Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
+    dO = bf16_tensor(dO_bits, dev)
+    ws = isa.workspace(p, dev)
+    O, dbg = isa.forward(Q, K, V, p, debug=True, workspace=ws)
+    dQ, dK, dV = isa.backward(Q, K, V, O, dO, p, ws)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy()
+    return dict(dQ=f(dQ), dK=f(dK), dV=f(dV), O=f(O),
+                sel={k: v.cpu().numpy() for k, v in dbg.items()})
+
+
+def _compare(name, got, ref):
+    err = np.abs(got - ref)
+    rms = float(np.sqrt((ref ** 2).mean()))
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    assert np.isfinite(got).all(), f"{name}: non-finite"
+    log(f"  {name}: max-abs {err.max():.3e} (rms {rms:.3e}, ratio {err.max() / max(rms, 1e-30):.3f}) rel-L2 {rel:.2e}")
+    assert err.max() <= MAX_RMS * rms and rel <= REL_L2, (name, float(err.max()), rms, rel)
+    return rel
+
+
+def _oracle_grads(plan, inp, dO_vals, bi, h, sel, gamma=0.0, rope_base=0.0):
+    Qv, Kv, Vv = (inp[n][1][bi, h] for n in "QKV")
+    if rope_base:
+        Qv = isa_oracle.rope(Qv, plan.L_src, plan.L_ctx, rope_base)
+        Kv = isa_oracle.rope(Kv, plan.L_src, plan.L_ctx, rope_base)
+    selections = dict(ctx_idx=np.asarray(sel["ctx_idx"][bi, h], dtype=np.int64) - plan.N_src,
+                      sharp_idx=sel["sharp_idx"][bi, h], flat_idx=sel["flat_idx"][bi, h],
+                      flat_exact_idx=sel["flat_exact_idx"][bi, h])
+    ref_sel = isa_oracle.isa_head(Qv, Kv, Vv, plan, compute_output=False)
+    assert np.array_equal(ref_sel.ctx_idx, selections["ctx_idx"])
+    assert np.array_equal(ref_sel.sharp_idx, selections["sharp_idx"])
+    assert np.array_equal(ref_sel.flat_exact_idx, selections["flat_exact_idx"].reshape(ref_sel.flat_exact_idx.shape))
+    gq, gk, gv = isa_oracle.isa_head_backward(Qv, Kv, Vv, dO_vals[bi, h], plan, selections=selections,
+                                              gamma=gamma)
+    if rope_base:
+        gq = isa_oracle.rope_backward(gq, plan.L_src, plan.L_ctx, rope_base)
+        gk = isa_oracle.rope_backward(gk, plan.L_src, plan.L_ctx, rope_base)
+    return gq, gk, gv
+
+
+def _check_all_rows(p, cfg_id=1, seed=0, heads=None):
+    inp = isa_inputs.make_inputs(cfg_id, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    dO_bits, dO_vals = _dO(p, seed)
+    res = _run(p, inp, dO_bits, torch.device("cuda:0"))
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    for (bi, h) in (heads or [(x, y) for x in range(p.B) for y in range(p.H)]):
+        log(f"head ({bi},{h})")
+        gq, gk, gv = _oracle_grads(plan, inp, dO_vals, bi, h, res["sel"], rope_base=p.rope_base)
+        _compare("dQ", res["dQ"][bi, h], gq)
+        _compare("dK", res["dK"][bi, h], gk)
+        _compare("dV", res["dV"][bi, h], gv)
+    return res, plan
+
+
+@pytest.mark.parametrize("D,b", [(128, 64), (64, 32), (128, 32), (64, 64)])
+def test_backward_small_all_rows(dev, D, b):
+    """Ragged segments (700 + 451 tokens), sharp and flat blocks, pruned
+    context blocks; every gradient element against the oracle."""
+    p = isa.Params(1, 2, 700, 451, D, b, 0.25, 0.5, 0.125)
+    _check_all_rows(p)
+
+
+def test_backward_batch_and_heads(dev):
+    p = isa.Params(2, 3, 333, 290, 128, 64, 0.5, 0.5, 0.25)
+    _check_all_rows(p, heads=[(0, 0), (1, 2)])
+
+
+@pytest.mark.parametrize("a_s,a_f,a_ns,L_ctx", [
+    (1.0, 0.0, 0.25, 451),    # dense special case: every block sharp over every token
+    (1.0, 1.0, 0.0, 451),     # pure Taylor: every block flat over pooled keys only
+    (0.25, 1.0, 1.0, 451),    # alpha_ns = 1: flat blocks exact over J, no pooled keys
+    (0.125, 0.5, 0.125, 0),   # no context segment
+])
+def test_backward_special_cases(dev, a_s, a_f, a_ns, L_ctx):
+    p = isa.Params(1, 2, 700, L_ctx, 128, 64, a_s, a_f, a_ns)
+    _check_all_rows(p)
+
+
+def test_backward_closed_form_sums_and_determinism(dev):
+    """Per head, the dV rows add up to the dO rows' sum and the dK rows to
+    zero (within the rounding of the bf16 gradients); two calls give the same
+    bits."""
+    p = isa.Params(1, 4, 1500, 1300, 128, 64, 0.25, 0.5, 0.125)
+    inp = isa_inputs.make_inputs(1, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    dO_bits, dO_vals = _dO(p, 3)
+    r1 = _run(p, inp, dO_bits, dev)
+    r2 = _run(p, inp, dO_bits, dev)
+    for k in ("dQ", "dK", "dV"):
+        assert np.array_equal(r1[k], r2[k]), k
+    for h in range(p.H):
+        sv, so = r1["dV"][0, h].sum(0), dO_vals[0, h].sum(0)
+        sk = r1["dK"][0, h].sum(0)
+        scale_v = np.abs(r1["dV"][0, h]).sum(0)
+        scale_k = np.abs(r1["dK"][0, h]).sum(0)
+        log(f"head {h}: |sum dV - sum dO| max {np.abs(sv - so).max():.3e}; |sum dK| max {np.abs(sk).max():.3e}")
+        assert (np.abs(sv - so) <= 0.02 * scale_v + 1e-3).all()
+        assert (np.abs(sk) <= 0.02 * scale_k + 1e-3).all()
+
+
+def test_backward_with_rope(dev):
+    """RoPE on: the gradients of the unrotated Q, K (oracle: the backward on
+    the rotated tensors, then the transposed rotation)."""
+    p = isa.Params(1, 2, 700, 451, 128, 64, 0.25, 0.5, 0.125, rope_base=10000.0)
+    _check_all_rows(p)
+
+
+def test_backward_16k_workload(dev):
+    """16K-token workload (H = 40, D = 128, b = 64, default ratios): two heads
+    against the oracle element by element, every head through the sums."""
+    c = isa_inputs.CONFIGS[2]
+    p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"])
+    log("16k backward")
+    res, _ = _check_all_rows(p, cfg_id=2, heads=[(0, 0), (0, 39)])
+    _, dO_vals = _dO(p, 0)
+    for h in range(p.H):
+        sv, so, sk = res["dV"][0, h].sum(0), dO_vals[0, h].sum(0), res["dK"][0, h].sum(0)
+        assert (np.abs(sv - so) <= 0.02 * np.abs(res["dV"][0, h]).sum(0) + 1e-3).all(), h
+        assert (np.abs(sk) <= 0.02 * np.abs(res["dK"][0, h]).sum(0) + 1e-3).all(), h

@@ -132,6 +132,13 @@ def test_calls_fail_before_launch(isa):
                                   fake, fake, 1 << 40, None) == -1
     assert L.isa_rope_pool_coarse(ctypes.byref(rp), fake, fake, fake, fake, fake, fake, fake, fake,
                                   fake, fake, 16, None) == -3
+    assert L.isa_backward(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, fake,
+                          1 << 40, None) == -1
+    assert L.isa_backward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                          16, None) == -3
+    g = _params(isa, gamma=0.5)
+    assert L.isa_backward(ctypes.byref(g), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                          1 << 40, None) == -2
     assert L.isa_dense_attn(1, 1, 0, 128, fake, fake, fake, fake, None) == -1
     assert L.isa_dense_attn(1, 1, 16, 96, fake, fake, fake, fake, None) == -2
     assert L.isa_dense_attn(1, 1, 16, 128, None, fake, fake, fake, None) == -1
