@@ -55,6 +55,8 @@ def parse():
                     help="launch only this kernel --steps times (for counter collection)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time isa_forward + isa_backward (and the dense configuration on the same kernels)")
     ap.add_argument("--fig6", action="store_true",
                     help="pure 0th-order Taylor variant (alpha_f=1, alpha_ns=0) vs exact "
                          "attention over J: latencies and the error/sharpness rank correlation")
@@ -215,6 +217,49 @@ def fig6(isa, torch, p, Q, K, V, args):
     del starts
 
 
+def backward_bench(isa, torch, p, Q, K, V, args):
+    """Training step of the operator (isa_forward + isa_backward) at the
+    benchmark workload, and the same kernels in the dense configuration
+    (alpha_s = 1, alpha_f = 0: every block exact over every token), which is
+    the dense attention forward + backward on this engine."""
+    import dataclasses
+    pd = dataclasses.replace(p, alpha_s=1.0, alpha_f=0.0)
+    g = torch.Generator(device=Q.device).manual_seed(5)
+    dO = torch.randn(Q.shape, device=Q.device, generator=g).to(torch.bfloat16)
+    res = {}
+    runs = [("isa", p)] + ([] if args.no_dense else [("dense_same_engine", pd)])
+    for name, q in runs:
+        ws = isa.workspace(q, Q.device)
+        O = isa.forward(Q, K, V, q, workspace=ws)
+        grads = isa.backward(Q, K, V, O, dO, q, ws)
+        torch.cuda.synchronize()
+        reps = max(args.steps // 4, 2) if name == "isa" else max(args.dense_reps, 1)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        fwd = bwd = 0.0
+        for _ in range(reps):
+            ev[0].record()
+            isa.forward(Q, K, V, q, out=O, workspace=ws)
+            ev[1].record()
+            isa.backward(Q, K, V, O, dO, q, ws, out=grads)
+            ev[2].record()
+            torch.cuda.synchronize()
+            fwd += ev[0].elapsed_time(ev[1])
+            bwd += ev[1].elapsed_time(ev[2])
+        res[name] = {"forward_ms": fwd / reps, "backward_ms": bwd / reps,
+                     "step_ms": (fwd + bwd) / reps}
+        del ws, grads
+    if not args.no_dense:
+        L = p.L_src + p.L_ctx
+        dense_bwd_flop = 10 * p.D * L * L * p.B * p.H   # 5 products of 2*D per query-key pair
+        res["dense_same_engine"]["backward_tflops_algorithmic"] = (
+            dense_bwd_flop / (res["dense_same_engine"]["backward_ms"] * 1e-3) / 1e12)
+        res["speedup_vs_dense_same_engine"] = {
+            "backward": res["dense_same_engine"]["backward_ms"] / res["isa"]["backward_ms"],
+            "forward_plus_backward": res["dense_same_engine"]["step_ms"] / res["isa"]["step_ms"]}
+    print(json.dumps({"backward": res, "config": {"workload": "isa_fwd_64k_tokens_h40_d128"}}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -246,6 +291,9 @@ def main():
     Q, K, V = T["Q"], T["K"], T["V"]
     if args.fig6:
         fig6(isa, torch, p, Q, K, V, args)
+        return
+    if args.backward:
+        backward_bench(isa, torch, p, Q, K, V, args)
         return
     O = torch.empty_like(Q)
     BH = p.B * p.H
