@@ -286,6 +286,21 @@ __device__ __forceinline__ void exp_pack(const float4_t (&s)[QT][4], float xs, c
   }
 }
 
+// log2-domain log-sum-exp of each owned row (m is the running reference of
+// the logits in log2 units, lsum the row's partial sums), kept for the
+// backward pass.
+template <int QT>
+__device__ __forceinline__ void save_lse(float* lse, size_t head, const int (&qtok)[QT],
+                                         const bool (&qval)[QT], const float (&m)[QT],
+                                         const float (&lsum)[QT], int g) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float lt = xor16_sum(lsum[qt]);
+    lt = xor32_sum(lt);
+    if (qval[qt] && g == 0) lse[head + qtok[qt]] = m[qt] + __log2f(lt);
+  }
+}
+
 // O^T += V^T P^T for the 64 keys of the LDS tile at `vb`.
 template <int D, int QT>
 __device__ __forceinline__ void pv_tile(const char* vb, const bf16x8_t (&pb)[QT][2],
@@ -540,6 +555,9 @@ void attn_kernel(AttnArgs a) {
       row_max<QT>(sc, hb ? 1.0f : cscale, mx);
       rescale<D, QT>(mx, m, lsum, oacc);
       exp_pack<QT>(sc, hb ? 1.0f : cscale, m, lsum, pb);
+      // the row statistics are final after the last tile's probabilities:
+      // saving them here keeps m from living through the last PV product
+      if (t == ntiles - 1 && a.lse != nullptr) save_lse<QT>(a.lse, head, qtok, qval, m, lsum, g);
       pv_tile<D, QT>(v_lds[0], pb, oacc, g, c16);
     }
   } else {
@@ -632,9 +650,6 @@ void attn_kernel(AttnArgs a) {
     float lt = xor16_sum(lsum[qt]);
     lt = xor32_sum(lt);
     if (!qval[qt]) continue;
-    // log2-domain log-sum-exp of the row (m is the running reference of the
-    // logits in log2 units), kept for the backward pass
-    if (a.lse != nullptr && g == 0) a.lse[head + qtok[qt]] = m[qt] + __log2f(lt);
     const float inv = 1.0f / lt;
     uint16_t* orow = a.O + (head + qtok[qt]) * D;
 #pragma unroll
@@ -645,6 +660,7 @@ void attn_kernel(AttnArgs a) {
       *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = w;
     }
   }
+  if (LOOP != 0 && a.lse != nullptr) save_lse<QT>(a.lse, head, qtok, qval, m, lsum, g);
 }
 
 template <int D, int MODE, int QT, int NWAVES, int LOOP>

@@ -19,11 +19,12 @@
 //   * dq_kernel (query-major, as the forward): per query block, over the key
 //     tiles the forward used; S^T = K Q^T and dP^T = V dO^T on the matrix
 //     cores, P recomputed from the saved log-sum-exp, dQ^T += K^T dS^T;
-//   * dkv_kernel (key-major): per kept block j, its keys held in registers,
-//     over every query block that reads j exactly (all sharp blocks and the
-//     flat blocks listing j in E_i); S = Q K^T, dP = dO V^T, dV^T += dO^T P,
-//     dK^T += Q^T dS; the pooled gradients dKc_j / n_j, dVc_j / n_j are added
-//     before the rows are written; blocks outside J get zero gradients;
+//   * dkv_kernel (key-major): per 64*NF keys of J (whole kept blocks), the
+//     keys held in registers, over every query block that reads them exactly
+//     (all sharp blocks, then each kept block's flat blocks with the other
+//     keys masked); S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS;
+//     the pooled gradients dKc_j / n_j, dVc_j / n_j are added before the rows
+//     are written; zero_pruned_kernel zeroes the rows of pruned blocks;
 //   * dkv_pooled_kernel (key-major over the pooled keys): per 64 positions of
 //     J, over every flat block; writes dKc, dVc (fp32).
 // With decoupled RoPE the gradients of the rotated Q and K are turned back by
@@ -470,154 +471,240 @@ __global__ __launch_bounds__(NWAVES * 64) void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-// Loads the b token rows of query block jq (Q and dO) into LDS, zero rows
-// past its n valid tokens, and the rows' log-sum-exp and Delta (+inf and 0
-// for the padding, so those rows get zero probability).
+// The key-major kernels stream query blocks (b token rows of Q and dO, with
+// the rows' log-sum-exp and Delta) through two LDS buffers: the next block is
+// fetched into registers while the current one is used. Rows past a block's
+// n valid tokens are zero with log-sum-exp +inf, so they get probability 0.
 template <int D, int NT, int BR>
-__device__ __forceinline__ void load_query_block(const BwdArgs& a, size_t head, int jq, char* q_lds,
-                                                 char* d_lds, float* l_lds, float* dl_lds, int tid) {
-  constexpr int STR = 2 * D + 32;
-  constexpr int CPR = D / 8;
-  constexpr int CHQ = BR * CPR / NT;
+struct QueryStage {
+  static constexpr int STR = 2 * D + 32;
+  static constexpr int CPR = D / 8;
+  static constexpr int CHQ = BR * CPR / NT;
   static_assert(CHQ >= 1 && (BR * CPR) % NT == 0, "query tile split");
-  int st, n;
-  isa_block_range(a.s, jq, st, n);
-  uint4 qr[CHQ], dr[CHQ];
+  uint4 q[CHQ], d[CHQ];
+  float lv, dv;
+
+  __device__ __forceinline__ void fetch(const BwdArgs& a, size_t head, int jq, int tid) {
+    int st, n;
+    isa_block_range(a.s, jq, st, n);
 #pragma unroll
-  for (int i = 0; i < CHQ; ++i) {
-    const int ch = tid + i * NT, r = ch / CPR, c = ch % CPR;
-    qr[i] = make_uint4(0, 0, 0, 0);
-    dr[i] = make_uint4(0, 0, 0, 0);
-    if (r < n) {
-      qr[i] = *reinterpret_cast<const uint4*>(a.Q + (head + st + r) * D + c * 8);
-      dr[i] = *reinterpret_cast<const uint4*>(a.dO + (head + st + r) * D + c * 8);
+    for (int i = 0; i < CHQ; ++i) {
+      const int ch = tid + i * NT, r = ch / CPR, c = ch % CPR;
+      q[i] = make_uint4(0, 0, 0, 0);
+      d[i] = make_uint4(0, 0, 0, 0);
+      if (r < n) {
+        q[i] = *reinterpret_cast<const uint4*>(a.Q + (head + st + r) * D + c * 8);
+        d[i] = *reinterpret_cast<const uint4*>(a.dO + (head + st + r) * D + c * 8);
+      }
+    }
+    lv = INFINITY;
+    dv = 0.0f;
+    if (tid < BR && tid < n) {
+      lv = a.lse[head + st + tid];
+      dv = a.delta[head + st + tid];
     }
   }
-  float lv = INFINITY, dv = 0.0f;
-  if (tid < BR && tid < n) {
-    lv = a.lse[head + st + tid];
-    dv = a.delta[head + st + tid];
-  }
-  __syncthreads();   // previous block fully consumed
-#pragma unroll
-  for (int i = 0; i < CHQ; ++i) {
-    const int ch = tid + i * NT, r = ch / CPR, c = ch % CPR;
-    *reinterpret_cast<uint4*>(q_lds + r * STR + c * 16) = qr[i];
-    *reinterpret_cast<uint4*>(d_lds + r * STR + c * 16) = dr[i];
-  }
-  if (tid < BR) {
-    l_lds[tid] = lv;
-    dl_lds[tid] = dv;
-  }
-  __syncthreads();
-}
 
-// One query block against this wave's 16 keys (kf, vf in registers, per-lane
-// additive logit kbias in log2 units): accumulates dK^T (raw, before the
-// 1/sqrt(D) scale) and dV^T.
-template <int D, int MT>
+  __device__ __forceinline__ void put(char* q_lds, char* d_lds, float* l_lds, float* dl_lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CHQ; ++i) {
+      const int ch = tid + i * NT, r = ch / CPR, c = ch % CPR;
+      *reinterpret_cast<uint4*>(q_lds + r * STR + c * 16) = q[i];
+      *reinterpret_cast<uint4*>(d_lds + r * STR + c * 16) = d[i];
+    }
+    if (tid < BR) {
+      l_lds[tid] = lv;
+      dl_lds[tid] = dv;
+    }
+  }
+};
+
+// One query block against this wave's 16*NF keys (kf, vf in registers,
+// per-fragment additive logit kbias in log2 units): accumulates dK^T (raw,
+// before the 1/sqrt(D) scale) and dV^T.
+template <int D, int MT, int NF>
 __device__ __forceinline__ void kv_block(const char* q_lds, const char* d_lds, const float* l_lds,
-                                         const float* dl_lds, const bf16x8_t (&kf)[1][D / 32],
-                                         const bf16x8_t (&vf)[1][D / 32], float kbias, float cscale,
-                                         float4_t (&dk)[1][D / 16], float4_t (&dv)[1][D / 16],
-                                         int g, int c16) {
-  float4_t sc[1][MT], dp[1][MT];
-  mm_rows<D, MT, 1>(q_lds, kf, sc, g, c16);
-  mm_rows<D, MT, 1>(d_lds, vf, dp, g, c16);
+                                         const float* dl_lds, const bf16x8_t (&kf)[NF][D / 32],
+                                         const bf16x8_t (&vf)[NF][D / 32], const float (&kbias)[NF],
+                                         float cscale, float4_t (&dk)[NF][D / 16],
+                                         float4_t (&dv)[NF][D / 16], int g, int c16) {
+  float4_t sc[NF][MT], dp[NF][MT];
+  mm_rows<D, MT, NF>(q_lds, kf, sc, g, c16);
+  mm_rows<D, MT, NF>(d_lds, vf, dp, g, c16);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const float4_t lv = *reinterpret_cast<const float4_t*>(l_lds + 16 * mt + 4 * g);
     const float4_t dl = *reinterpret_cast<const float4_t*>(dl_lds + 16 * mt + 4 * g);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][mt][e], cscale, kbias) - lv[e]);
-      sc[0][mt][e] = p;
-      dp[0][mt][e] = p * (dp[0][mt][e] - dl[e]);
+    for (int nf = 0; nf < NF; ++nf) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nf][mt][e], cscale, kbias[nf]) - lv[e]);
+        sc[nf][mt][e] = p;
+        dp[nf][mt][e] = p * (dp[nf][mt][e] - dl[e]);
+      }
     }
   }
-  bf16x8_t pp[1][MT / 2], pd[1][MT / 2];
-  pack_bf16<MT, 1>(sc, pp);
-  pack_bf16<MT, 1>(dp, pd);
-  mm_tr<D, MT, 1>(d_lds, pp, dv, g, c16);
-  mm_tr<D, MT, 1>(q_lds, pd, dk, g, c16);
+  bf16x8_t pp[NF][MT / 2], pd[NF][MT / 2];
+  pack_bf16<MT, NF>(sc, pp);
+  pack_bf16<MT, NF>(dp, pd);
+  mm_tr<D, MT, NF>(d_lds, pp, dv, g, c16);
+  mm_tr<D, MT, NF>(q_lds, pd, dk, g, c16);
 }
 
-// Exact keys: one workgroup per global key block j (NWAVES = b/16 waves of
-// 16 keys), over every query block that reads j exactly.
-template <int D, int NWAVES>
-__global__ __launch_bounds__(NWAVES * 64) void dkv_kernel(BwdArgs a) {
-  constexpr int NT = NWAVES * 64;
-  constexpr int BR = NWAVES * 16;   // block size b
+#ifndef ISA_DKV_NF
+#define ISA_DKV_NF 1
+#endif
+
+// Exact keys, key-major: one workgroup per KPB consecutive positions of J
+// (4 waves of 16*NF keys, KPB = 64*NF/b kept blocks), over the sharp blocks
+// (every kept block is read by all of them) and then, block by block, the
+// flat blocks whose E_i holds that kept block (the workgroup's other keys
+// masked for those).
+template <int D, int NF, int BR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NF == 1 ? 2 : 1)))
+void dkv_kernel(BwdArgs a) {
+  constexpr int NT = 256;
   constexpr int MT = BR / 16;
+  constexpr int KW = 16 * NF;
+  constexpr int KPB = 4 * KW / BR;
   constexpr int STR = 2 * D + 32;
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;
-  __shared__ __attribute__((aligned(16))) char q_lds[BR * STR];
-  __shared__ __attribute__((aligned(16))) char d_lds[BR * STR];
-  __shared__ __attribute__((aligned(16))) float l_lds[BR];
-  __shared__ __attribute__((aligned(16))) float dl_lds[BR];
+  static_assert(KPB >= 1 && KPB * BR == 4 * KW, "whole blocks per workgroup");
+  __shared__ __attribute__((aligned(16))) char q_lds[2][BR * STR];
+  __shared__ __attribute__((aligned(16))) char d_lds[2][BR * STR];
+  __shared__ __attribute__((aligned(16))) float l_lds[2][BR];
+  __shared__ __attribute__((aligned(16))) float dl_lds[2][BR];
 
   const IsaShape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  // heads vary fastest, so neighbouring workgroups share the query blocks
-  const int bh = blockIdx.x, j = blockIdx.y;
+  const int bh = blockIdx.x, pb = blockIdx.y * KPB;   // heads vary fastest
   const size_t head = (size_t)bh * s.L;
   const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
-  int kst, kn;
-  isa_block_range(s, j, kst, kn);
-  const int p = kept_pos(s, ctx_row, j);
-  const int kr = wave * 16 + c16;
-  const bool kval = kr < kn;
-  const int ktok = kst + (kval ? kr : 0);
-  const int pos = ktok - (j < s.N_src ? 0 : s.L_src);
-  const float rs = 1.0f / sqrtf((float)D);
 
-  float4_t dk[1][DT], dv[1][DT];
+  int kb[NF], kj[NF], ktok[NF], kn[NF];
+  bool kval[NF];
+  bf16x8_t kf[NF][KK], vf[NF][KK];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) dk[0][dt] = dv[0][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  if (p >= 0) {
-    bf16x8_t kf[1][KK], vf[1][KK];
+  for (int nf = 0; nf < NF; ++nf) {
+    const int kidx = wave * KW + 16 * nf + c16;
+    kb[nf] = kidx / BR;
+    const int o = kidx % BR;
+    kj[nf] = kept_id(s, ctx_row, pb + kb[nf]);
+    int st = 0, n = 0;
+    if (kj[nf] >= 0) isa_block_range(s, kj[nf], st, n);
+    kn[nf] = n;
+    kval[nf] = o < n;
+    ktok[nf] = st + (kval[nf] ? o : 0);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       uint4 wk = make_uint4(0, 0, 0, 0), wv = make_uint4(0, 0, 0, 0);
-      if (kval) {
-        wk = *reinterpret_cast<const uint4*>(a.K + (head + ktok) * D + 32 * kk + 8 * g);
-        wv = *reinterpret_cast<const uint4*>(a.V + (head + ktok) * D + 32 * kk + 8 * g);
+      if (kval[nf]) {
+        wk = *reinterpret_cast<const uint4*>(a.K + (head + ktok[nf]) * D + 32 * kk + 8 * g);
+        wv = *reinterpret_cast<const uint4*>(a.V + (head + ktok[nf]) * D + 32 * kk + 8 * g);
       }
-      kf[0][kk] = __builtin_bit_cast(bf16x8_t, wk);
-      vf[0][kk] = __builtin_bit_cast(bf16x8_t, wv);
-    }
-    const float kbias = kval ? 0.0f : -INFINITY;
-    const float cscale = kLog2e / sqrtf((float)D);
-    const int32_t* srow = a.sharp_idx + (size_t)bh * s.n_sharp;
-    const int32_t* off = a.inv_off + (size_t)bh * (s.N_kv + 1);
-    const int32_t* lst = a.inv_list + (size_t)bh * s.n_flat * s.k_ns;
-    const int f0 = s.n_flat > 0 ? off[p] : 0;
-    const int nf = s.n_flat > 0 ? off[p + 1] - f0 : 0;
-    const int total = s.n_sharp + nf;
-    for (int qi = 0; qi < total; ++qi) {
-      const int jq = qi < s.n_sharp ? srow[qi] : lst[f0 + qi - s.n_sharp];
-      load_query_block<D, NT, BR>(a, head, jq, q_lds, d_lds, l_lds, dl_lds, tid);
-      kv_block<D, MT>(q_lds, d_lds, l_lds, dl_lds, kf, vf, kbias, cscale, dk, dv, g, c16);
+      kf[nf][kk] = __builtin_bit_cast(bf16x8_t, wk);
+      vf[nf][kk] = __builtin_bit_cast(bf16x8_t, wv);
     }
   }
-  if (!kval) return;
-  // pooled-key gradients reach every token of the block through the mean
-  const float* gk = (p >= 0 && a.dkc) ? a.dkc + ((size_t)bh * s.N + j) * D : nullptr;
-  const float* gv = (p >= 0 && a.dvc) ? a.dvc + ((size_t)bh * s.N + j) * D : nullptr;
-  const float inv_n = 1.0f / (float)kn;
-  uint16_t* krow = a.dK + (head + ktok) * D;
-  uint16_t* vrow = a.dV + (head + ktok) * D;
+
+  // query schedule: the sharp blocks, then each kept block's flat list
+  const int32_t* srow = a.sharp_idx + (size_t)bh * s.n_sharp;
+  const int32_t* off = a.inv_off + (size_t)bh * (s.N_kv + 1);
+  const int32_t* lst = a.inv_list + (size_t)bh * s.n_flat * s.k_ns;
+  int fb[KPB + 1];
+  fb[0] = s.n_sharp;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const int d0 = 16 * dt + 4 * g;
-    float4_t xk = dk[0][dt] * rs, xv = dv[0][dt];
-    if (gk) xk += *reinterpret_cast<const float4_t*>(gk + d0) * inv_n;
-    if (gv) xv += *reinterpret_cast<const float4_t*>(gv + d0) * inv_n;
-    store4(krow, d0, xk, a.rope, D / 2, pos);
-    store4(vrow, d0, xv, nullptr, 0, 0);
+  for (int u = 0; u < KPB; ++u) {
+    const int p = pb + u;
+    const int c = (s.n_flat > 0 && p < s.N_kv) ? off[p + 1] - off[p] : 0;
+    fb[u + 1] = fb[u] + c;
+  }
+  const int total = fb[KPB];
+  auto query_at = [&](int i, int& act) -> int {
+    if (i < s.n_sharp) {
+      act = -1;
+      return srow[i];
+    }
+    int u = 0;
+#pragma unroll
+    for (int v = 0; v < KPB; ++v)
+      if (i >= fb[v + 1]) u = v + 1;
+    act = u;
+    return lst[off[pb + u] + (i - fb[u])];
+  };
+
+  const float cscale = kLog2e / sqrtf((float)D);
+  float4_t dk[NF][DT], dv[NF][DT];
+#pragma unroll
+  for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dk[nf][dt] = dv[nf][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (total > 0) {
+    QueryStage<D, NT, BR> stage;
+    int act_cur;
+    stage.fetch(a, head, query_at(0, act_cur), tid);
+    stage.put(q_lds[0], d_lds[0], l_lds[0], dl_lds[0], tid);
+    __syncthreads();
+    for (int i = 0; i < total; ++i) {
+      const int buf = i & 1;
+      int act_next = -1;
+      const bool more = i + 1 < total;
+      if (more) stage.fetch(a, head, query_at(i + 1, act_next), tid);
+      float kbias[NF];
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf)
+        kbias[nf] = (kval[nf] && (act_cur < 0 || act_cur == kb[nf])) ? 0.0f : -INFINITY;
+      kv_block<D, MT, NF>(q_lds[buf], d_lds[buf], l_lds[buf], dl_lds[buf], kf, vf, kbias, cscale, dk, dv,
+                          g, c16);
+      if (more) stage.put(q_lds[buf ^ 1], d_lds[buf ^ 1], l_lds[buf ^ 1], dl_lds[buf ^ 1], tid);
+      __syncthreads();
+      act_cur = act_next;
+    }
+  }
+
+  const float rs = 1.0f / sqrtf((float)D);
+#pragma unroll
+  for (int nf = 0; nf < NF; ++nf) {
+    if (!kval[nf]) continue;
+    const int j = kj[nf];
+    // pooled-key gradients reach every token of the block through the mean
+    const float* gk = a.dkc ? a.dkc + ((size_t)bh * s.N + j) * D : nullptr;
+    const float* gv = a.dvc ? a.dvc + ((size_t)bh * s.N + j) * D : nullptr;
+    const float inv_n = 1.0f / (float)kn[nf];
+    const int pos = ktok[nf] - (j < s.N_src ? 0 : s.L_src);
+    uint16_t* krow = a.dK + (head + ktok[nf]) * D;
+    uint16_t* vrow = a.dV + (head + ktok[nf]) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d0 = 16 * dt + 4 * g;
+      float4_t xk = dk[nf][dt] * rs, xv = dv[nf][dt];
+      if (gk) xk += *reinterpret_cast<const float4_t*>(gk + d0) * inv_n;
+      if (gv) xv += *reinterpret_cast<const float4_t*>(gv + d0) * inv_n;
+      store4(krow, d0, xk, a.rope, D / 2, pos);
+      store4(vrow, d0, xv, nullptr, 0, 0);
+    }
+  }
+}
+
+// Zero gradients for the tokens of pruned context blocks (not in J).
+template <int D>
+__global__ __launch_bounds__(256) void zero_pruned_kernel(BwdArgs a) {
+  const IsaShape& s = a.s;
+  const int bh = blockIdx.x, j = s.N_src + blockIdx.y;
+  const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
+  if (kept_pos(s, ctx_row, j) >= 0) return;
+  int st, n;
+  isa_block_range(s, j, st, n);
+  constexpr int CPR = D / 8;
+  const size_t head = (size_t)bh * s.L;
+  for (int ch = threadIdx.x; ch < n * CPR; ch += 256) {
+    const size_t off = (head + st + ch / CPR) * D + (ch % CPR) * 8;
+    *reinterpret_cast<uint4*>(a.dK + off) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(a.dV + off) = make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -630,10 +717,10 @@ __global__ __launch_bounds__(256) void dkv_pooled_kernel(BwdArgs a) {
   constexpr int STR = 2 * D + 32;
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;
-  __shared__ __attribute__((aligned(16))) char q_lds[BR * STR];
-  __shared__ __attribute__((aligned(16))) char d_lds[BR * STR];
-  __shared__ __attribute__((aligned(16))) float l_lds[BR];
-  __shared__ __attribute__((aligned(16))) float dl_lds[BR];
+  __shared__ __attribute__((aligned(16))) char q_lds[2][BR * STR];
+  __shared__ __attribute__((aligned(16))) char d_lds[2][BR * STR];
+  __shared__ __attribute__((aligned(16))) float l_lds[2][BR];
+  __shared__ __attribute__((aligned(16))) float dl_lds[2][BR];
 
   const IsaShape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -664,11 +751,20 @@ __global__ __launch_bounds__(256) void dkv_pooled_kernel(BwdArgs a) {
   float4_t dk[1][DT], dv[1][DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dk[0][dt] = dv[0][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  QueryStage<D, NT, BR> stage;
+  stage.fetch(a, head, frow[0], tid);
+  stage.put(q_lds[0], d_lds[0], l_lds[0], dl_lds[0], tid);
+  __syncthreads();
   for (int r = 0; r < s.n_flat; ++r) {
+    const int buf = r & 1;
+    const bool more = r + 1 < s.n_flat;
+    if (more) stage.fetch(a, head, frow[r + 1], tid);
     const uint64_t w = bits[(size_t)r * a.W];
-    const float kbias = ((w >> (kp - p0)) & 1ull) ? -INFINITY : kb0;
-    load_query_block<D, NT, BR>(a, head, frow[r], q_lds, d_lds, l_lds, dl_lds, tid);
-    kv_block<D, MT>(q_lds, d_lds, l_lds, dl_lds, kf, vf, kbias, cscale, dk, dv, g, c16);
+    const float kbias[1] = {((w >> (kp - p0)) & 1ull) ? -INFINITY : kb0};
+    kv_block<D, MT, 1>(q_lds[buf], d_lds[buf], l_lds[buf], dl_lds[buf], kf, vf, kbias, cscale, dk, dv,
+                       g, c16);
+    if (more) stage.put(q_lds[buf ^ 1], d_lds[buf ^ 1], l_lds[buf ^ 1], dl_lds[buf ^ 1], tid);
+    __syncthreads();
   }
   if (!kval) return;
   const float rs = 1.0f / sqrtf((float)D);
@@ -715,11 +811,18 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
   {
     BwdArgs k = a;
     if (!pooled) k.dkc = k.dvc = nullptr;
-    dim3 grid(BH, s.N);
-    if (s.b == 64) dkv_kernel<D, 4><<<grid, 256, 0, st>>>(k);
-    else dkv_kernel<D, 2><<<grid, 128, 0, st>>>(k);
+    constexpr int KEYS = 64 * ISA_DKV_NF;   // keys per workgroup
+    const int kpb = KEYS / s.b;
+    dim3 grid(BH, (s.N_kv + kpb - 1) / kpb);
+    if (s.b == 64) dkv_kernel<D, ISA_DKV_NF, 64><<<grid, 256, 0, st>>>(k);
+    else dkv_kernel<D, ISA_DKV_NF, 32><<<grid, 256, 0, st>>>(k);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (s.N_ctx > s.k_ctx) {
+      zero_pruned_kernel<D><<<dim3(BH, s.N_ctx), 256, 0, st>>>(k);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   const int max_dyn = 2 * ISA_MAX_NKV * (int)sizeof(int);
   if (s.n_sharp > 0) {
