@@ -306,23 +306,29 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------- dQ
-// One query block per workgroup (NWAVES = b/16 waves, 16 rows each); key
-// tiles of 64 keys as in the forward: sharp blocks over the tokens of J,
-// flat blocks over the tokens of E_i and then the pooled keys of J.
+// Query-major, as the forward: each wave owns 16*QT query rows. Sharp
+// blocks all read the tokens of J, so a workgroup takes NWAVES*16*QT rows
+// (several blocks) and the key tiles stream through two LDS buffers (PIPE);
+// a flat block has its own key set (the tokens of E_i, then the pooled keys
+// of J), so it gets a workgroup of its own (NWAVES*16*QT = b).
 enum : int { kSharp = 1, kFlat = 2 };
 
-template <int D, int MODE, int NWAVES>
-__global__ __launch_bounds__(NWAVES * 64) void dq_kernel(BwdArgs a) {
+template <int D, int MODE, int QT, int NWAVES, bool PIPE>
+__global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(PIPE ? 2 : 3)))
+void dq_kernel(BwdArgs a) {
   constexpr int NT = NWAVES * 64;
   constexpr int STR = 2 * D + 32;
   constexpr int CPR = D / 8;
   constexpr int CH = kKeyTile * CPR / NT;
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;
+  constexpr int ROWS_W = 16 * QT;
+  constexpr int ROWS = NWAVES * ROWS_W;
+  constexpr int NB = PIPE ? 2 : 1;
   static_assert(CH >= 1 && NT % CPR == 0, "tile split");
-  __shared__ __attribute__((aligned(16))) char k_lds[kKeyTile * STR];
-  __shared__ __attribute__((aligned(16))) char v_lds[kKeyTile * STR];
-  __shared__ __attribute__((aligned(16))) float bias_lds[kKeyTile];
+  __shared__ __attribute__((aligned(16))) char k_lds[NB][kKeyTile * STR];
+  __shared__ __attribute__((aligned(16))) char v_lds[NB][kKeyTile * STR];
+  __shared__ __attribute__((aligned(16))) float bias_lds[NB][kKeyTile];
   extern __shared__ int tabs[];   // sharp: [N_kv]; flat: [k_ns] then [N_kv]
 
   const IsaShape& s = a.s;
@@ -333,26 +339,37 @@ __global__ __launch_bounds__(NWAVES * 64) void dq_kernel(BwdArgs a) {
   const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
   const int b = s.b, lb = b == 64 ? 6 : 5;
 
-  // this lane's query row
-  const int jq = a.qlist[(size_t)bh * a.n_q + blockIdx.x];
-  int qst, qn;
-  isa_block_range(s, jq, qst, qn);
-  const int lr = wave * 16 + c16;
-  const bool qval = lr < qn;
-  const int qtok = qst + (qval ? lr : 0);
-  bf16x8_t qf[1][KK], df[1][KK];
+  // this lane's query rows
+  int qtok[QT];
+  bool qval[QT];
+  float lse2[QT], dl[QT];
+  bf16x8_t qf[QT][KK], df[QT][KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    uint4 wq = make_uint4(0, 0, 0, 0), wd = make_uint4(0, 0, 0, 0);
-    if (qval) {
-      wq = *reinterpret_cast<const uint4*>(a.Q + (head + qtok) * D + 32 * kk + 8 * g);
-      wd = *reinterpret_cast<const uint4*>(a.dO + (head + qtok) * D + 32 * kk + 8 * g);
+  for (int qt = 0; qt < QT; ++qt) {
+    const int lr = wave * ROWS_W + 16 * qt + c16;
+    const int e = MODE == kSharp ? blockIdx.x * (ROWS >> lb) + (lr >> lb) : blockIdx.x;
+    const int o = MODE == kSharp ? (lr & (b - 1)) : lr;
+    qval[qt] = false;
+    qtok[qt] = 0;
+    if (e < a.n_q) {
+      int st, n;
+      isa_block_range(s, a.qlist[(size_t)bh * a.n_q + e], st, n);
+      qval[qt] = o < n;
+      qtok[qt] = st + (qval[qt] ? o : 0);
     }
-    qf[0][kk] = __builtin_bit_cast(bf16x8_t, wq);
-    df[0][kk] = __builtin_bit_cast(bf16x8_t, wd);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      uint4 wq = make_uint4(0, 0, 0, 0), wd = make_uint4(0, 0, 0, 0);
+      if (qval[qt]) {
+        wq = *reinterpret_cast<const uint4*>(a.Q + (head + qtok[qt]) * D + 32 * kk + 8 * g);
+        wd = *reinterpret_cast<const uint4*>(a.dO + (head + qtok[qt]) * D + 32 * kk + 8 * g);
+      }
+      qf[qt][kk] = __builtin_bit_cast(bf16x8_t, wq);
+      df[qt][kk] = __builtin_bit_cast(bf16x8_t, wd);
+    }
+    lse2[qt] = qval[qt] ? a.lse[head + qtok[qt]] : INFINITY;
+    dl[qt] = qval[qt] ? a.delta[head + qtok[qt]] : 0.0f;
   }
-  const float lse2 = qval ? a.lse[head + qtok] : INFINITY;
-  const float dl = qval ? a.delta[head + qtok] : 0.0f;
 
   // key tables: (start << 7) | n per listed block; pooled: (j << 8) | (n << 1) | in_E
   int* jtab = tabs;
@@ -396,14 +413,16 @@ __global__ __launch_bounds__(NWAVES * 64) void dq_kernel(BwdArgs a) {
   const uint16_t* vch = MODE == kFlat ? a.vcb + (size_t)bh * s.N * D : nullptr;
   const int c8 = tid % CPR;
   const float cscale = kLog2e / sqrtf((float)D);
-  float4_t dq[1][DT];
+  float4_t dq[QT][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) dq[0][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dq[qt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int t = 0; t < a.ntiles; ++t) {
-    uint4 kr[CH], vr[CH];
-    float br[CH];
-    uint32_t vm[CH];
+  uint4 kr[CH], vr[CH];
+  float br[CH];
+  uint32_t vm[CH];
+  auto fetch = [&](int t) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int slot = (tid + i * NT) / CPR;
@@ -433,41 +452,69 @@ __global__ __launch_bounds__(NWAVES * 64) void dq_kernel(BwdArgs a) {
       kr[i] = *reinterpret_cast<const uint4*>(kp + c8 * 8);
       vr[i] = *reinterpret_cast<const uint4*>(vp + c8 * 8);
     }
-    if (t > 0) __syncthreads();
+  };
+  auto put = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int slot = (tid + i * NT) / CPR;
       const uint32_t m = vm[i];
-      *reinterpret_cast<uint4*>(&k_lds[slot * STR + c8 * 16]) =
+      *reinterpret_cast<uint4*>(&k_lds[buf][slot * STR + c8 * 16]) =
           make_uint4(kr[i].x & m, kr[i].y & m, kr[i].z & m, kr[i].w & m);
-      *reinterpret_cast<uint4*>(&v_lds[slot * STR + c8 * 16]) =
+      *reinterpret_cast<uint4*>(&v_lds[buf][slot * STR + c8 * 16]) =
           make_uint4(vr[i].x & m, vr[i].y & m, vr[i].z & m, vr[i].w & m);
-      if (c8 == 0) bias_lds[slot] = br[i];
+      if (c8 == 0) bias_lds[buf][slot] = br[i];
     }
-    __syncthreads();
-    float4_t sc[1][4], dp[1][4];
-    mm_rows<D, 4, 1>(k_lds, qf, sc, g, c16);
-    mm_rows<D, 4, 1>(v_lds, df, dp, g, c16);
+  };
+  auto consume = [&](int buf) {
+    float4_t sc[QT][4], dp[QT][4];
+    mm_rows<D, 4, QT>(k_lds[buf], qf, sc, g, c16);
+    mm_rows<D, 4, QT>(v_lds[buf], df, dp, g, c16);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const float4_t bv = *reinterpret_cast<const float4_t*>(bias_lds + 16 * mt + 4 * g);
+      const float4_t bv = *reinterpret_cast<const float4_t*>(bias_lds[buf] + 16 * mt + 4 * g);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][mt][e], cscale, bv[e]) - lse2);
-        sc[0][mt][e] = p * (dp[0][mt][e] - dl);
-      }
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][mt][e], cscale, bv[e]) - lse2[qt]);
+          sc[qt][mt][e] = p * (dp[qt][mt][e] - dl[qt]);
+        }
     }
-    bf16x8_t pk[1][2];
-    pack_bf16<4, 1>(sc, pk);
-    mm_tr<D, 4, 1>(k_lds, pk, dq, g, c16);
+    bf16x8_t pk[QT][2];
+    pack_bf16<4, QT>(sc, pk);
+    mm_tr<D, 4, QT>(k_lds[buf], pk, dq, g, c16);
+  };
+
+  if (PIPE) {
+    fetch(0);
+    put(0);
+    __syncthreads();
+    for (int t = 0; t < a.ntiles; ++t) {
+      const bool more = t + 1 < a.ntiles;
+      if (more) fetch(t + 1);
+      consume(t & 1);
+      if (more) put((t + 1) & 1);
+      __syncthreads();
+    }
+  } else {
+    for (int t = 0; t < a.ntiles; ++t) {
+      fetch(t);
+      if (t > 0) __syncthreads();
+      put(0);
+      __syncthreads();
+      consume(0);
+    }
   }
 
-  if (!qval) return;
   const float rs = 1.0f / sqrtf((float)D);
-  const int pos = qtok - (jq < s.N_src ? 0 : s.L_src);
-  uint16_t* row = a.dQ + (head + qtok) * D;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) store4(row, 16 * dt + 4 * g, dq[0][dt] * rs, a.rope, D / 2, pos);
+  for (int qt = 0; qt < QT; ++qt) {
+    if (!qval[qt]) continue;
+    const int pos = qtok[qt] < s.L_src ? qtok[qt] : qtok[qt] - s.L_src;
+    uint16_t* row = a.dQ + (head + qtok[qt]) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) store4(row, 16 * dt + 4 * g, dq[qt][dt] * rs, a.rope, D / 2, pos);
+  }
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -830,17 +877,12 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
     q.qlist = a.sharp_idx;
     q.n_q = s.n_sharp;
     q.ntiles_exact = q.ntiles = (s.N_kv * s.b + kKeyTile - 1) / kKeyTile;
-    dim3 grid(s.n_sharp, BH);
+    constexpr int ROWS = 8 * 32;   // 8 waves of 32 rows
+    dim3 grid((s.n_sharp + ROWS / s.b - 1) / (ROWS / s.b), BH);
     const size_t dyn = (size_t)s.N_kv * sizeof(int);
-    if (s.b == 64) {
-      static hipError_t attr = set_dyn_lds(&dq_kernel<D, kSharp, 4>, max_dyn);
-      if (attr != hipSuccess) return attr;
-      dq_kernel<D, kSharp, 4><<<grid, 256, dyn, st>>>(q);
-    } else {
-      static hipError_t attr = set_dyn_lds(&dq_kernel<D, kSharp, 2>, max_dyn);
-      if (attr != hipSuccess) return attr;
-      dq_kernel<D, kSharp, 2><<<grid, 128, dyn, st>>>(q);
-    }
+    static hipError_t attr = set_dyn_lds(&dq_kernel<D, kSharp, 2, 8, true>, max_dyn);
+    if (attr != hipSuccess) return attr;
+    dq_kernel<D, kSharp, 2, 8, true><<<grid, 512, dyn, st>>>(q);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -853,13 +895,13 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
     dim3 grid(s.n_flat, BH);
     const size_t dyn = (size_t)(s.k_ns + s.N_kv) * sizeof(int);
     if (s.b == 64) {
-      static hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 4>, max_dyn);
+      static hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 1, 4, false>, max_dyn);
       if (attr != hipSuccess) return attr;
-      dq_kernel<D, kFlat, 4><<<grid, 256, dyn, st>>>(q);
+      dq_kernel<D, kFlat, 1, 4, false><<<grid, 256, dyn, st>>>(q);
     } else {
-      static hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 2>, max_dyn);
+      static hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 1, 2, false>, max_dyn);
       if (attr != hipSuccess) return attr;
-      dq_kernel<D, kFlat, 2><<<grid, 128, dyn, st>>>(q);
+      dq_kernel<D, kFlat, 1, 2, false><<<grid, 128, dyn, st>>>(q);
     }
     e = hipGetLastError();
   }
