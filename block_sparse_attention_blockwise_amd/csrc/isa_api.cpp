@@ -30,6 +30,7 @@ struct Layout {
   size_t qr, kr, rope;          // RoPE buffers (only when rope_base > 0)
   size_t lse;                   // saved by isa_forward for isa_backward
   size_t delta, dkc, dvc, ebits, inv_off, inv_list;   // backward scratch
+  size_t dqc, doc, ocs, dsc, pc;                     // backward of the residual (gamma != 0)
   size_t total;
 };
 
@@ -68,6 +69,14 @@ Layout make_layout(const IsaShape& s) {
   l.ebits = o;     o = align256(o + bh * s.n_flat * (size_t)((s.N_kv + 63) / 64) * 8);
   l.inv_off = o;   o = align256(o + bh * (size_t)(s.N_kv + 1) * 4);
   l.inv_list = o;  o = align256(o + bh * s.n_flat * (size_t)s.k_ns * 4);
+  const bool res = s.gamma != 0.0f;
+  const size_t rnd = res ? nd * 4 : 0;
+  const size_t rnk = res ? bh * s.N * (size_t)s.N_kv * 4 : 0;
+  l.dqc = o;       o = align256(o + rnd);
+  l.doc = o;       o = align256(o + rnd);
+  l.ocs = o;       o = align256(o + rnd);
+  l.dsc = o;       o = align256(o + rnk);
+  l.pc = o;        o = align256(o + rnk);
   l.total = o;
   return l;
 }
@@ -314,7 +323,6 @@ int isa_backward(const isa_params_t* p, const void* Q, const void* K, const void
   int rc = make_shape(p, &s);
   if (rc != ISA_OK) return rc;
   if (!Q || !K || !V || !O || !dO || !dQ || !dK || !dV || !ws) return ISA_ERR_ARG;
-  if (s.gamma != 0.0f) return ISA_ERR_UNSUPPORTED;
   const Layout l = make_layout(s);
   if (ws_bytes < l.total) return ISA_ERR_WORKSPACE;
   char* w = (char*)ws;
@@ -339,6 +347,14 @@ int isa_backward(const isa_params_t* p, const void* Q, const void* K, const void
   b.dkc = (float*)(w + l.dkc);
   b.dvc = (float*)(w + l.dvc);
   b.rope = rope ? (const float2*)(w + l.rope) : nullptr;
+  b.srows = (const double*)(w + l.srows);
+  b.qc = (const double*)(w + l.qc);
+  b.kc = (const double*)(w + l.kc);
+  b.dqc = (float*)(w + l.dqc);
+  b.doc = (float*)(w + l.doc);
+  b.ocs = (float*)(w + l.ocs);
+  b.dsc = (float*)(w + l.dsc);
+  b.pc = (float*)(w + l.pc);
   b.dQ = (uint16_t*)dQ;
   b.dK = (uint16_t*)dK;
   b.dV = (uint16_t*)dV;

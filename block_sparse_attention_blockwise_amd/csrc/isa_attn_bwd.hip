@@ -66,6 +66,15 @@ struct BwdArgs {
   float* dkc_out;
   float* dvc_out;
   const float2* rope;         // cos/sin table (nullable: no RoPE)
+  // residual gamma * O_coarse (gamma != 0 only)
+  const double* srows;        // [B,H,N,N_kv] coarse rows S[i, J] of the forward
+  const double* qc;           // [B,H,N,D] fp64 block means
+  const double* kc;
+  float* dqc;                 // [B,H,N,D] gradient of Qc (scaled), added to the rows' dQ
+  float* doc;                 // [B,H,N,D] gamma * sum of dO over each block
+  float* ocs;                 // [B,H,N,D] O_coarse as the forward added it (without gamma)
+  float* dsc;                 // [B,H,N,N_kv] gradient of the coarse logits
+  float* pc;                  // [B,H,N,N_kv] coarse softmax
   uint16_t* dQ;
   uint16_t* dK;
   uint16_t* dV;
@@ -282,27 +291,209 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- Delta
+// Delta_t = dO_t . o_t with o_t the attention output: with the residual on,
+// the forward added gamma * O_coarse of the row's block to it, which is taken
+// off again here.
+__device__ inline int token_block(const IsaShape& s, int t) {
+  return t < s.L_src ? t / s.b : s.N_src + (t - s.L_src) / s.b;
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ dO,
-                                                    const uint16_t* __restrict__ O,
-                                                    float* __restrict__ delta, size_t rows) {
+__global__ __launch_bounds__(256) void delta_kernel(BwdArgs a, const uint16_t* __restrict__ O, size_t rows) {
   constexpr int TPR = D / 8;
   const size_t row = ((size_t)blockIdx.x * 256 + threadIdx.x) / TPR;
   const int c = threadIdx.x % TPR;
   float acc = 0.f;
   if (row < rows) {
-    const uint4 x = *reinterpret_cast<const uint4*>(dO + row * D + c * 8);
+    const uint4 x = *reinterpret_cast<const uint4*>(a.dO + row * D + c * 8);
     const uint4 y = *reinterpret_cast<const uint4*>(O + row * D + c * 8);
     const uint32_t xu[4] = {x.x, x.y, x.z, x.w}, yu[4] = {y.x, y.y, y.z, y.w};
+    float oc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (a.ocs != nullptr) {
+      const size_t bh = row / a.s.L;
+      const int i = token_block(a.s, (int)(row % a.s.L));
+      const float* src = a.ocs + ((bh * a.s.N + i) * D + c * 8);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) oc[k] = a.s.gamma * src[k];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc += __uint_as_float(xu[i] << 16) * __uint_as_float(yu[i] << 16);
-      acc += __uint_as_float(xu[i] & 0xffff0000u) * __uint_as_float(yu[i] & 0xffff0000u);
+      acc += __uint_as_float(xu[i] << 16) * (__uint_as_float(yu[i] << 16) - oc[2 * i]);
+      acc += __uint_as_float(xu[i] & 0xffff0000u) * (__uint_as_float(yu[i] & 0xffff0000u) - oc[2 * i + 1]);
     }
   }
 #pragma unroll
   for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
-  if (row < rows && c == 0) delta[row] = acc;
+  if (row < rows && c == 0) const_cast<float*>(a.delta)[row] = acc;
+}
+
+// ---------------------------------------------------------------- residual
+// Backward of gamma * O_coarse (O_coarse_i = softmax over J of S[i, J]
+// applied to Vc[J], broadcast to the tokens of block i). Per query block i
+// (one workgroup): dOc_i = gamma * sum of dO over the block's rows, the
+// coarse softmax P_i (fp64, from the forward's coarse rows), O_coarse_i as
+// the forward computed it, Delta_i = dOc_i . O_coarse_i, the logit gradient
+// dS_i = P_i * (dOc_i . Vc_p - Delta_i) and dQc_i = sum_p dS_ip Kc_p / sqrt(D).
+constexpr int kResThreads = 256;
+
+__device__ inline double block_sum_f64(double x, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < kResThreads / 64; ++w) t += red[w];
+  return t;
+}
+
+__device__ inline double block_max_f64(double x, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  double t = red[0];
+  for (int w = 1; w < kResThreads / 64; ++w) t = fmax(t, red[w]);
+  return t;
+}
+
+__device__ inline float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+template <int D>
+__global__ __launch_bounds__(kResThreads) void res_row_kernel(BwdArgs a) {
+  const IsaShape& s = a.s;
+  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  __shared__ double w[ISA_MAX_NKV];
+  __shared__ double red[kResThreads / 64];
+  __shared__ float part[2][D];
+  __shared__ float dov[D], ocv[D];
+  __shared__ int jid[ISA_MAX_NKV];
+  const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
+  const double* row = a.srows + ((size_t)bh * s.N + i) * s.N_kv;
+  const size_t nbase = ((size_t)bh * s.N) * D;
+  for (int p = tid; p < s.N_kv; p += kResThreads) jid[p] = kept_id(s, ctx_row, p);
+  double mx = -INFINITY;
+  for (int p = tid; p < s.N_kv; p += kResThreads) mx = fmax(mx, row[p]);
+  mx = block_max_f64(mx, red);
+  double z = 0.0;
+  for (int p = tid; p < s.N_kv; p += kResThreads) {
+    const double e = exp(row[p] - mx);
+    w[p] = e;
+    z += e;
+  }
+  z = block_sum_f64(z, red);
+  // gamma * sum of the block's dO rows; O_coarse as the forward formed it
+  const int d = tid % D, half = tid / D;
+  int st, n;
+  isa_block_range(s, i, st, n);
+  float acc = 0.f, oacc = 0.f;
+  if (half < 2) {
+    for (int r = half; r < n; r += 2) acc += bf16f(a.dO[((size_t)bh * s.L + st + r) * D + d]);
+    for (int p = half; p < s.N_kv; p += 2) {
+      const int j = jid[p];
+      if (j >= 0) oacc += (float)w[p] * bf16f(a.vcb[nbase + (size_t)j * D + d]);
+    }
+    part[half][d] = acc;
+  }
+  __syncthreads();
+  if (tid < D) dov[tid] = s.gamma * (part[0][tid] + part[1][tid]);
+  __syncthreads();
+  if (half < 2) part[half][d] = oacc;
+  __syncthreads();
+  if (tid < D) ocv[tid] = (float)((double)(part[0][tid] + part[1][tid]) / z);
+  __syncthreads();
+  double dl = 0.0;
+  if (tid < D) dl = (double)dov[tid] * (double)ocv[tid];
+  dl = block_sum_f64(dl, red);
+  // dS over the kept blocks; the softmax goes to pc, dS to dsc and w
+  float* pc_row = a.pc + ((size_t)bh * s.N + i) * s.N_kv;
+  float* ds_row = a.dsc + ((size_t)bh * s.N + i) * s.N_kv;
+  for (int p = tid; p < s.N_kv; p += kResThreads) {
+    const int j = jid[p];
+    double dot = 0.0;
+    if (j >= 0)
+      for (int k = 0; k < D; ++k) dot += (double)dov[k] * (double)bf16f(a.vcb[nbase + (size_t)j * D + k]);
+    const double P = w[p] / z;
+    const double ds = P * (dot - dl);
+    w[p] = ds;
+    pc_row[p] = (float)P;
+    ds_row[p] = (float)ds;
+  }
+  __syncthreads();
+  double q = 0.0;
+  if (half < 2)
+    for (int p = half; p < s.N_kv; p += 2) {
+      const int j = jid[p];
+      if (j >= 0) q += w[p] * a.kc[nbase + (size_t)j * D + d];
+    }
+  __syncthreads();
+  if (half < 2) part[half][d] = (float)q;
+  __syncthreads();
+  if (tid < D) {
+    const size_t o = nbase + (size_t)i * D + tid;
+    a.dqc[o] = (part[0][tid] + part[1][tid]) / sqrtf((float)D);
+    a.doc[o] = dov[tid];
+    a.ocs[o] = ocv[tid];
+  }
+}
+
+// dKc_p += sum_i dS_ip Qc_i / sqrt(D) and dVc_p += sum_i P_ip dOc_i for 64
+// kept blocks per workgroup (a product of the coarse-row matrices with Qc
+// and dOc), summed in a fixed order over i; adds to the pooled-key gradients
+// when those were written (accumulate), else stores.
+template <int D>
+__global__ __launch_bounds__(256) void res_col_kernel(BwdArgs a, int accumulate) {
+  constexpr int PT = 64, IC = 32;
+  constexpr int DPT = D / 4;   // d values per thread
+  const IsaShape& s = a.s;
+  const int bh = blockIdx.y, p0 = blockIdx.x * PT, tid = threadIdx.x;
+  const int pl = tid / 4, d0 = (tid % 4) * DPT;
+  __shared__ float ds_t[IC][PT], p_t[IC][PT];
+  __shared__ float qc_t[IC][D], do_t[IC][D];
+  float dk[DPT], dv[DPT];
+#pragma unroll
+  for (int x = 0; x < DPT; ++x) dk[x] = dv[x] = 0.f;
+  const size_t rbase = (size_t)bh * s.N;
+  for (int i0 = 0; i0 < s.N; i0 += IC) {
+    __syncthreads();
+    for (int x = tid; x < IC * PT; x += 256) {
+      const int ii = x / PT, pp = x % PT;
+      const bool ok = i0 + ii < s.N && p0 + pp < s.N_kv;
+      const size_t o = (rbase + i0 + ii) * s.N_kv + p0 + pp;
+      ds_t[ii][pp] = ok ? a.dsc[o] : 0.f;
+      p_t[ii][pp] = ok ? a.pc[o] : 0.f;
+    }
+    for (int x = tid; x < IC * D; x += 256) {
+      const int ii = x / D, dd = x % D;
+      const bool ok = i0 + ii < s.N;
+      const size_t o = (rbase + i0 + ii) * D + dd;
+      qc_t[ii][dd] = ok ? (float)a.qc[o] : 0.f;
+      do_t[ii][dd] = ok ? a.doc[o] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int ii = 0; ii < IC; ++ii) {
+      const float x = ds_t[ii][pl], y = p_t[ii][pl];
+#pragma unroll
+      for (int k = 0; k < DPT; ++k) {
+        dk[k] += x * qc_t[ii][d0 + k];
+        dv[k] += y * do_t[ii][d0 + k];
+      }
+    }
+  }
+  const int p = p0 + pl;
+  if (p >= s.N_kv) return;
+  const int j = kept_id(s, a.ctx_idx + (size_t)bh * s.k_ctx, p);
+  if (j < 0) return;
+  const float rs = 1.0f / sqrtf((float)D);
+  float* ok = a.dkc_out + (rbase + j) * D + d0;
+  float* ov = a.dvc_out + (rbase + j) * D + d0;
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) {
+    ok[k] = (accumulate ? ok[k] : 0.f) + dk[k] * rs;
+    ov[k] = (accumulate ? ov[k] : 0.f) + dv[k];
+  }
 }
 
 // ---------------------------------------------------------------- dQ
@@ -512,8 +703,22 @@ void dq_kernel(BwdArgs a) {
     if (!qval[qt]) continue;
     const int pos = qtok[qt] < s.L_src ? qtok[qt] : qtok[qt] - s.L_src;
     uint16_t* row = a.dQ + (head + qtok[qt]) * D;
+    // the residual reaches Q through the block mean
+    const float* gq = nullptr;
+    float inv_n = 0.f;
+    if (a.dqc != nullptr) {
+      const int jb = token_block(s, qtok[qt]);
+      int st, n;
+      isa_block_range(s, jb, st, n);
+      gq = a.dqc + ((size_t)bh * s.N + jb) * D;
+      inv_n = 1.0f / (float)n;
+    }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) store4(row, 16 * dt + 4 * g, dq[qt][dt] * rs, a.rope, D / 2, pos);
+    for (int dt = 0; dt < DT; ++dt) {
+      float4_t x = dq[qt][dt] * rs;
+      if (gq) x += *reinterpret_cast<const float4_t*>(gq + 16 * dt + 4 * g) * inv_n;
+      store4(row, 16 * dt + 4 * g, x, a.rope, D / 2, pos);
+    }
   }
 }
 
@@ -840,10 +1045,17 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const bool residual = s.gamma != 0.0f;
+  if (!residual) a.dqc = a.doc = a.ocs = nullptr;
+  if (residual) {
+    res_row_kernel<D><<<dim3(s.N, BH), kResThreads, 0, st>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   {
     const size_t rows = (size_t)BH * s.L;
     const size_t threads = rows * (D / 8);
-    delta_kernel<D><<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(a.dO, O, const_cast<float*>(a.delta), rows);
+    delta_kernel<D><<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(a, O, rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -855,9 +1067,14 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (residual) {
+    res_col_kernel<D><<<dim3((s.N_kv + 63) / 64, BH), 256, 0, st>>>(a, pooled ? 1 : 0);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   {
     BwdArgs k = a;
-    if (!pooled) k.dkc = k.dvc = nullptr;
+    if (!pooled && !residual) k.dkc = k.dvc = nullptr;
     constexpr int KEYS = 64 * ISA_DKV_NF;   // keys per workgroup
     const int kpb = KEYS / s.b;
     dim3 grid(BH, (s.N_kv + kpb - 1) / kpb);
@@ -931,6 +1148,14 @@ hipError_t isa_launch_backward(const IsaShape& s, const IsaBwdBuffers& w, hipStr
   a.dkc = a.dkc_out = w.dkc;
   a.dvc = a.dvc_out = w.dvc;
   a.rope = w.rope;
+  a.srows = w.srows;
+  a.qc = w.qc;
+  a.kc = w.kc;
+  a.dqc = w.dqc;
+  a.doc = w.doc;
+  a.ocs = w.ocs;
+  a.dsc = w.dsc;
+  a.pc = w.pc;
   a.dQ = w.dQ;
   a.dK = w.dK;
   a.dV = w.dV;

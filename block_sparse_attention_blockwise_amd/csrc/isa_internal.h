@@ -90,6 +90,15 @@ struct IsaBwdBuffers {
   float* dkc;
   float* dvc;
   const float2* rope;         // nullable
+  // residual (gamma != 0) inputs and scratch
+  const double* srows;
+  const double* qc;
+  const double* kc;
+  float* dqc;
+  float* doc;
+  float* ocs;
+  float* dsc;
+  float* pc;
   uint16_t* dQ;
   uint16_t* dK;
   uint16_t* dV;

@@ -195,15 +195,16 @@ ISA_API int isa_forward(const isa_params_t* p, const void* Q, const void* K, con
  * constant): the exact terms give the usual softmax-attention gradients; the
  * 0th-order Taylor terms reach K and V through the block means (each token of
  * block j receives 1/n_j of the gradient of Kc_j, Vc_j); tokens of pruned
- * context blocks get zero gradient. With rope_base != 0 the gradients are
- * those of the unrotated Q and K (the transposed rotation is applied).
+ * context blocks get zero gradient; with gamma != 0 the residual
+ * gamma * O_coarse adds its gradient through Qc, Kc, Vc. With rope_base != 0
+ * the gradients are those of the unrotated Q and K (the transposed rotation
+ * is applied).
  * Q, K, V: the inputs of the isa_forward call that filled `ws` (same
  * params), O its output, dO [B,H,L,D] bf16; writes dQ, dK, dV [B,H,L,D]
  * bf16 (caller-owned, every row written). `ws` must be that call's workspace,
  * unmodified since: the forward saved its selections, each row's softmax
  * log-sum-exp and the rotated Q, K there, and the backward uses the rest of
- * it as scratch. Deterministic (fixed summation orders, no float atomics).
- * gamma != 0 returns ISA_ERR_UNSUPPORTED. */
+ * it as scratch. Deterministic (fixed summation orders, no float atomics). */
 ISA_API int isa_backward(const isa_params_t* p, const void* Q, const void* K, const void* V,
                          const void* O, const void* dO, void* dQ, void* dK, void* dV,
                          void* ws, size_t ws_bytes, void* stream);

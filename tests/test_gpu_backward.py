@@ -99,7 +99,8 @@ def _check_all_rows(p, cfg_id=1, seed=0, heads=None):
     plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
     for (bi, h) in (heads or [(x, y) for x in range(p.B) for y in range(p.H)]):
         log(f"head ({bi},{h})")
-        gq, gk, gv = _oracle_grads(plan, inp, dO_vals, bi, h, res["sel"], rope_base=p.rope_base)
+        gq, gk, gv = _oracle_grads(plan, inp, dO_vals, bi, h, res["sel"], gamma=p.gamma,
+                                   rope_base=p.rope_base)
         _compare("dQ", res["dQ"][bi, h], gq)
         _compare("dK", res["dK"][bi, h], gk)
         _compare("dV", res["dV"][bi, h], gv)
@@ -149,6 +150,28 @@ def test_backward_closed_form_sums_and_determinism(dev):
         log(f"head {h}: |sum dV - sum dO| max {np.abs(sv - so).max():.3e}; |sum dK| max {np.abs(sk).max():.3e}")
         assert (np.abs(sv - so) <= 0.02 * scale_v + 1e-3).all()
         assert (np.abs(sk) <= 0.02 * scale_k + 1e-3).all()
+
+
+@pytest.mark.parametrize("gamma,D,b", [(0.5, 128, 64), (-0.3, 64, 32)])
+def test_backward_with_residual(dev, gamma, D, b):
+    """gamma != 0: the residual gamma * O_coarse adds its gradient through the
+    block means (oracle R12); every element against the oracle."""
+    p = isa.Params(1, 2, 700, 451, D, b, 0.25, 0.5, 0.125, gamma)
+    _check_all_rows(p)
+
+
+def test_backward_residual_sums(dev):
+    """With the residual the dV rows add up to (1 + gamma) times the summed dO
+    rows (each coarse softmax row sums to one too)."""
+    gamma = 0.4
+    p = isa.Params(1, 2, 1500, 1300, 128, 64, 0.25, 0.5, 0.125, gamma)
+    inp = isa_inputs.make_inputs(1, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    dO_bits, dO_vals = _dO(p, 4)
+    r = _run(p, inp, dO_bits, dev)
+    for h in range(p.H):
+        sv, so = r["dV"][0, h].sum(0), (1 + gamma) * dO_vals[0, h].sum(0)
+        log(f"head {h}: |sum dV - (1+gamma) sum dO| max {np.abs(sv - so).max():.3e}")
+        assert (np.abs(sv - so) <= 0.02 * np.abs(r["dV"][0, h]).sum(0) + 1e-3).all()
 
 
 def test_backward_with_rope(dev):

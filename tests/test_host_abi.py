@@ -136,9 +136,14 @@ def test_calls_fail_before_launch(isa):
                           1 << 40, None) == -1
     assert L.isa_backward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
                           16, None) == -3
-    g = _params(isa, gamma=0.5)
+    g = _params(isa, gamma=float("nan"))
     assert L.isa_backward(ctypes.byref(g), fake, fake, fake, fake, fake, fake, fake, fake, fake,
-                          1 << 40, None) == -2
+                          1 << 40, None) == -1
+    # the residual's scratch makes the workspace larger
+    pl0, pl1 = isa.IsaPlan(), isa.IsaPlan()
+    assert L.isa_plan(ctypes.byref(p), ctypes.byref(pl0)) == 0
+    assert L.isa_plan(ctypes.byref(_params(isa, gamma=0.5)), ctypes.byref(pl1)) == 0
+    assert pl1.workspace_bytes > pl0.workspace_bytes
     assert L.isa_dense_attn(1, 1, 0, 128, fake, fake, fake, fake, None) == -1
     assert L.isa_dense_attn(1, 1, 16, 96, fake, fake, fake, fake, None) == -2
     assert L.isa_dense_attn(1, 1, 16, 128, None, fake, fake, fake, None) == -1
