@@ -382,6 +382,29 @@ def main():
     torch.cuda.synchronize()
     same = bool(torch.equal(O_fwd.view(torch.int16), O.view(torch.int16)))
 
+    # backward of the same forward (dO ~ N(0, 1)): isa_forward saves its state in
+    # ws_f, isa_backward reuses it
+    g = torch.Generator(device=dev).manual_seed(5)
+    dO = torch.randn(Q.shape, device=dev, generator=g).to(torch.bfloat16)
+    gQ, gK, gV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+
+    def fwd_bwd():
+        chk("fwd", lib.isa_forward(pr, Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                                   ws_f.data_ptr(), ws_f.numel(), None, sp))
+        e0.record(stream)
+        chk("bwd", lib.isa_backward(pr, Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                                    dO.data_ptr(), gQ.data_ptr(), gK.data_ptr(), gV.data_ptr(),
+                                    ws_f.data_ptr(), ws_f.numel(), sp))
+        e1.record(stream)
+    fwd_bwd()
+    bwd_ms = 0.0
+    nb = max(args.steps // 5, 2)
+    for _ in range(nb):
+        fwd_bwd()
+        torch.cuda.synchronize()
+        bwd_ms += e0.elapsed_time(e1) / nb
+    del dO, gQ, gK, gV
+
     # decoupled RoPE fused with pooling (same workload, base 10000): reads Q, K, V
     # once, writes the rotated Q and K and the block means
     pr_rope = isa.Params(p.B, p.H, p.L_src, p.L_ctx, p.D, p.b, p.alpha_s, p.alpha_f, p.alpha_ns,
@@ -449,6 +472,7 @@ def main():
                       "flat_taylor_attn": (flops["flat_exact"] + flops["taylor"]) /
                       (per["flat_taylor_attn"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "pool_hbm_frac": pool_bytes / (per["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "isa_backward_ms": bwd_ms,
         "rope_pool_ms": rope_ms,
         "rope_pool_hbm_frac": (pool_bytes + 2 * BH * (p.L_src + p.L_ctx) * p.D * 2) /
                               (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
