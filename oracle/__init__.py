@@ -8,9 +8,9 @@ generator module isa_inputs, which holds no arithmetic of the method.
 from .isa_oracle import (Plan, make_plan, pool, coarse_scores, context_scores, top_k,
                          sharpness, split, kept_blocks, exact_sets, isa_head, isa_forward,
                          dense_attention, HeadResult, coarse_output, rope, rope_positions,
-                         rope_tables, isa_head_backward, rope_backward)
+                         rope_tables, isa_head_backward, isa_head_dq_rows, rope_backward)
 
 __all__ = ["Plan", "make_plan", "pool", "coarse_scores", "context_scores", "top_k",
            "sharpness", "split", "kept_blocks", "exact_sets", "isa_head", "isa_forward",
            "dense_attention", "HeadResult", "coarse_output", "rope", "rope_positions",
-           "rope_tables", "isa_head_backward", "rope_backward"]
+           "rope_tables", "isa_head_backward", "isa_head_dq_rows", "rope_backward"]

@@ -440,6 +440,40 @@ def isa_head_backward(Q, K, V, dO, plan: Plan, selections: dict | None = None,
     return dQ, dK, dV
 
 
+def isa_head_dq_rows(Q, K, V, dO, plan: Plan, rows, selections: dict | None = None):
+    """dQ of the listed token rows only (gamma = 0), [len(rows), D] fp64: each
+    row's own softmax over its key set gives its dQ (R12), so large shapes can
+    be sampled row by row."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    D = Q.shape[1]
+    scale = 1.0 / math.sqrt(D)
+    f = isa_head(Q, K, V, plan, selections=selections, compute_output=False)
+    J = kept_blocks(f.ctx_idx, plan)
+    counts = np.asarray(plan.counts, dtype=np.float64)
+    J_tok = np.concatenate([_token_range(plan, j) for j in J])
+    block_of = np.concatenate([np.full(n, j) for j, n in enumerate(plan.counts)])
+    flat_row = {int(i): r for r, i in enumerate(f.flat_idx)}
+    out = np.empty((len(rows), D))
+    for k, t in enumerate(np.asarray(rows, dtype=np.int64)):
+        i = int(block_of[t])
+        if i in flat_row:
+            Ei = f.flat_exact_idx[flat_row[i]]
+            Ti = np.setdiff1d(J, Ei)
+            ex = (np.concatenate([_token_range(plan, j) for j in Ei]) if Ei.size
+                  else np.zeros(0, dtype=np.int64))
+            Kx = np.vstack([K[ex], f.Kc[Ti]])
+            Vx = np.vstack([V[ex], f.Vc[Ti]])
+            bias = np.concatenate([np.zeros(ex.size), np.log(counts[Ti])])
+        else:
+            Kx, Vx, bias = K[J_tok], V[J_tok], np.zeros(J_tok.size)
+        gq, _, _ = _attn_rows_backward(Q[t:t + 1], dO[t:t + 1], Kx, Vx, bias, scale)
+        out[k] = gq[0]
+    return out
+
+
 def rope_backward(dXr: np.ndarray, L_src: int, L_ctx: int, base: float) -> np.ndarray:
     """Gradient through the rotation of R11 (the transpose of each 2x2
     rotation, with the same fp32 cos/sin values), fp64, rounding taken as

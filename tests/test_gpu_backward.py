@@ -84,8 +84,7 @@ def _oracle_grads(plan, inp, dO_vals, bi, h, sel, gamma=0.0, rope_base=0.0):
     assert np.array_equal(ref_sel.ctx_idx, selections["ctx_idx"])
     assert np.array_equal(ref_sel.sharp_idx, selections["sharp_idx"])
     assert np.array_equal(ref_sel.flat_exact_idx, selections["flat_exact_idx"].reshape(ref_sel.flat_exact_idx.shape))
-    gq, gk, gv = isa_oracle.isa_head_backward(Qv, Kv, Vv, dO_vals[bi, h], plan, selections=selections,
-                                              gamma=gamma)
+    gq, gk, gv = isa_oracle.isa_head_backward(Qv, Kv, Vv, dO_vals[bi, h], plan, gamma=gamma)
     if rope_base:
         gq = isa_oracle.rope_backward(gq, plan.L_src, plan.L_ctx, rope_base)
         gk = isa_oracle.rope_backward(gk, plan.L_src, plan.L_ctx, rope_base)
@@ -193,3 +192,44 @@ def test_backward_16k_workload(dev):
         sv, so, sk = res["dV"][0, h].sum(0), dO_vals[0, h].sum(0), res["dK"][0, h].sum(0)
         assert (np.abs(sv - so) <= 0.02 * np.abs(res["dV"][0, h]).sum(0) + 1e-3).all(), h
         assert (np.abs(sk) <= 0.02 * np.abs(res["dK"][0, h]).sum(0) + 1e-3).all(), h
+
+
+def test_backward_64k_workload(dev):
+    """The 64K-token workload (H = 40, D = 128, b = 64, default ratios) in the
+    launch configuration the benchmark times: dQ of sampled rows (segment and
+    tail edges included) of three heads against the oracle row by row, and
+    the gradient sums of every head."""
+    c = isa_inputs.CONFIGS[4]
+    p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"])
+    inp = isa_inputs.make_inputs(4, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    dO_bits, dO_vals = _dO(p, 9)
+    log("64k backward")
+    Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
+    dO = bf16_tensor(dO_bits, dev)
+    ws = isa.workspace(p, dev)
+    O, dbg = isa.forward(Q, K, V, p, debug=True, workspace=ws)
+    dQ, dK, dV = isa.backward(Q, K, V, O, dO, p, ws)
+    torch.cuda.synchronize()
+    sv = dV.float().sum(dim=2)[0]
+    sk = dK.float().sum(dim=2)[0]
+    av = dV.float().abs().sum(dim=2)[0]
+    ak = dK.float().abs().sum(dim=2)[0]
+    so = dO.float().sum(dim=2)[0]
+    assert bool(((sv - so).abs() <= 0.02 * av + 1e-3).all())
+    assert bool((sk.abs() <= 0.02 * ak + 1e-3).all())
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    sel = {k: v.cpu().numpy() for k, v in dbg.items()}
+    rng = np.random.default_rng(21)
+    for h in (0, 17, 39):
+        rows = set(rng.choice(plan.L_src + plan.L_ctx, size=160, replace=False).tolist())
+        rows |= {0, plan.L_src - 1, plan.L_src, plan.L_src + plan.L_ctx - 1}
+        rows = np.array(sorted(rows))
+        Qv, Kv, Vv = (inp[n][1][0, h] for n in "QKV")
+        own = isa_oracle.isa_head(Qv, Kv, Vv, plan, compute_output=False)
+        assert np.array_equal(own.ctx_idx + plan.N_src, sel["ctx_idx"][0, h])
+        assert np.array_equal(own.sharp_idx, sel["sharp_idx"][0, h])
+        assert np.array_equal(own.flat_exact_idx, sel["flat_exact_idx"][0, h])
+        ref = isa_oracle.isa_head_dq_rows(Qv, Kv, Vv, dO_vals[0, h], plan, rows)
+        got = dQ[0, h, torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+        log(f"head {h}")
+        _compare("dQ rows", got, ref)

@@ -138,3 +138,13 @@ def test_rope_backward_is_the_conjugate_rotation():
     R = np.empty_like(X)
     R[:, 0::2], R[:, 1::2] = xz.real, xz.imag
     np.testing.assert_allclose(O.rope_backward(R, L_src, L_ctx, base), X, rtol=0, atol=1e-6)
+
+
+def test_row_sampled_dq_matches_full_backward():
+    """The row-by-row dQ (for sampling large shapes) equals the full
+    backward's rows, sharp and flat alike."""
+    plan = O.make_plan(200, 170, 32, 0.5, 0.5, 0.3)
+    Q, K, V, dO = _rand(8, 370, 16)
+    gq, _, _ = O.isa_head_backward(Q, K, V, dO, plan)
+    rows = np.array([0, 5, 63, 64, 150, 199, 200, 250, 369])
+    np.testing.assert_allclose(O.isa_head_dq_rows(Q, K, V, dO, plan, rows), gq[rows], rtol=1e-10, atol=1e-12)
