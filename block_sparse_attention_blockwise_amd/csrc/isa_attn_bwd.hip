@@ -19,12 +19,14 @@
 //   * dq_kernel (query-major, as the forward): per query block, over the key
 //     tiles the forward used; S^T = K Q^T and dP^T = V dO^T on the matrix
 //     cores, P recomputed from the saved log-sum-exp, dQ^T += K^T dS^T;
-//   * dkv_kernel (key-major): per 64*NF keys of J (whole kept blocks), the
+//   * dkv_pc_kernel (key-major): per 128 keys of J (whole kept blocks), the
 //     keys held in registers, over every query block that reads them exactly
 //     (all sharp blocks, then each kept block's flat blocks with the other
-//     keys masked); S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS;
-//     the pooled gradients dKc_j / n_j, dVc_j / n_j are added before the rows
-//     are written; zero_pruned_kernel zeroes the rows of pruned blocks;
+//     keys masked); producer waves form S = Q K^T, P and dV^T += dO^T P,
+//     consumer waves (one block behind, P passed through LDS) dP = dO V^T,
+//     dS and dK^T += Q^T dS; the pooled gradients dKc_j / n_j, dVc_j / n_j
+//     are added before the rows are written; zero_pruned_kernel zeroes the
+//     rows of pruned blocks;
 //   * dkv_pooled_kernel (key-major over the pooled keys): per 64 positions of
 //     J, over every flat block; writes dKc, dVc (fp32).
 // With decoupled RoPE the gradients of the rotated Q and K are turned back by
@@ -731,8 +733,9 @@ template <int D, int NT, int BR>
 struct QueryStage {
   static constexpr int STR = 2 * D + 32;
   static constexpr int CPR = D / 8;
-  static constexpr int CHQ = BR * CPR / NT;
-  static_assert(CHQ >= 1 && (BR * CPR) % NT == 0, "query tile split");
+  static constexpr int NCH = BR * CPR;               // 16-byte chunks per tensor
+  static constexpr int CHQ = (NCH + NT - 1) / NT;
+  static_assert(NCH % NT == 0 || NCH < NT, "query tile split");
   uint4 q[CHQ], d[CHQ];
   float lv, dv;
 
@@ -744,7 +747,7 @@ struct QueryStage {
       const int ch = tid + i * NT, r = ch / CPR, c = ch % CPR;
       q[i] = make_uint4(0, 0, 0, 0);
       d[i] = make_uint4(0, 0, 0, 0);
-      if (r < n) {
+      if (ch < NCH && r < n) {
         q[i] = *reinterpret_cast<const uint4*>(a.Q + (head + st + r) * D + c * 8);
         d[i] = *reinterpret_cast<const uint4*>(a.dO + (head + st + r) * D + c * 8);
       }
@@ -761,8 +764,10 @@ struct QueryStage {
 #pragma unroll
     for (int i = 0; i < CHQ; ++i) {
       const int ch = tid + i * NT, r = ch / CPR, c = ch % CPR;
-      *reinterpret_cast<uint4*>(q_lds + r * STR + c * 16) = q[i];
-      *reinterpret_cast<uint4*>(d_lds + r * STR + c * 16) = d[i];
+      if (ch < NCH) {
+        *reinterpret_cast<uint4*>(q_lds + r * STR + c * 16) = q[i];
+        *reinterpret_cast<uint4*>(d_lds + r * STR + c * 16) = d[i];
+      }
     }
     if (tid < BR) {
       l_lds[tid] = lv;
@@ -804,44 +809,50 @@ __device__ __forceinline__ void kv_block(const char* q_lds, const char* d_lds, c
   mm_tr<D, MT, NF>(q_lds, pd, dk, g, c16);
 }
 
-#ifndef ISA_DKV_NF
-#define ISA_DKV_NF 1
-#endif
-
-// Exact keys, key-major: one workgroup per KPB consecutive positions of J
-// (4 waves of 16*NF keys, KPB = 64*NF/b kept blocks), over the sharp blocks
-// (every kept block is read by all of them) and then, block by block, the
-// flat blocks whose E_i holds that kept block (the workgroup's other keys
-// masked for those).
-template <int D, int NF, int BR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NF == 1 ? 2 : 1)))
-void dkv_kernel(BwdArgs a) {
-  constexpr int NT = 256;
+// Exact keys, producer/consumer form: one workgroup per 128 keys of J (whole
+// kept blocks), 8 waves in 4 pairs, each pair owning 32 keys. The producer
+// wave of a pair computes S = Q K^T and P for the current query block,
+// passes P (bf16) to its consumer through LDS and accumulates dV^T += dO^T P;
+// the consumer works one query block behind: dP = dO V^T, dS = P (dP - Delta)
+// and dK^T += Q^T dS. Each operand read from LDS feeds two matrix-core
+// products (32 keys per wave) while both roles stay within 256 registers, so
+// two waves share each SIMD. Query blocks stream through three LDS buffers
+// (the producer's, the consumer's and the one being filled).
+template <int D, int BR>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void dkv_pc_kernel(BwdArgs a) {
+  constexpr int NT = 512;
   constexpr int MT = BR / 16;
-  constexpr int KW = 16 * NF;
-  constexpr int KPB = 4 * KW / BR;
+  constexpr int NF = 2;                    // 32 keys per wave
+  constexpr int KEYS = 128;
+  constexpr int KPB = KEYS / BR;
   constexpr int STR = 2 * D + 32;
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;
-  static_assert(KPB >= 1 && KPB * BR == 4 * KW, "whole blocks per workgroup");
-  __shared__ __attribute__((aligned(16))) char q_lds[2][BR * STR];
-  __shared__ __attribute__((aligned(16))) char d_lds[2][BR * STR];
-  __shared__ __attribute__((aligned(16))) float l_lds[2][BR];
-  __shared__ __attribute__((aligned(16))) float dl_lds[2][BR];
+  constexpr int PX = NF * MT * 2;          // packed bf16 pairs of P per lane
+  __shared__ __attribute__((aligned(16))) char q_lds[3][BR * STR];
+  __shared__ __attribute__((aligned(16))) char d_lds[3][BR * STR];
+  __shared__ __attribute__((aligned(16))) float l_lds[3][BR];
+  __shared__ __attribute__((aligned(16))) float dl_lds[3][BR];
+  __shared__ uint32_t pex[2][4][PX][64];
 
   const IsaShape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int bh = blockIdx.x, pb = blockIdx.y * KPB;   // heads vary fastest
+  const bool producer = wave < 4;
+  const int pair = wave & 3;
+  const int bh = blockIdx.x, pb = blockIdx.y * KPB;
   const size_t head = (size_t)bh * s.L;
   const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
 
   int kb[NF], kj[NF], ktok[NF], kn[NF];
   bool kval[NF];
-  bf16x8_t kf[NF][KK], vf[NF][KK];
+  // producer: K rows of its keys; consumer: V rows of the same keys
+  bf16x8_t fr[NF][KK];
+  const uint16_t* src = producer ? a.K : a.V;
 #pragma unroll
   for (int nf = 0; nf < NF; ++nf) {
-    const int kidx = wave * KW + 16 * nf + c16;
+    const int kidx = pair * 32 + 16 * nf + c16;
     kb[nf] = kidx / BR;
     const int o = kidx % BR;
     kj[nf] = kept_id(s, ctx_row, pb + kb[nf]);
@@ -852,13 +863,9 @@ void dkv_kernel(BwdArgs a) {
     ktok[nf] = st + (kval[nf] ? o : 0);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      uint4 wk = make_uint4(0, 0, 0, 0), wv = make_uint4(0, 0, 0, 0);
-      if (kval[nf]) {
-        wk = *reinterpret_cast<const uint4*>(a.K + (head + ktok[nf]) * D + 32 * kk + 8 * g);
-        wv = *reinterpret_cast<const uint4*>(a.V + (head + ktok[nf]) * D + 32 * kk + 8 * g);
-      }
-      kf[nf][kk] = __builtin_bit_cast(bf16x8_t, wk);
-      vf[nf][kk] = __builtin_bit_cast(bf16x8_t, wv);
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (kval[nf]) w = *reinterpret_cast<const uint4*>(src + (head + ktok[nf]) * D + 32 * kk + 8 * g);
+      fr[nf][kk] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
 
@@ -889,11 +896,11 @@ void dkv_kernel(BwdArgs a) {
   };
 
   const float cscale = kLog2e / sqrtf((float)D);
-  float4_t dk[NF][DT], dv[NF][DT];
+  float4_t acc[NF][DT];   // producer: dV^T; consumer: dK^T (raw)
 #pragma unroll
   for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) dk[nf][dt] = dv[nf][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; ++dt) acc[nf][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   if (total > 0) {
     QueryStage<D, NT, BR> stage;
@@ -901,18 +908,61 @@ void dkv_kernel(BwdArgs a) {
     stage.fetch(a, head, query_at(0, act_cur), tid);
     stage.put(q_lds[0], d_lds[0], l_lds[0], dl_lds[0], tid);
     __syncthreads();
-    for (int i = 0; i < total; ++i) {
-      const int buf = i & 1;
+    for (int i = 0; i <= total; ++i) {
+      const int cur = i % 3, prev = (i + 2) % 3, next = (i + 1) % 3;
       int act_next = -1;
       const bool more = i + 1 < total;
       if (more) stage.fetch(a, head, query_at(i + 1, act_next), tid);
-      float kbias[NF];
+      if (producer) {
+        if (i < total) {
+          float kbias[NF];
 #pragma unroll
-      for (int nf = 0; nf < NF; ++nf)
-        kbias[nf] = (kval[nf] && (act_cur < 0 || act_cur == kb[nf])) ? 0.0f : -INFINITY;
-      kv_block<D, MT, NF>(q_lds[buf], d_lds[buf], l_lds[buf], dl_lds[buf], kf, vf, kbias, cscale, dk, dv,
-                          g, c16);
-      if (more) stage.put(q_lds[buf ^ 1], d_lds[buf ^ 1], l_lds[buf ^ 1], dl_lds[buf ^ 1], tid);
+          for (int nf = 0; nf < NF; ++nf)
+            kbias[nf] = (kval[nf] && (act_cur < 0 || act_cur == kb[nf])) ? 0.0f : -INFINITY;
+          float4_t sc[NF][MT];
+          mm_rows<D, MT, NF>(q_lds[cur], fr, sc, g, c16);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const float4_t lv = *reinterpret_cast<const float4_t*>(l_lds[cur] + 16 * mt + 4 * g);
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                sc[nf][mt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nf][mt][e], cscale, kbias[nf]) - lv[e]);
+          }
+          bf16x8_t pp[NF][MT / 2];
+          pack_bf16<MT, NF>(sc, pp);
+          uint32_t* px = &pex[i & 1][pair][0][lane];
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              px[(2 * (nf * MT + mt)) * 64] = pack_bf16x2(sc[nf][mt][0], sc[nf][mt][1]);
+              px[(2 * (nf * MT + mt) + 1) * 64] = pack_bf16x2(sc[nf][mt][2], sc[nf][mt][3]);
+            }
+          mm_tr<D, MT, NF>(d_lds[cur], pp, acc, g, c16);
+        }
+      } else if (i > 0) {
+        float4_t dp[NF][MT];
+        mm_rows<D, MT, NF>(d_lds[prev], fr, dp, g, c16);
+        const uint32_t* px = &pex[(i - 1) & 1][pair][0][lane];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const float4_t dl = *reinterpret_cast<const float4_t*>(dl_lds[prev] + 16 * mt + 4 * g);
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf) {
+            const uint32_t u0 = px[(2 * (nf * MT + mt)) * 64], u1 = px[(2 * (nf * MT + mt) + 1) * 64];
+            const float p[4] = {__uint_as_float(u0 << 16), __uint_as_float(u0 & 0xffff0000u),
+                                __uint_as_float(u1 << 16), __uint_as_float(u1 & 0xffff0000u)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[nf][mt][e] = p[e] * (dp[nf][mt][e] - dl[e]);
+          }
+        }
+        bf16x8_t pd[NF][MT / 2];
+        pack_bf16<MT, NF>(dp, pd);
+        mm_tr<D, MT, NF>(q_lds[prev], pd, acc, g, c16);
+      }
+      if (more) stage.put(q_lds[next], d_lds[next], l_lds[next], dl_lds[next], tid);
       __syncthreads();
       act_cur = act_next;
     }
@@ -923,21 +973,18 @@ void dkv_kernel(BwdArgs a) {
   for (int nf = 0; nf < NF; ++nf) {
     if (!kval[nf]) continue;
     const int j = kj[nf];
-    // pooled-key gradients reach every token of the block through the mean
-    const float* gk = a.dkc ? a.dkc + ((size_t)bh * s.N + j) * D : nullptr;
-    const float* gv = a.dvc ? a.dvc + ((size_t)bh * s.N + j) * D : nullptr;
     const float inv_n = 1.0f / (float)kn[nf];
     const int pos = ktok[nf] - (j < s.N_src ? 0 : s.L_src);
-    uint16_t* krow = a.dK + (head + ktok[nf]) * D;
-    uint16_t* vrow = a.dV + (head + ktok[nf]) * D;
+    // pooled-key gradients reach every token of the block through the mean
+    const float* gp = producer ? a.dvc : a.dkc;
+    if (gp) gp += ((size_t)bh * s.N + j) * D;
+    uint16_t* row = (producer ? a.dV : a.dK) + (head + ktok[nf]) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int d0 = 16 * dt + 4 * g;
-      float4_t xk = dk[nf][dt] * rs, xv = dv[nf][dt];
-      if (gk) xk += *reinterpret_cast<const float4_t*>(gk + d0) * inv_n;
-      if (gv) xv += *reinterpret_cast<const float4_t*>(gv + d0) * inv_n;
-      store4(krow, d0, xk, a.rope, D / 2, pos);
-      store4(vrow, d0, xv, nullptr, 0, 0);
+      float4_t x = producer ? acc[nf][dt] : acc[nf][dt] * rs;
+      if (gp) x += *reinterpret_cast<const float4_t*>(gp + d0) * inv_n;
+      store4(row, d0, x, producer ? nullptr : a.rope, D / 2, pos);
     }
   }
 }
@@ -1075,11 +1122,10 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
   {
     BwdArgs k = a;
     if (!pooled && !residual) k.dkc = k.dvc = nullptr;
-    constexpr int KEYS = 64 * ISA_DKV_NF;   // keys per workgroup
-    const int kpb = KEYS / s.b;
+const int kpb = 128 / s.b;   // 128 keys per workgroup
     dim3 grid(BH, (s.N_kv + kpb - 1) / kpb);
-    if (s.b == 64) dkv_kernel<D, ISA_DKV_NF, 64><<<grid, 256, 0, st>>>(k);
-    else dkv_kernel<D, ISA_DKV_NF, 32><<<grid, 256, 0, st>>>(k);
+    if (s.b == 64) dkv_pc_kernel<D, 64><<<grid, 512, 0, st>>>(k);
+    else dkv_pc_kernel<D, 32><<<grid, 512, 0, st>>>(k);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (s.N_ctx > s.k_ctx) {
