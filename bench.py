@@ -260,6 +260,56 @@ def backward_bench(isa, torch, p, Q, K, V, args):
           flush=True)
 
 
+def measured_peaks(torch, dev):
+    """Achievable peaks on this device: bf16 matrix-core rate from the probe
+    kernel (independent MFMA chains, no memory traffic), HBM read bandwidth
+    of a streaming 16-byte-load kernel over 2 GiB, and HBM bandwidth of a
+    2 GiB device-to-device copy (read + write bytes)."""
+    from block_sparse_attention_blockwise_amd import _build
+    probe = ctypes.CDLL(_build.PROBE_PATH)
+    probe.isa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe.isa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    probe.isa_probe_mfma_flops.restype = ctypes.c_double
+    blocks, iters = 4096, 1024
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rc = probe.isa_probe_mfma_bf16(blocks, iters, out.data_ptr(), sp)
+    if rc != 0:
+        raise RuntimeError(f"probe launch failed: {rc}")
+    e0.record()
+    for _ in range(3):
+        probe.isa_probe_mfma_bf16(blocks, iters, out.data_ptr(), sp)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma_tflops = 3 * probe.isa_probe_mfma_flops(blocks, iters) / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    n = 1 << 30   # 2^30 bf16 = 2 GiB
+    src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    hbm_copy = 5 * 2 * 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    probe.isa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    rblocks = 8192
+    rout = torch.empty(rblocks * 256, dtype=torch.float32, device=dev)
+    rc = probe.isa_probe_read(src.data_ptr(), 2 * n, rblocks, rout.data_ptr(), sp)
+    if rc != 0:
+        raise RuntimeError(f"probe launch failed: {rc}")
+    e0.record()
+    for _ in range(5):
+        probe.isa_probe_read(src.data_ptr(), 2 * n, rblocks, rout.data_ptr(), sp)
+    e1.record()
+    torch.cuda.synchronize()
+    hbm_read = 5 * 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst, out, rout
+    return {"mfma_bf16_tflops": mfma_tflops, "hbm_read_gbs": hbm_read, "hbm_copy_gbs": hbm_copy}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -447,11 +497,14 @@ def main():
 
     sharp_tflops = flops["sharp"] / (per["sharp_attn"] * 1e-3) / 1e12
     rec = traffic_record()
+    peaks = measured_peaks(torch, dev)
     roofline = {"bound": "mfma", "kernel": "isa_sharp_attn (attn_kernel<128,sharp>)",
                 "achieved": sharp_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": sharp_tflops / PEAK_BF16_TFLOPS, "traffic": rec,
                 "algorithmic_flops_per_launch": flops["sharp"],
-                "avg_launch_ms": per["sharp_attn"]}
+                "avg_launch_ms": per["sharp_attn"],
+                "measured_peak": peaks["mfma_bf16_tflops"],
+                "frac_of_measured_peak": sharp_tflops / peaks["mfma_bf16_tflops"]}
     pool_bytes = 3 * BH * (p.L_src + p.L_ctx) * p.D * 2 + BH * pl["N"] * p.D * (8 + 8 + 2 + 2)
     out = {
         "metric": METRIC, "value": step_ms, "unit": "ms", "n_gpus": 1, "steps": args.steps,
@@ -472,6 +525,8 @@ def main():
                       "flat_taylor_attn": (flops["flat_exact"] + flops["taylor"]) /
                       (per["flat_taylor_attn"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "pool_hbm_frac": pool_bytes / (per["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "pool_hbm_frac_of_measured_read": pool_bytes / (per["pool"] * 1e-3) / 1e9 / peaks["hbm_read_gbs"],
+        "measured_peaks": peaks,
         "isa_backward_ms": bwd_ms,
         "rope_pool_ms": rope_ms,
         "rope_pool_hbm_frac": (pool_bytes + 2 * BH * (p.L_src + p.L_ctx) * p.D * 2) /

@@ -19,6 +19,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libisa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# measurement-only probe (achievable matrix-core rate), a library of its own
+PROBE_SOURCES = ["isa_probe.hip"]
+PROBE_PATH = os.path.join(PKG, "libisa_probe.so")
 SOURCES = ["isa_api.cpp", "isa_pool.hip", "isa_select.hip", "isa_attn.hip", "isa_attn_bwd.hip"]
 ARCH = "gfx950"
 
@@ -62,8 +65,16 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB_PATH)
+    pobjs = [_compile(src) for src in PROBE_SOURCES]
+    tmp = PROBE_PATH + ".tmp"
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + pobjs,
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, PROBE_PATH)
     if verbose:
         print(f"built {LIB_PATH}")
+        print(f"built {PROBE_PATH}")
     return LIB_PATH
 
 

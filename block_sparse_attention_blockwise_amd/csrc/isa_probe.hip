@@ -1,0 +1,80 @@
+// Achievable-peak probes for the measurement harness (not part of the ISA
+// operator): a kernel that keeps the bf16 matrix cores busy with
+// independent v_mfma_f32_16x16x32_bf16 chains and touches no memory in its
+// loop (its rate is the matrix-core throughput the chip sustains), and a
+// kernel that streams a large buffer from HBM with 16-byte loads (the read
+// bandwidth it sustains).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define PROBE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef float float4_t __attribute__((__vector_size__(16)));
+
+constexpr int kChains = 8;   // independent accumulators per wave (hide the MFMA latency)
+
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* out) {
+  const int t = threadIdx.x;
+  bf16x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (float)((t + i) & 7));
+    b[i] = (__bf16)(0.002f * (float)((t * 3 + i) & 7));
+  }
+  float4_t c[kChains];
+#pragma unroll
+  for (int k = 0; k < kChains; ++k) c[k] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < kChains; ++k)
+      // accumulate in place: the builtin form made the compiler rotate the
+      // accumulators through register copies on every iteration
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c[k]) : "v"(a), "v"(b));
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < kChains; ++k) s += c[k][0] + c[k][1] + c[k][2] + c[k][3];
+  out[(size_t)blockIdx.x * blockDim.x + t] = s;
+}
+
+// Streams `n16` 16-byte chunks with one load per chunk (grid-stride), adds
+// their words so the loads cannot be dropped, one float per thread to `out`.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src, size_t n16,
+                                                         float* __restrict__ out) {
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  for (size_t i = tid; i < n16; i += stride) {
+    const uint4 w = src[i];
+    acc += w.x ^ w.y ^ w.z ^ w.w;
+  }
+  out[tid] = (float)acc;
+}
+
+}  // namespace
+
+// Reads `bytes` (a multiple of 16) from device memory `src` once with
+// `blocks` workgroups of 256 threads; `out` must hold blocks * 256 floats.
+PROBE_API int isa_probe_read(const void* src, size_t bytes, int blocks, float* out, void* stream) {
+  if (!src || !out || blocks < 1 || bytes % 16) return -1;
+  read_probe_kernel<<<blocks, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      reinterpret_cast<const uint4*>(src), bytes / 16, out);
+  return (int)hipGetLastError();
+}
+
+// Launches `blocks` workgroups of 256 threads, each wave issuing
+// iters * 8 MFMAs of 16x16x32 (16384 flops each); `out` must hold
+// blocks * 256 floats. Returns 0 or the HIP error code.
+PROBE_API int isa_probe_mfma_bf16(int blocks, int iters, float* out, void* stream) {
+  if (blocks < 1 || iters < 1 || !out) return -1;
+  mfma_probe_kernel<<<blocks, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(iters, out);
+  return (int)hipGetLastError();
+}
+
+// Flops one isa_probe_mfma_bf16 launch performs.
+PROBE_API double isa_probe_mfma_flops(int blocks, int iters) {
+  return (double)blocks * 4.0 * iters * kChains * 16.0 * 16.0 * 32.0 * 2.0;
+}
