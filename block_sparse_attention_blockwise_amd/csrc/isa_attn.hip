@@ -168,6 +168,17 @@ __device__ inline SlotSrc slot_src(const TileCtx& c, int t, int slot) {
   return r;
 }
 
+// Key row of `slot` in a plain tile (full kept blocks or full dense tiles,
+// no additive logits). Each wave's 16-byte chunks of one tile fall inside
+// one kept block, so the block's start is read once per wave into a scalar
+// register and the row addresses need no per-lane table lookups or masks.
+template <int MODE>
+__device__ inline int plain_row(const TileCtx& c, int t, int slot) {
+  if (MODE == kDense) return t * kKeyTile + slot;
+  const int e = __builtin_amdgcn_readfirstlane(c.tab[t * c.per + (slot >> c.lb)]);
+  return (e >> 7) + (slot & (c.b - 1));
+}
+
 // Whether tile t carries any non-zero additive logit (uniform over the
 // workgroup).
 template <int MODE>
@@ -495,6 +506,18 @@ void attn_kernel(AttnArgs a) {
     kr[i] = *reinterpret_cast<const uint4*>(ss.k + c8 * 8);                     \
     vr[i] = *reinterpret_cast<const uint4*>(ss.v + c8 * 8);                     \
   }
+#define ISA_LOAD_PLAIN(T)                                                       \
+  _Pragma("unroll") for (int i = 0; i < CH; ++i) {                              \
+    const size_t row = (size_t)plain_row<MODE>(tc, (T), (tid + i * NT) / CPR);  \
+    kr[i] = *reinterpret_cast<const uint4*>(tc.K + row * D + c8 * 8);           \
+    vr[i] = *reinterpret_cast<const uint4*>(tc.V + row * D + c8 * 8);           \
+  }
+#define ISA_STORE_PLAIN(KB, VB)                                                 \
+  _Pragma("unroll") for (int i = 0; i < CH; ++i) {                              \
+    const int slot = (tid + i * NT) / CPR;                                      \
+    *reinterpret_cast<uint4*>(&k_lds[(KB)][slot * KSTR + c8 * 16]) = kr[i];     \
+    *reinterpret_cast<uint4*>(&v_lds[(VB)][slot * VSTR + c8 * 16]) = vr[i];     \
+  }
 #define ISA_STORE_TILE(KB, VB)                                                  \
   _Pragma("unroll") for (int i = 0; i < CH; ++i) {                              \
     const int slot = (tid + i * NT) / CPR;                                      \
@@ -565,11 +588,11 @@ void attn_kernel(AttnArgs a) {
     const int P = a.ntiles_plain;
     if (P > 0) {
       // Prologue: tiles 0 and 1 in LDS, scores of tile 0 in registers.
-      ISA_LOAD_TILE(0)
-      ISA_STORE_TILE(0, 0)
+      ISA_LOAD_PLAIN(0)
+      ISA_STORE_PLAIN(0, 0)
       if (P > 1) {
-        ISA_LOAD_TILE(1)
-        ISA_STORE_TILE(1, 1)
+        ISA_LOAD_PLAIN(1)
+        ISA_STORE_PLAIN(1, 1)
       }
       __syncthreads();
       float4_t scur[QT][4], snext[QT][4];
@@ -580,7 +603,7 @@ void attn_kernel(AttnArgs a) {
       for (int t = 0; t < P; ++t) {
         __syncthreads();
         const bool more2 = t + 2 < P;
-        if (more2) { ISA_LOAD_TILE(t + 2) }
+        if (more2) { ISA_LOAD_PLAIN(t + 2) }
         rescale<D, QT>(mx, m, lsum, oacc);
         // matrix cores: scores of tile t+1 (stale data on the last tile,
         // unused); vector ALUs meanwhile: probabilities of tile t. The group
@@ -615,7 +638,7 @@ void attn_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
           __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
         }
-        if (more2) { ISA_STORE_TILE(t & 1, vb_load) }
+        if (more2) { ISA_STORE_PLAIN(t & 1, vb_load) }
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -643,6 +666,8 @@ void attn_kernel(AttnArgs a) {
   }
 #undef ISA_LOAD_TILE
 #undef ISA_STORE_TILE
+#undef ISA_LOAD_PLAIN
+#undef ISA_STORE_PLAIN
 
   // ---- normalise and write the owned rows
 #pragma unroll
