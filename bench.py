@@ -55,6 +55,8 @@ def parse():
                     help="launch only this kernel --steps times (for counter collection)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="131072-token grid of (b, alpha_s, alpha_ns, alpha_f) against dense attention")
     ap.add_argument("--backward", action="store_true",
                     help="time isa_forward + isa_backward (and the dense configuration on the same kernels)")
     ap.add_argument("--fig6", action="store_true",
@@ -310,6 +312,64 @@ def measured_peaks(torch, dev):
     return {"mfma_bf16_tflops": mfma_tflops, "hbm_read_gbs": hbm_read, "hbm_copy_gbs": hbm_copy}
 
 
+def sweep_128k(isa, torch, dev, args):
+    """The 131072-token grid (b, alpha_s, alpha_ns, alpha_f) against dense
+    attention at the same length, H = 40, D = 128. Every block is full at this
+    length, so the work of each point is fixed by its ratios; four generated
+    heads are tiled over the 40 head slots."""
+    import isa_inputs
+    Ls = Lc = 65536
+    H, D = 40, 128
+    L = Ls + Lc
+    gen = 4
+    T = {n: torch.empty((1, H, L, D), dtype=torch.bfloat16, device=dev) for n in "QKV"}
+    for h in range(gen):
+        qkv = isa_inputs.make_head(5, 0, h, Ls, Lc, D)
+        for n, x in zip("QKV", qkv):
+            bits, _ = isa_inputs.round_to_bf16(x)
+            T[n][0, h].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+    for h in range(gen, H):
+        for n in "QKV":
+            T[n][0, h].copy_(T[n][0, h % gen])
+    Q, K, V = T["Q"], T["K"], T["V"]
+    O = torch.empty_like(Q)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    dense_ms = timed(lambda: isa.dense_attn(Q, K, V, out=O), 2)
+    dense_flop = 4 * D * L * L * H
+    rows = []
+    for b in (64, 32):
+        for a_s in (0.125, 0.25):
+            for a_ns in (0.0625, 0.125):
+                for a_f in (0.25, 0.5, 0.75):
+                    p = isa.Params(1, H, Ls, Lc, D, b, a_s, a_f, a_ns)
+                    pl = isa.plan(p)
+                    ws = isa.workspace(p, dev)
+                    ms = timed(lambda: isa.forward(Q, K, V, p, out=O, workspace=ws), 3)
+                    del ws
+                    nf, ns, nkv, kns = pl["n_flat"], pl["n_sharp"], pl["N_kv"], pl["k_ns"]
+                    flop = H * (4 * D * (ns * b) * (nkv * b) + 4 * D * (nf * b) * (kns * b)
+                                + 4 * D * (nf * b) * (nkv - kns) + 2 * D * pl["N"] * nkv)
+                    rows.append({"b": b, "alpha_s": a_s, "alpha_ns": a_ns, "alpha_f": a_f, "ms": ms,
+                                 "alg_tflop": flop / 1e12, "tflops": flop / (ms * 1e-3) / 1e12,
+                                 "speedup_vs_dense": dense_ms / ms, "ceiling": dense_flop / flop})
+                    log(f"sweep b={b} a_s={a_s} a_ns={a_ns} a_f={a_f}: {ms:.1f} ms, "
+                        f"{dense_ms / ms:.2f}x (ceiling {dense_flop / flop:.2f}x)")
+    print(json.dumps({"sweep_128k": rows, "dense_ms": dense_ms,
+                      "dense_tflops": dense_flop / (dense_ms * 1e-3) / 1e12,
+                      "config": {"workload": "isa_fwd_128k_tokens_h40_d128_grid"}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -320,6 +380,9 @@ def main():
     import block_sparse_attention_blockwise_amd as isa
 
     dev = torch.device("cuda:0")
+    if args.sweep:
+        sweep_128k(isa, torch, dev, args)
+        return
     if args.copy_calibration:
         n = 1 << 29   # 2^29 bf16 = 1 GiB
         src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
