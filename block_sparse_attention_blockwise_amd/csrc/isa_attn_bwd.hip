@@ -14,7 +14,8 @@
 //
 // Kernels (all deterministic: every sum has a fixed order, no float atomics):
 //   * bwd_prep_kernel: per head, a bitmap of E_i over the positions of J and,
-//     for every kept block, the ascending list of flat blocks whose E_i holds it;
+//     for every kept block, the ascending list of flat blocks whose E_i holds
+//     it (filled in order from the bitmap, linear in the number of blocks);
 //   * delta_kernel: Delta_t for every row;
 //   * dq_kernel (query-major, as the forward): per query block, over the key
 //     tiles the forward used; S^T = K Q^T and dP^T = V dO^T on the matrix
@@ -206,8 +207,11 @@ __device__ inline void store4(uint16_t* row, int d0, float4_t v, const float2* r
 }
 
 // ---------------------------------------------------------------- prep
-// One workgroup per head: E bitmap, then the per-position lists of flat
-// blocks that read a kept block exactly (ascending block ids).
+// One workgroup per head: the E bitmap (one row of ceil(N_kv/64) words per
+// flat block), the count of flat blocks per kept position, their offsets,
+// and then each position's list of flat blocks, filled in ascending order by
+// one thread walking the bitmap column (linear in n_flat, no sort, so the
+// order is fixed however many flat blocks share a position).
 constexpr int kPrepThreads = 1024;
 
 __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
@@ -220,7 +224,6 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
   int32_t* off = const_cast<int32_t*>(a.inv_off) + (size_t)bh * (s.N_kv + 1);
   int32_t* lst = const_cast<int32_t*>(a.inv_list) + (size_t)bh * s.n_flat * s.k_ns;
   __shared__ int cnt[ISA_MAX_NKV + 1];
-  __shared__ int cur[ISA_MAX_NKV];
   __shared__ int part[kPrepThreads];
   for (int p = tid; p <= s.N_kv; p += kPrepThreads) cnt[p] = 0;
   __syncthreads();
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
     for (int q = 0; q < s.k_ns; ++q) {
       const int p = kept_pos(s, ctx_row, ex[(size_t)r * s.k_ns + q]);
       if (p < 0) continue;
-      atomicAdd(&cnt[p], 1);
+      atomicAdd(&cnt[p], 1);   // integer count: the result does not depend on the order
       if ((p >> 6) != cw) {
         if (cw >= 0) brow[cw] = word;
         cw = p >> 6;
@@ -261,34 +264,27 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
   __syncthreads();
   int acc = part[tid];
   for (int p = p0; p < p1; ++p) {
-    const int v = cnt[p];
     off[p] = acc;
-    cur[p] = acc;
-    acc += v;
+    acc += cnt[p];
   }
   if (tid == kPrepThreads - 1) off[s.N_kv] = part[tid] + sum;
   __syncthreads();
-  for (int r = tid; r < s.n_flat; r += kPrepThreads) {
-    for (int q = 0; q < s.k_ns; ++q) {
-      const int p = kept_pos(s, ctx_row, ex[(size_t)r * s.k_ns + q]);
-      if (p < 0) continue;
-      const int slot = atomicAdd(&cur[p], 1);
-      lst[slot] = frow[r];
-    }
-  }
-  __syncthreads();
-  // the slots were taken in arbitrary order: sort each list ascending
+  // each position's flat blocks in ascending order: walk the bitmap column
   for (int p = tid; p < s.N_kv; p += kPrepThreads) {
-    const int b0 = off[p], b1 = cur[p];
-    for (int x = b0 + 1; x < b1; ++x) {
-      const int v = lst[x];
-      int y = x - 1;
-      while (y >= b0 && lst[y] > v) {
-        lst[y + 1] = lst[y];
-        --y;
-      }
-      lst[y + 1] = v;
+    int k = off[p];
+    const uint64_t bit = 1ull << (p & 63);
+    const uint64_t* col = bits + (p >> 6);
+    int r = 0;
+    for (; r + 8 <= s.n_flat; r += 8) {
+      uint64_t w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = col[(size_t)(r + u) * a.W];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (w[u] & bit) lst[k++] = frow[r + u];
     }
+    for (; r < s.n_flat; ++r)
+      if (col[(size_t)r * a.W] & bit) lst[k++] = frow[r];
   }
 }
 

@@ -233,3 +233,34 @@ def test_backward_64k_workload(dev):
         got = dQ[0, h, torch.from_numpy(rows).to(dev)].float().cpu().numpy()
         log(f"head {h}")
         _compare("dQ rows", got, ref)
+
+
+def test_backward_block_shared_by_every_exact_set(dev):
+    """One kept block that every flat block reads exactly (every query shares
+    a component its keys point along): its list of flat blocks holds all of
+    them, the longest the backward's inverse lists can get. Every gradient
+    element against the oracle."""
+    p = isa.Params(1, 2, 6400, 6400, 64, 64, 0.25, 0.5, 0.125)
+    inp = isa_inputs.make_inputs(1, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    rng = np.random.default_rng(123)
+    for h in range(p.H):
+        u = rng.standard_normal(p.D).astype(np.float32)
+        u /= np.linalg.norm(u)
+        q = inp["Q"][1][0, h].astype(np.float32) + 2.0 * u[None, :]    # a component every query shares
+        k = inp["K"][1][0, h].astype(np.float32).copy()
+        k[:64] = 6.0 * u[None, :] + 0.1 * k[:64]                        # block 0 points along it
+        for name, x in (("Q", q), ("K", k)):
+            bits, val = isa_inputs.round_to_bf16(x)
+            inp[name][0][0, h] = bits
+            inp[name][1][0, h] = val
+    dO_bits, dO_vals = _dO(p, 5)
+    res = _run(p, inp, dO_bits, dev)
+    E = res["sel"]["flat_exact_idx"]
+    assert (E[0] == 0).any(axis=-1).all(), "block 0 must be in every exact set"
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    for h in range(p.H):
+        log(f"head {h}")
+        gq, gk, gv = _oracle_grads(plan, inp, dO_vals, 0, h, res["sel"])
+        _compare("dQ", res["dQ"][0, h], gq)
+        _compare("dK", res["dK"][0, h], gk)
+        _compare("dV", res["dV"][0, h], gv)
