@@ -12,6 +12,8 @@
 #include <cstdint>
 #include <cstring>
 
+#include <initializer_list>
+
 #include "isa_internal.h"
 
 namespace {
@@ -126,6 +128,13 @@ int hip_status(hipError_t e) { return e == hipSuccess ? ISA_OK : ISA_ERR_HIP; }
 
 hipStream_t as_stream(void* st) { return reinterpret_cast<hipStream_t>(st); }
 
+// The kernels move token rows and workspace data in 16-byte vectors.
+bool aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* q : ptrs)
+    if (reinterpret_cast<uintptr_t>(q) & 15u) return false;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,7 +157,7 @@ int isa_pool_coarse(const isa_params_t* p, const void* Q, const void* K, const v
   IsaShape s;
   int rc = make_shape(p, &s);
   if (rc != ISA_OK) return rc;
-  if (!Q || !K || !V || !qc || !kc) return ISA_ERR_ARG;
+  if (!Q || !K || !V || !qc || !kc || !aligned16({Q, K, V})) return ISA_ERR_ARG;
   return hip_status(isa_launch_pool(s, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V,
                                     qc, kc, (uint16_t*)kc_bf16, (uint16_t*)vc_bf16,
                                     as_stream(stream)));
@@ -161,6 +170,7 @@ int isa_rope_pool_coarse(const isa_params_t* p, const void* Q, const void* K, co
   int rc = make_shape(p, &s);
   if (rc != ISA_OK) return rc;
   if (!Q || !K || !V || !Qr || !Kr || !qc || !kc || !ws || s.rope_base == 0.0) return ISA_ERR_ARG;
+  if (!aligned16({Q, K, V, Qr, Kr, ws})) return ISA_ERR_ARG;
   if (ws_bytes < rope_table_bytes(s)) return ISA_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
   float2* table = (float2*)ws;
@@ -209,6 +219,7 @@ int isa_sharp_attn(const isa_params_t* p, const void* Q, const void* K, const vo
   if (rc != ISA_OK) return rc;
   if (!Q || !K || !V || !O || (!ctx_idx && s.k_ctx > 0) || (!sharp_idx && s.n_sharp > 0))
     return ISA_ERR_ARG;
+  if (!aligned16({Q, K, V, O})) return ISA_ERR_ARG;
   return hip_status(isa_launch_sharp_attn(s, (const uint16_t*)Q, (const uint16_t*)K,
                                           (const uint16_t*)V, ctx_idx, sharp_idx, (uint16_t*)O, nullptr,
                                           as_stream(stream)));
@@ -224,6 +235,7 @@ int isa_flat_taylor_attn(const isa_params_t* p, const void* Q, const void* K, co
   if (!Q || !K || !V || !O || !kc_bf16 || !vc_bf16 || (!ctx_idx && s.k_ctx > 0) ||
       (!flat_idx && s.n_flat > 0) || (!flat_exact_idx && s.n_flat > 0 && s.k_ns > 0))
     return ISA_ERR_ARG;
+  if (!aligned16({Q, K, V, O, kc_bf16, vc_bf16})) return ISA_ERR_ARG;
   return hip_status(isa_launch_flat_attn(s, (const uint16_t*)Q, (const uint16_t*)K,
                                          (const uint16_t*)V, (const uint16_t*)kc_bf16,
                                          (const uint16_t*)vc_bf16, ctx_idx, flat_idx,
@@ -253,7 +265,7 @@ int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void*
   IsaShape s;
   int rc = make_shape(p, &s);
   if (rc != ISA_OK) return rc;
-  if (!Q || !K || !V || !O || !ws) return ISA_ERR_ARG;
+  if (!Q || !K || !V || !O || !ws || !aligned16({Q, K, V, O, ws})) return ISA_ERR_ARG;
   const Layout l = make_layout(s);
   if (ws_bytes < l.total) return ISA_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
@@ -323,6 +335,7 @@ int isa_backward(const isa_params_t* p, const void* Q, const void* K, const void
   int rc = make_shape(p, &s);
   if (rc != ISA_OK) return rc;
   if (!Q || !K || !V || !O || !dO || !dQ || !dK || !dV || !ws) return ISA_ERR_ARG;
+  if (!aligned16({Q, K, V, O, dO, dQ, dK, dV, ws})) return ISA_ERR_ARG;
   const Layout l = make_layout(s);
   if (ws_bytes < l.total) return ISA_ERR_WORKSPACE;
   char* w = (char*)ws;
@@ -364,6 +377,7 @@ int isa_backward(const isa_params_t* p, const void* Q, const void* K, const void
 int isa_dense_attn(int32_t B, int32_t H, int32_t L, int32_t D, const void* Q, const void* K,
                    const void* V, void* O, void* stream) {
   if (B < 1 || H < 1 || L < 1 || D < 1 || !Q || !K || !V || !O) return ISA_ERR_ARG;
+  if (!aligned16({Q, K, V, O})) return ISA_ERR_ARG;
   if (D != 64 && D != 128) return ISA_ERR_UNSUPPORTED;
   return hip_status(isa_launch_dense_attn(B, H, L, D, (const uint16_t*)Q, (const uint16_t*)K,
                                           (const uint16_t*)V, (uint16_t*)O, as_stream(stream)));

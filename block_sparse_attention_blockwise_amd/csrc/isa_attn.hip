@@ -694,9 +694,10 @@ hipError_t launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
   if (MODE == kFlat) {
     dyn = (size_t)(a.s.k_ns + a.s.N_kv) * sizeof(int);
     // Raise the dynamic LDS limit once per instantiation (host-side only).
-    static hipError_t attr = hipFuncSetAttribute(
+    static unsigned long long done = 0;
+    const hipError_t attr = isa_ensure_dyn_lds(
         reinterpret_cast<const void*>(&attn_kernel<D, MODE, QT, NWAVES, LOOP>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * ISA_MAX_NKV * sizeof(int)));
+        (int)(2 * ISA_MAX_NKV * sizeof(int)), &done);
     if (attr != hipSuccess) return attr;
   }
   attn_kernel<D, MODE, QT, NWAVES, LOOP><<<grid, NWAVES * 64, dyn, st>>>(a);

@@ -1074,9 +1074,8 @@ __global__ __launch_bounds__(256) void dkv_pooled_kernel(BwdArgs a) {
 }
 
 template <typename F>
-hipError_t set_dyn_lds(F* kernel, int bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+hipError_t set_dyn_lds(F* kernel, int bytes, unsigned long long* done) {
+  return isa_ensure_dyn_lds(reinterpret_cast<const void*>(kernel), bytes, done);
 }
 
 template <int D>
@@ -1139,7 +1138,8 @@ const int kpb = 128 / s.b;   // 128 keys per workgroup
     constexpr int ROWS = 8 * 32;   // 8 waves of 32 rows
     dim3 grid((s.n_sharp + ROWS / s.b - 1) / (ROWS / s.b), BH);
     const size_t dyn = (size_t)s.N_kv * sizeof(int);
-    static hipError_t attr = set_dyn_lds(&dq_kernel<D, kSharp, 2, 8, true>, max_dyn);
+    static unsigned long long done = 0;
+    const hipError_t attr = set_dyn_lds(&dq_kernel<D, kSharp, 2, 8, true>, max_dyn, &done);
     if (attr != hipSuccess) return attr;
     dq_kernel<D, kSharp, 2, 8, true><<<grid, 512, dyn, st>>>(q);
     e = hipGetLastError();
@@ -1154,11 +1154,13 @@ const int kpb = 128 / s.b;   // 128 keys per workgroup
     dim3 grid(s.n_flat, BH);
     const size_t dyn = (size_t)(s.k_ns + s.N_kv) * sizeof(int);
     if (s.b == 64) {
-      static hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 1, 4, false>, max_dyn);
+      static unsigned long long done = 0;
+      const hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 1, 4, false>, max_dyn, &done);
       if (attr != hipSuccess) return attr;
       dq_kernel<D, kFlat, 1, 4, false><<<grid, 256, dyn, st>>>(q);
     } else {
-      static hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 1, 2, false>, max_dyn);
+      static unsigned long long done = 0;
+      const hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 1, 2, false>, max_dyn, &done);
       if (attr != hipSuccess) return attr;
       dq_kernel<D, kFlat, 1, 2, false><<<grid, 128, dyn, st>>>(q);
     }

@@ -30,6 +30,19 @@ __host__ __device__ inline void isa_block_range(const IsaShape& s, int j, int& s
   }
 }
 
+// Raises a kernel's dynamic-LDS limit on the current device, once per device
+// (the attribute is per device; `done` is a per-kernel bit set of devices).
+inline hipError_t isa_ensure_dyn_lds(const void* kernel, int bytes, unsigned long long* done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = 1ull << (dev & 63);
+  if (__atomic_load_n(done, __ATOMIC_ACQUIRE) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) __atomic_fetch_or(done, bit, __ATOMIC_RELEASE);
+  return e;
+}
+
 // Hard limits of the kernels (see isa.h).
 constexpr int ISA_MAX_SEG_BLOCKS = 4096;
 constexpr int ISA_MAX_NKV = 4096;

@@ -147,6 +147,14 @@ def test_calls_fail_before_launch(isa):
     assert L.isa_dense_attn(1, 1, 0, 128, fake, fake, fake, fake, None) == -1
     assert L.isa_dense_attn(1, 1, 16, 96, fake, fake, fake, fake, None) == -2
     assert L.isa_dense_attn(1, 1, 16, 128, None, fake, fake, fake, None) == -1
+    # 16-byte alignment of the vector-accessed tensors
+    odd = fake + 8
+    assert L.isa_forward(ctypes.byref(p), odd, fake, fake, fake, fake, 1 << 40, None, None) == -1
+    assert L.isa_backward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, odd, fake, fake,
+                          1 << 40, None) == -1
+    assert L.isa_sharp_attn(ctypes.byref(p), fake, fake, fake, fake, fake, odd, None) == -1
+    assert L.isa_dense_attn(1, 1, 16, 128, fake, odd, fake, fake, None) == -1
+    assert L.isa_pool_coarse(ctypes.byref(p), fake, fake, odd, fake, fake, None, None, None) == -1
     bad = _params(isa, D=96)
     assert L.isa_forward(ctypes.byref(bad), fake, fake, fake, fake, fake, 1 << 40, None, None) == -2
 
