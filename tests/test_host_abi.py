@@ -172,3 +172,35 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(isa, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         isa.lib()
+
+
+def test_header_is_plain_c_and_links(isa, tmp_path):
+    """include/isa.h compiles as C99 on its own, and a C program linked
+    against the library can plan a forward pass and read status strings (no
+    GPU needed)."""
+    src = tmp_path / "client.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "isa.h"
+int main(void) {
+  isa_params_t p = {1, 40, 32768, 32768, 128, 64, 0.125, 0.5, 0.0625, 0.0, 0.0};
+  isa_plan_t pl;
+  int rc = isa_plan(&p, &pl);
+  if (rc != ISA_OK) { printf("plan failed: %s\n", isa_strerror(rc)); return 1; }
+  printf("%d %d %d %d %d %d %zu\n", pl.N, pl.k_ctx, pl.N_kv, pl.n_flat, pl.n_sharp, pl.k_ns,
+         pl.workspace_bytes);
+  p.D = 96;
+  return isa_plan(&p, &pl) == ISA_ERR_UNSUPPORTED ? 0 : 2;
+}
+''')
+    exe = tmp_path / "client"
+    lib_dir = os.path.dirname(isa.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-L", lib_dir, "-lisa_mi355x", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    N, k_ctx, N_kv, n_flat, n_sharp, k_ns, ws = (int(x) for x in r.stdout.split())
+    assert (N, k_ctx, N_kv, n_flat, n_sharp, k_ns) == (1024, 64, 576, 512, 512, 36)
+    assert ws > 0
