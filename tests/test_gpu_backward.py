@@ -173,6 +173,13 @@ def test_backward_residual_sums(dev):
         assert (np.abs(sv - so) <= 0.02 * np.abs(r["dV"][0, h]).sum(0) + 1e-3).all()
 
 
+def test_backward_with_rope_and_residual(dev):
+    """RoPE and the residual together (b = 32, D = 64): every gradient of the
+    unrotated Q, K and of V against the oracle."""
+    p = isa.Params(1, 2, 700, 451, 64, 32, 0.25, 0.5, 0.125, 0.3, rope_base=10000.0)
+    _check_all_rows(p)
+
+
 def test_backward_with_rope(dev):
     """RoPE on: the gradients of the unrotated Q, K (oracle: the backward on
     the rotated tensors, then the transposed rotation)."""
