@@ -657,6 +657,9 @@ void dq_kernel(BwdArgs a) {
   auto consume = [&](int buf) {
     float4_t sc[QT][4], dp[QT][4];
     mm_rows<D, 4, QT>(k_lds[buf], qf, sc, g, c16);
+    // the probabilities need only S: the vector ALUs form them while the
+    // matrix cores compute dP (group barriers interleave one MFMA with six
+    // VALU ops)
     mm_rows<D, 4, QT>(v_lds[buf], df, dp, g, c16);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -664,11 +667,20 @@ void dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][mt][e], cscale, bv[e]) - lse2[qt]);
-          sc[qt][mt][e] = p * (dp[qt][mt][e] - dl[qt]);
-        }
+        for (int e = 0; e < 4; ++e)
+          sc[qt][mt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][mt][e], cscale, bv[e]) - lse2[qt]);
     }
+#pragma unroll
+    for (int i = 0; i < 4 * QT * 4 / 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[qt][mt][e] = sc[qt][mt][e] * (dp[qt][mt][e] - dl[qt]);
     bf16x8_t pk[QT][2];
     pack_bf16<4, QT>(sc, pk);
     mm_tr<D, 4, QT>(k_lds[buf], pk, dq, g, c16);
