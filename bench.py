@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "ISA fwd latency (ms) + effective TFLOP/s & MFMA util at 64K tokens, H=40, D=128"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-WORKLOAD = dict(cfg_id=4, B=1, H=40, L_src=32768, L_ctx=32768, D=128, b=64,
+WORKLOAD = dict(stream=4, B=1, H=40, L_src=32768, L_ctx=32768, D=128, b=64,
                 alpha_s=0.125, alpha_f=0.5, alpha_ns=0.0625)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sharp_attn_64k_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_blockwise_amd", "csrc", "isa_attn.hip")
@@ -75,7 +75,7 @@ def make_inputs(dev):
     host = {}
     for bi in range(w["B"]):
         for h in range(w["H"]):
-            qkv = isa_inputs.make_head(w["cfg_id"], bi, h, w["L_src"], w["L_ctx"], w["D"])
+            qkv = isa_inputs.make_head(w["stream"], bi, h, w["L_src"], w["L_ctx"], w["D"])
             for n, x in zip("QKV", qkv):
                 bits, val = isa_inputs.round_to_bf16(x)
                 out[n][bi, h].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
@@ -324,7 +324,7 @@ def sweep_128k(isa, torch, dev, args):
     gen = 4
     T = {n: torch.empty((1, H, L, D), dtype=torch.bfloat16, device=dev) for n in "QKV"}
     for h in range(gen):
-        qkv = isa_inputs.make_head(5, 0, h, Ls, Lc, D)
+        qkv = isa_inputs.make_head(isa_inputs.WORKLOADS["128k"]["stream"], 0, h, Ls, Lc, D)
         for n, x in zip("QKV", qkv):
             bits, _ = isa_inputs.round_to_bf16(x)
             T[n][0, h].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))

@@ -59,13 +59,14 @@ def _segment_blocks(L_src: int, L_ctx: int, g: int):
     return out
 
 
-def make_head(cfg_id: int, b_idx: int, h: int, L_src: int, L_ctx: int, D: int):
+def make_head(stream: int, b_idx: int, h: int, L_src: int, L_ctx: int, D: int):
     """Generate fp32 (Q, K, V) of shape [L, D] for one (batch, head).
 
-    Stream: numpy default_rng([cfg_id, b_idx, h]); each head can be
+    Stream: numpy default_rng([stream, b_idx, h]) (`stream` is the
+    workload's seed stream, WORKLOADS[name]["stream"]); each head can be
     regenerated on its own.
     """
-    rng = np.random.default_rng([cfg_id, b_idx, h])
+    rng = np.random.default_rng([stream, b_idx, h])
     L = L_src + L_ctx
     centres = rng.standard_normal((N_CENTRES, D)).astype(np.float32)
     blocks = _segment_blocks(L_src, L_ctx, GEN_BLOCK)
@@ -86,7 +87,7 @@ def make_head(cfg_id: int, b_idx: int, h: int, L_src: int, L_ctx: int, D: int):
     return Q.astype(np.float32), K.astype(np.float32), V
 
 
-def make_inputs(cfg_id: int, B: int, H: int, L_src: int, L_ctx: int, D: int,
+def make_inputs(stream: int, B: int, H: int, L_src: int, L_ctx: int, D: int,
                 heads=None, bf16: bool = True):
     """Generate Q, K, V as [B, H, L, D] arrays.
 
@@ -105,7 +106,7 @@ def make_inputs(cfg_id: int, B: int, H: int, L_src: int, L_ctx: int, D: int,
         for nm in names:
             out[nm] = np.zeros((B, H, L, D), np.float32)
     for (b, h) in sel:
-        qkv = make_head(cfg_id, b, h, L_src, L_ctx, D)
+        qkv = make_head(stream, b, h, L_src, L_ctx, D)
         for nm, x in zip(names, qkv):
             if bf16:
                 bits, val = round_to_bf16(x)
@@ -116,12 +117,13 @@ def make_inputs(cfg_id: int, B: int, H: int, L_src: int, L_ctx: int, D: int,
     return out
 
 
-# Workload shapes (B, H, D, L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns).
+# Workload shapes (B, H, D, L_src, L_ctx, b, alpha_s, alpha_f, alpha_ns) and
+# the seed stream each one's inputs are drawn from.
 DEFAULT_RATIOS = dict(alpha_s=0.125, alpha_f=0.5, alpha_ns=0.0625)
-CONFIGS = {
-    1: dict(name="tiny", B=1, H=2, D=64, L_src=1024, L_ctx=1024, b=64, **DEFAULT_RATIOS),
-    2: dict(name="16k", B=1, H=40, D=128, L_src=8192, L_ctx=8192, b=64, **DEFAULT_RATIOS),
-    3: dict(name="23768-ragged", B=1, H=40, D=128, L_src=11884, L_ctx=11884, b=64, **DEFAULT_RATIOS),
-    4: dict(name="64k", B=1, H=40, D=128, L_src=32768, L_ctx=32768, b=64, **DEFAULT_RATIOS),
-    5: dict(name="128k", B=1, H=40, D=128, L_src=65536, L_ctx=65536, b=64, **DEFAULT_RATIOS),
+WORKLOADS = {
+    "tiny": dict(stream=1, B=1, H=2, D=64, L_src=1024, L_ctx=1024, b=64, **DEFAULT_RATIOS),
+    "16k": dict(stream=2, B=1, H=40, D=128, L_src=8192, L_ctx=8192, b=64, **DEFAULT_RATIOS),
+    "23768_ragged": dict(stream=3, B=1, H=40, D=128, L_src=11884, L_ctx=11884, b=64, **DEFAULT_RATIOS),
+    "64k": dict(stream=4, B=1, H=40, D=128, L_src=32768, L_ctx=32768, b=64, **DEFAULT_RATIOS),
+    "128k": dict(stream=5, B=1, H=40, D=128, L_src=65536, L_ctx=65536, b=64, **DEFAULT_RATIOS),
 }

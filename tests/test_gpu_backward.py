@@ -22,6 +22,8 @@ import isa_inputs
 from oracle import isa_oracle
 from parity_util import bf16_tensor
 
+STREAM = {name: w["stream"] for name, w in isa_inputs.WORKLOADS.items()}
+
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
@@ -91,8 +93,8 @@ def _oracle_grads(plan, inp, dO_vals, bi, h, sel, gamma=0.0, rope_base=0.0):
     return gq, gk, gv
 
 
-def _check_all_rows(p, cfg_id=1, seed=0, heads=None):
-    inp = isa_inputs.make_inputs(cfg_id, p.B, p.H, p.L_src, p.L_ctx, p.D)
+def _check_all_rows(p, stream=1, seed=0, heads=None):
+    inp = isa_inputs.make_inputs(stream, p.B, p.H, p.L_src, p.L_ctx, p.D)
     dO_bits, dO_vals = _dO(p, seed)
     res = _run(p, inp, dO_bits, torch.device("cuda:0"))
     plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
@@ -135,7 +137,7 @@ def test_backward_closed_form_sums_and_determinism(dev):
     zero (within the rounding of the bf16 gradients); two calls give the same
     bits."""
     p = isa.Params(1, 4, 1500, 1300, 128, 64, 0.25, 0.5, 0.125)
-    inp = isa_inputs.make_inputs(1, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    inp = isa_inputs.make_inputs(STREAM["tiny"], p.B, p.H, p.L_src, p.L_ctx, p.D)
     dO_bits, dO_vals = _dO(p, 3)
     r1 = _run(p, inp, dO_bits, dev)
     r2 = _run(p, inp, dO_bits, dev)
@@ -164,7 +166,7 @@ def test_backward_residual_sums(dev):
     rows (each coarse softmax row sums to one too)."""
     gamma = 0.4
     p = isa.Params(1, 2, 1500, 1300, 128, 64, 0.25, 0.5, 0.125, gamma)
-    inp = isa_inputs.make_inputs(1, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    inp = isa_inputs.make_inputs(STREAM["tiny"], p.B, p.H, p.L_src, p.L_ctx, p.D)
     dO_bits, dO_vals = _dO(p, 4)
     r = _run(p, inp, dO_bits, dev)
     for h in range(p.H):
@@ -190,10 +192,10 @@ def test_backward_with_rope(dev):
 def test_backward_16k_workload(dev):
     """16K-token workload (H = 40, D = 128, b = 64, default ratios): two heads
     against the oracle element by element, every head through the sums."""
-    c = isa_inputs.CONFIGS[2]
+    c = isa_inputs.WORKLOADS["16k"]
     p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"])
     log("16k backward")
-    res, _ = _check_all_rows(p, cfg_id=2, heads=[(0, 0), (0, 39)])
+    res, _ = _check_all_rows(p, stream=STREAM["16k"], heads=[(0, 0), (0, 39)])
     _, dO_vals = _dO(p, 0)
     for h in range(p.H):
         sv, so, sk = res["dV"][0, h].sum(0), dO_vals[0, h].sum(0), res["dK"][0, h].sum(0)
@@ -206,9 +208,9 @@ def test_backward_64k_workload(dev):
     launch configuration the benchmark times: dQ of sampled rows (segment and
     tail edges included) of three heads against the oracle row by row, and
     the gradient sums of every head."""
-    c = isa_inputs.CONFIGS[4]
+    c = isa_inputs.WORKLOADS["64k"]
     p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"])
-    inp = isa_inputs.make_inputs(4, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    inp = isa_inputs.make_inputs(STREAM["64k"], p.B, p.H, p.L_src, p.L_ctx, p.D)
     dO_bits, dO_vals = _dO(p, 9)
     log("64k backward")
     Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
@@ -248,7 +250,7 @@ def test_backward_block_shared_by_every_exact_set(dev):
     them, the longest the backward's inverse lists can get. Every gradient
     element against the oracle."""
     p = isa.Params(1, 2, 6400, 6400, 64, 64, 0.25, 0.5, 0.125)
-    inp = isa_inputs.make_inputs(1, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    inp = isa_inputs.make_inputs(STREAM["tiny"], p.B, p.H, p.L_src, p.L_ctx, p.D)
     rng = np.random.default_rng(123)
     for h in range(p.H):
         u = rng.standard_normal(p.D).astype(np.float32)

@@ -16,6 +16,8 @@ import isa_inputs
 from oracle import isa_oracle
 from parity_util import bf16_tensor, compare_head
 
+STREAM = {name: w["stream"] for name, w in isa_inputs.WORKLOADS.items()}
+
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
@@ -34,13 +36,13 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _inputs(cfg_id, p, heads=None, tile_heads=False):
+def _inputs(stream, p, heads=None, tile_heads=False):
     """bf16 inputs [B,H,L,D]. With tile_heads, only `heads` are generated and
     copied round-robin into the other head slots (the launch shape stays the
     full one; only the listed heads are checked)."""
     if not tile_heads:
-        return isa_inputs.make_inputs(cfg_id, p.B, p.H, p.L_src, p.L_ctx, p.D)
-    gen = isa_inputs.make_inputs(cfg_id, p.B, p.H, p.L_src, p.L_ctx, p.D, heads=heads)
+        return isa_inputs.make_inputs(stream, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    gen = isa_inputs.make_inputs(stream, p.B, p.H, p.L_src, p.L_ctx, p.D, heads=heads)
     for nm in "QKV":
         bits, val = gen[nm]
         for bi in range(p.B):
@@ -95,24 +97,24 @@ def _check(p, inp, res, out_heads, rows_per_head, seed=0, all_sel=True):
 
 # ------------------------------------------------------------- workloads
 def test_tiny_all_rows(dev):
-    c = isa_inputs.CONFIGS[1]
+    c = isa_inputs.WORKLOADS["tiny"]
     p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"])
-    inp = _inputs(1, p)
+    inp = _inputs(STREAM["tiny"], p)
     log("tiny: forward")
     res = _run(p, inp, dev)
     _check(p, inp, res, {(0, 0), (0, 1)}, None)
 
 
-@pytest.mark.parametrize("cfg_id", [2, 3, 4])
-def test_workload_configs(dev, cfg_id):
-    c = isa_inputs.CONFIGS[cfg_id]
+@pytest.mark.parametrize("name", ["16k", "23768_ragged", "64k"])
+def test_workloads(dev, name):
+    c = isa_inputs.WORKLOADS[name]
     p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"])
-    log(f"cfg {cfg_id}: generating inputs")
-    inp = _inputs(cfg_id, p)
-    log(f"cfg {cfg_id}: forward")
+    log(f"{name}: generating inputs")
+    inp = _inputs(c["stream"], p)
+    log(f"{name}: forward")
     res = _run(p, inp, dev)
-    log(f"cfg {cfg_id}: checking selections of {p.H} heads, outputs of 3 heads")
-    _check(p, inp, res, {(0, 0), (0, 17), (0, p.H - 1)}, 384, seed=cfg_id)
+    log(f"{name}: checking selections of {p.H} heads, outputs of 3 heads")
+    _check(p, inp, res, {(0, 0), (0, 17), (0, p.H - 1)}, 384, seed=c["stream"])
 
 
 SWEEP = [  # (b, alpha_s, alpha_ns, alpha_f) points of the 131072-token sweep
@@ -125,20 +127,20 @@ SWEEP = [  # (b, alpha_s, alpha_ns, alpha_f) points of the 131072-token sweep
 
 @pytest.mark.parametrize("b,a_s,a_ns,a_f", SWEEP)
 def test_128k_sweep_points(dev, b, a_s, a_ns, a_f):
-    c = isa_inputs.CONFIGS[5]
+    c = isa_inputs.WORKLOADS["128k"]
     p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], b, a_s, a_f, a_ns)
     heads = [(0, 3), (0, 29)]
     log(f"128k b={b} a_s={a_s} a_ns={a_ns} a_f={a_f}: inputs")
-    inp = _inputs(5, p, heads=heads, tile_heads=True)
+    inp = _inputs(STREAM["128k"], p, heads=heads, tile_heads=True)
     log("128k: forward")
     res = _run(p, inp, dev)
     _check(p, inp, res, set(heads), 128, seed=b, all_sel=False)
 
 
 # -------------------------------------------------------- special cases
-def _small(dev, L_src, L_ctx, D, b, a_s, a_f, a_ns, H=2, cfg_id=1, modify=None):
+def _small(dev, L_src, L_ctx, D, b, a_s, a_f, a_ns, H=2, stream=1, modify=None):
     p = isa.Params(1, H, L_src, L_ctx, D, b, a_s, a_f, a_ns)
-    inp = _inputs(cfg_id, p)
+    inp = _inputs(stream, p)
     if modify:
         modify(inp, p)
     res = _run(p, inp, dev)
@@ -155,7 +157,7 @@ def test_small_shapes_all_rows(dev, D, b):
 def test_batch_and_odd_head_counts(dev, B, H):
     """B > 1 and head counts that do not fill the XCD remap evenly."""
     p = isa.Params(B, H, 640, 520, 128, 64, 0.25, 0.5, 0.125)
-    inp = _inputs(2, p)
+    inp = _inputs(STREAM["16k"], p)
     res = _run(p, inp, dev)
     _check(p, inp, res, {(B - 1, H - 1), (0, 1)}, None)
     Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
@@ -244,9 +246,9 @@ def test_deterministic(dev):
 
 
 def test_step_entry_points_compose_to_forward(dev):
-    c = isa_inputs.CONFIGS[3]
+    c = isa_inputs.WORKLOADS["23768_ragged"]
     p = isa.Params(1, 4, c["L_src"], c["L_ctx"], c["D"], c["b"])
-    inp = _inputs(3, p)
+    inp = _inputs(STREAM["23768_ragged"], p)
     Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
     O_ref, dbg = isa.forward(Q, K, V, p, debug=True)
     qc, kc, kcb, vcb = isa.pool_coarse(Q, K, V, p)
@@ -279,7 +281,7 @@ def test_coarse_residual_gamma(dev, gamma):
     """Step (6) residual: forward with gamma matches the oracle, and the
     residual entry point composes with the other steps."""
     p = isa.Params(1, 2, 700, 451, 128, 64, 0.25, 0.5, 0.125, gamma)
-    inp = _inputs(1, p)
+    inp = _inputs(STREAM["tiny"], p)
     res = _run(p, inp, dev)
     plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
     for h in range(p.H):
@@ -305,9 +307,9 @@ def test_pure_taylor_flat_path_at_16k(dev):
     every head, sampled rows of three heads; then the Fig. 6 property on the
     GPU outputs: per-block Taylor error rises with sharpness."""
     from scipy.stats import spearmanr
-    c = isa_inputs.CONFIGS[2]
+    c = isa_inputs.WORKLOADS["16k"]
     p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"], 0.125, 1.0, 0.0)
-    inp = _inputs(2, p)
+    inp = _inputs(STREAM["16k"], p)
     log("pure Taylor 16k: forward")
     res = _run(p, inp, dev)
     assert res["sharp_idx"].size == 0
@@ -352,7 +354,7 @@ def test_rope_pool_matches_oracle(dev, D):
     and the pooled means of the rotated tensors."""
     base = 10000.0
     p = isa.Params(2, 3, 700, 451, D, 64, rope_base=base)
-    inp = _inputs(1, p)
+    inp = _inputs(STREAM["tiny"], p)
     Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
     Qr, Kr, qc, kc, kcb, vcb = isa.rope_pool_coarse(Q, K, V, p)
     torch.cuda.synchronize()
@@ -381,7 +383,7 @@ def test_rope_forward_small_all_rows(dev):
     tensors of the RoPE entry point."""
     base = 10000.0
     p = isa.Params(1, 2, 700, 451, 128, 64, 0.25, 0.5, 0.125, rope_base=base)
-    inp = _inputs(1, p)
+    inp = _inputs(STREAM["tiny"], p)
     res = _run(p, inp, dev)
     plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
     for h in range(p.H):
@@ -402,10 +404,10 @@ def test_rope_forward_ragged_workload(dev):
     """RoPE on the ragged 11884 + 11884-token workload (both segments end in
     a partial block; positions restart at the context segment): every
     selection of every head, sampled rows of two heads."""
-    c = isa_inputs.CONFIGS[3]
+    c = isa_inputs.WORKLOADS["23768_ragged"]
     base = 10000.0
     p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"], rope_base=base)
-    inp = _inputs(3, p)
+    inp = _inputs(STREAM["23768_ragged"], p)
     log("rope ragged workload: forward")
     res = _run(p, inp, dev)
     plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)

@@ -53,7 +53,7 @@ def test_plan_matches_oracle_counts(isa):
     from oracle import isa_oracle
     import isa_inputs
     cases = []
-    for cid, c in isa_inputs.CONFIGS.items():
+    for c in isa_inputs.WORKLOADS.values():
         cases.append((c["L_src"], c["L_ctx"], c["D"], c["b"], c["alpha_s"], c["alpha_f"], c["alpha_ns"]))
     for b in (32, 64):
         for a_s in (0.125, 0.25):

@@ -14,6 +14,8 @@ import isa_inputs
 from oracle import isa_oracle as O
 from oracle.brute import brute_isa_head
 
+STREAM = {name: w["stream"] for name, w in isa_inputs.WORKLOADS.items()}
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -264,8 +266,8 @@ def test_blockwise_equals_brute_force(L_src, L_ctx, b, D, a_s, a_f, a_ns, seed):
 
 
 def test_tiny_config_blockwise_equals_brute_force():
-    c = isa_inputs.CONFIGS[1]
-    Q, K, V = isa_inputs.make_head(1, 0, 0, c["L_src"], c["L_ctx"], c["D"])
+    c = isa_inputs.WORKLOADS["tiny"]
+    Q, K, V = isa_inputs.make_head(STREAM["tiny"], 0, 0, c["L_src"], c["L_ctx"], c["D"])
     p = O.make_plan(c["L_src"], c["L_ctx"], c["b"], c["alpha_s"], c["alpha_f"], c["alpha_ns"])
     r = O.isa_head(Q, K, V, p)
     g = brute_isa_head(Q, K, V, c["L_src"], c["L_ctx"], c["b"], c["alpha_s"], c["alpha_f"], c["alpha_ns"])
@@ -316,8 +318,8 @@ def test_taylor_error_grows_with_sharpness_soft():
     peak of sharp rows on this generator and the correlation turns negative;
     that case is not what the figure measures."""
     from scipy.stats import spearmanr
-    c = isa_inputs.CONFIGS[1]
-    Q, K, V = isa_inputs.make_head(1, 0, 1, c["L_src"], c["L_ctx"], c["D"])
+    c = isa_inputs.WORKLOADS["tiny"]
+    Q, K, V = isa_inputs.make_head(STREAM["tiny"], 0, 1, c["L_src"], c["L_ctx"], c["D"])
     pt = O.make_plan(c["L_src"], c["L_ctx"], c["b"], c["alpha_s"], 1.0, 0.0)
     pe = O.make_plan(c["L_src"], c["L_ctx"], c["b"], c["alpha_s"], 0.0, 0.0)
     rt, re_ = O.isa_head(Q, K, V, pt), O.isa_head(Q, K, V, pe)
@@ -338,9 +340,9 @@ def test_bf16_rounding_matches_torch_rne():
 
 
 def test_generator_is_seeded_and_structured():
-    a = isa_inputs.make_head(4, 0, 3, 256, 256, 16)
-    b = isa_inputs.make_head(4, 0, 3, 256, 256, 16)
-    c = isa_inputs.make_head(4, 0, 4, 256, 256, 16)
+    a = isa_inputs.make_head(STREAM["64k"], 0, 3, 256, 256, 16)
+    b = isa_inputs.make_head(STREAM["64k"], 0, 3, 256, 256, 16)
+    c = isa_inputs.make_head(STREAM["64k"], 0, 4, 256, 256, 16)
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
     assert not np.array_equal(a[0], c[0])
     Q, K, V = a
