@@ -273,3 +273,27 @@ def test_backward_block_shared_by_every_exact_set(dev):
         _compare("dQ", res["dQ"][0, h], gq)
         _compare("dK", res["dK"][0, h], gk)
         _compare("dV", res["dV"][0, h], gv)
+
+
+@pytest.mark.parametrize("L_src,L_ctx,b,a_s,a_f,a_ns", [
+    (40, 0, 64, 0.25, 0.5, 0.25),    # one partial block, no context
+    (1, 70, 32, 0.5, 0.5, 0.5),      # a one-token source segment
+    (65, 1, 64, 1.0, 0.5, 0.5),      # one-token tails in both segments
+    (33, 97, 32, 0.34, 0.7, 0.2),    # one-token tails, one exact block per flat block
+])
+def test_forward_backward_tiny_edges(dev, L_src, L_ctx, b, a_s, a_f, a_ns):
+    """Degenerate shapes: forward (every row) and backward (every gradient)
+    against the oracle."""
+    p = isa.Params(1, 2, L_src, L_ctx, 64, b, a_s, a_f, a_ns)
+    inp = isa_inputs.make_inputs(STREAM["tiny"], p.B, p.H, p.L_src, p.L_ctx, p.D)
+    dO_bits, dO_vals = _dO(p, 6)
+    res = _run(p, inp, dO_bits, dev)
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    for h in range(p.H):
+        r = isa_oracle.isa_head(*(inp[n][1][0, h] for n in "QKV"), plan)
+        e = np.abs(res["O"][0, h] - r.O)
+        assert e.max() <= 2e-2 and e.mean() <= 2e-3, (h, e.max(), e.mean())
+        gq, gk, gv = _oracle_grads(plan, inp, dO_vals, 0, h, res["sel"])
+        _compare("dQ", res["dQ"][0, h], gq)
+        _compare("dK", res["dK"][0, h], gk)
+        _compare("dV", res["dV"][0, h], gv)
