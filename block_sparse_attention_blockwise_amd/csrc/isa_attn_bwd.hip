@@ -523,7 +523,7 @@ void dq_kernel(BwdArgs a) {
   const IsaShape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int bh = blockIdx.y;
+  const int qx = blockIdx.x, bh = blockIdx.y;
   const size_t head = (size_t)bh * s.L;
   const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
   const int b = s.b, lb = b == 64 ? 6 : 5;
@@ -536,7 +536,7 @@ void dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int lr = wave * ROWS_W + 16 * qt + c16;
-    const int e = MODE == kSharp ? blockIdx.x * (ROWS >> lb) + (lr >> lb) : blockIdx.x;
+    const int e = MODE == kSharp ? qx * (ROWS >> lb) + (lr >> lb) : qx;
     const int o = MODE == kSharp ? (lr & (b - 1)) : lr;
     qval[qt] = false;
     qtok[qt] = 0;
@@ -574,7 +574,7 @@ void dq_kernel(BwdArgs a) {
     }
   } else {
     ntab = s.k_ns;
-    const int32_t* ex = a.exact + ((size_t)bh * s.n_flat + blockIdx.x) * s.k_ns;
+    const int32_t* ex = a.exact + ((size_t)bh * s.n_flat + qx) * s.k_ns;
     for (int q = tid; q < s.k_ns; q += NT) {
       const int j = ex[q];
       int st = 0, n = 0;
@@ -849,7 +849,21 @@ void dkv_pc_kernel(BwdArgs a) {
   const int g = lane >> 4, c16 = lane & 15;
   const bool producer = wave < 4;
   const int pair = wave & 3;
-  const int bh = blockIdx.x, pb = blockIdx.y * KPB;
+  // Every workgroup of a head streams the same query blocks; dispatch goes
+  // round-robin over the 8 XCDs (each with its own L2), so the index is
+  // remapped to give each XCD a contiguous run of key chunks, i.e. mostly
+  // one head at a time (chunks vary fastest in the grid).
+  int cx = blockIdx.x, bh = blockIdx.y;
+  {
+    const int total = gridDim.x * gridDim.y;
+    if ((total & 7) == 0) {
+      const int id = blockIdx.x + gridDim.x * blockIdx.y;
+      const int logical = (id & 7) * (total >> 3) + (id >> 3);
+      cx = logical % gridDim.x;
+      bh = logical / gridDim.x;
+    }
+  }
+  const int pb = cx * KPB;
   const size_t head = (size_t)bh * s.L;
   const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
 
@@ -1130,7 +1144,7 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
     BwdArgs k = a;
     if (!pooled && !residual) k.dkc = k.dvc = nullptr;
 const int kpb = 128 / s.b;   // 128 keys per workgroup
-    dim3 grid(BH, (s.N_kv + kpb - 1) / kpb);
+    dim3 grid((s.N_kv + kpb - 1) / kpb, BH);
     if (s.b == 64) dkv_pc_kernel<D, 64><<<grid, 512, 0, st>>>(k);
     else dkv_pc_kernel<D, 32><<<grid, 512, 0, st>>>(k);
     e = hipGetLastError();
