@@ -93,6 +93,9 @@ size_t scores_bytes(const IsaShape& s) {
 }
 
 // Validates the parameters and derives every count. Makes no HIP call.
+// (batch, head) pairs index the second grid dimension of several launches.
+constexpr int64_t kMaxHeads = 65535;
+
 int make_shape(const isa_params_t* p, IsaShape* s) {
   if (!p || !s) return ISA_ERR_ARG;
   if (p->B < 1 || p->H < 1 || p->L_src < 1 || p->L_ctx < 0 || p->D < 1 || p->b < 1)
@@ -101,6 +104,7 @@ int make_shape(const isa_params_t* p, IsaShape* s) {
   if (!std::isfinite(p->gamma)) return ISA_ERR_ARG;
   if (!(p->rope_base == 0.0 || (std::isfinite(p->rope_base) && p->rope_base > 1.0))) return ISA_ERR_ARG;
   if (p->D != 64 && p->D != 128) return ISA_ERR_UNSUPPORTED;
+  if ((int64_t)p->B * p->H > kMaxHeads) return ISA_ERR_UNSUPPORTED;
   if (p->b != 32 && p->b != 64) return ISA_ERR_UNSUPPORTED;
   const int64_t N_src = ((int64_t)p->L_src + p->b - 1) / p->b;
   const int64_t N_ctx = ((int64_t)p->L_ctx + p->b - 1) / p->b;
@@ -379,6 +383,7 @@ int isa_dense_attn(int32_t B, int32_t H, int32_t L, int32_t D, const void* Q, co
   if (B < 1 || H < 1 || L < 1 || D < 1 || !Q || !K || !V || !O) return ISA_ERR_ARG;
   if (!aligned16({Q, K, V, O})) return ISA_ERR_ARG;
   if (D != 64 && D != 128) return ISA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > kMaxHeads) return ISA_ERR_UNSUPPORTED;
   return hip_status(isa_launch_dense_attn(B, H, L, D, (const uint16_t*)Q, (const uint16_t*)K,
                                           (const uint16_t*)V, (uint16_t*)O, as_stream(stream)));
 }

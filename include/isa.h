@@ -61,7 +61,8 @@
  *              every workspace must start on a 16-byte boundary (the kernels
  *              move 16-byte vectors); otherwise ISA_ERR_ARG.
  *   Limits:    D in {64, 128}; b in {32, 64}; L_src >= 1; L_ctx >= 0;
- *              B, H >= 1; N_src <= 4096; N_ctx <= 4096; N_kv <= 4096;
+ *              B, H >= 1; B * H <= 65535; N_src <= 4096; N_ctx <= 4096;
+ *              N_kv <= 4096;
  *              ratios in [0, 1] (NaN rejected); gamma finite; rope_base 0 or
  *              finite and > 1.
  */
@@ -213,7 +214,8 @@ ISA_API int isa_backward(const isa_params_t* p, const void* Q, const void* K, co
                          void* ws, size_t ws_bytes, void* stream);
 
 /* Dense baseline: O = softmax(Q K^T / sqrt(D)) V over all L tokens (no mask),
- * bf16 in/out, same tile engine as isa_sharp_attn. D in {64, 128}. The
+ * bf16 in/out, same tile engine as isa_sharp_attn. D in {64, 128},
+ * B * H <= 65535 (else ISA_ERR_UNSUPPORTED). The
  * comparison line the pages measure ISA against (rainbus.top summary,
  * "Prerequisites", SDPA and FlashAttention paragraph). */
 ISA_API int isa_dense_attn(int32_t B, int32_t H, int32_t L, int32_t D, const void* Q, const void* K,

@@ -100,6 +100,7 @@ def _params(isa, **kw):
     (dict(D=96), -2), (dict(D=256), -2), (dict(b=16), -2), (dict(b=128), -2),
     (dict(L_src=64 * 4097), -2), (dict(L_ctx=64 * 4097), -2),
     (dict(L_src=64 * 4000, L_ctx=64 * 4000, alpha_s=0.05), -2),   # N_kv > 4096
+    (dict(B=256, H=256), -2),                                       # B*H > 65535
 ])
 def test_plan_rejects(isa, kw, code):
     out = isa.IsaPlan()
@@ -146,6 +147,7 @@ def test_calls_fail_before_launch(isa):
     assert pl1.workspace_bytes > pl0.workspace_bytes
     assert L.isa_dense_attn(1, 1, 0, 128, fake, fake, fake, fake, None) == -1
     assert L.isa_dense_attn(1, 1, 16, 96, fake, fake, fake, fake, None) == -2
+    assert L.isa_dense_attn(256, 256, 16, 64, fake, fake, fake, fake, None) == -2
     assert L.isa_dense_attn(1, 1, 16, 128, None, fake, fake, fake, None) == -1
     # 16-byte alignment of the vector-accessed tensors
     odd = fake + 8
