@@ -265,8 +265,10 @@ def backward_bench(isa, torch, p, Q, K, V, args):
 def measured_peaks(torch, dev):
     """Achievable peaks on this device: bf16 matrix-core rate from the probe
     kernel (independent MFMA chains, no memory traffic), HBM read bandwidth
-    of a streaming 16-byte-load kernel over 2 GiB, and HBM bandwidth of a
-    2 GiB device-to-device copy (read + write bytes)."""
+    of a streaming 16-byte-load kernel over 2 GiB, HBM bandwidth of a
+    2 GiB device-to-device copy (read + write bytes), and the LDS read rate
+    of the attention kernels' two operand patterns (16-byte row reads and
+    8-byte transposed reads, 2048 workgroups of 256 threads)."""
     from block_sparse_attention_blockwise_amd import _build
     probe = ctypes.CDLL(_build.PROBE_PATH)
     probe.isa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
@@ -309,7 +311,24 @@ def measured_peaks(torch, dev):
     torch.cuda.synchronize()
     hbm_read = 5 * 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst, out, rout
-    return {"mfma_bf16_tflops": mfma_tflops, "hbm_read_gbs": hbm_read, "hbm_copy_gbs": hbm_copy}
+    probe.isa_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe.isa_probe_lds_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    probe.isa_probe_lds_bytes.restype = ctypes.c_double
+    lblocks, liters = 2048, 4000
+    lout = torch.empty(lblocks * 256, dtype=torch.float32, device=dev)
+    lds = {}
+    for mode, name in ((0, "lds_read_row_tbs"), (1, "lds_read_tr_tbs")):
+        rc = probe.isa_probe_lds(lblocks, 16, mode, lout.data_ptr(), sp)
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed: {rc}")
+        e0.record()
+        for _ in range(3):
+            probe.isa_probe_lds(lblocks, liters, mode, lout.data_ptr(), sp)
+        e1.record()
+        torch.cuda.synchronize()
+        lds[name] = 3 * probe.isa_probe_lds_bytes(lblocks, liters, mode) / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del lout
+    return {"mfma_bf16_tflops": mfma_tflops, "hbm_read_gbs": hbm_read, "hbm_copy_gbs": hbm_copy, **lds}
 
 
 def sweep_128k(isa, torch, dev, args):

@@ -3,7 +3,8 @@
 // independent v_mfma_f32_16x16x32_bf16 chains and touches no memory in its
 // loop (its rate is the matrix-core throughput the chip sustains), and a
 // kernel that streams a large buffer from HBM with 16-byte loads (the read
-// bandwidth it sustains).
+// bandwidth it sustains), and a kernel that reads LDS tiles with the access
+// patterns of the attention kernels' operand reads (the LDS read rate).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -13,6 +14,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef float float4_t __attribute__((__vector_size__(16)));
+typedef short short4_t __attribute__((__vector_size__(8)));
 
 constexpr int kChains = 8;   // independent accumulators per wave (hide the MFMA latency)
 
@@ -54,6 +56,50 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
   out[tid] = (float)acc;
 }
 
+
+// LDS tiles laid out as in the attention kernels: rows of 2*128 + 32 bytes.
+constexpr int kLdsStride = 288;
+constexpr int kLdsRows = 80;   // 64-row tile plus a sliding offset of up to 15 rows
+
+// mode 0: 16-byte row reads (the score operand pattern, ds_read_b128);
+// mode 1: 8-byte transposed reads (the value operand pattern, ds_read_b64_tr_b16).
+// 16 reads per lane per iteration; the row offset slides with the iteration
+// so that no read is loop-invariant. Every access stays inside the tile.
+__global__ __launch_bounds__(256) void lds_probe_kernel(int iters, int mode, float* out) {
+  __shared__ __attribute__((aligned(16))) char buf[kLdsRows * kLdsStride];
+  for (int i = threadIdx.x; i < kLdsRows * kLdsStride / 4; i += 256)
+    reinterpret_cast<uint32_t*>(buf)[i] = (uint32_t)i * 2654435761u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  uint32_t a0 = 0, a1 = 0;
+  if (mode == 0) {
+    for (int it = 0; it < iters; ++it) {
+      const int r0 = it & 15;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int mt = k & 3, kk = k >> 2;   // rows <= 48 + 15 + 15, bytes <= 2 * (96 + 24) + 16
+        const uint4 v = *reinterpret_cast<const uint4*>(buf + (16 * mt + c16 + r0) * kLdsStride + (32 * kk + 8 * g) * 2);
+        a0 ^= v.x ^ v.y;
+        a1 ^= v.z ^ v.w;
+      }
+    }
+  } else {
+    const int tr_row = 4 * g + (c16 >> 2), tr_col = 4 * (c16 & 3);
+    for (int it = 0; it < iters; ++it) {
+      const int r0 = it & 15;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int dt = k >> 1, half = k & 1;   // rows <= 16 + 15 + 15 (+ 32 below), bytes <= 2 * (112 + 12) + 8
+        const char* p = buf + (32 * (it & 1) + 16 * half + tr_row + r0) * kLdsStride + (16 * dt + tr_col) * 2;
+        const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
+        const uint2 w = __builtin_bit_cast(uint2, v);
+        a0 ^= w.x;
+        a1 ^= w.y;
+      }
+    }
+  }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = (float)(a0 ^ a1);
+}
 }  // namespace
 
 // Reads `bytes` (a multiple of 16) from device memory `src` once with
@@ -77,4 +123,18 @@ PROBE_API int isa_probe_mfma_bf16(int blocks, int iters, float* out, void* strea
 // Flops one isa_probe_mfma_bf16 launch performs.
 PROBE_API double isa_probe_mfma_flops(int blocks, int iters) {
   return (double)blocks * 4.0 * iters * kChains * 16.0 * 16.0 * 32.0 * 2.0;
+}
+
+// Launches `blocks` workgroups of 256 threads reading LDS (mode 0: 16-byte
+// row reads, mode 1: 8-byte transposed reads), iters * 16 reads per thread;
+// `out` must hold blocks * 256 floats. Returns 0 or the HIP error code.
+PROBE_API int isa_probe_lds(int blocks, int iters, int mode, float* out, void* stream) {
+  if (blocks < 1 || iters < 1 || (mode != 0 && mode != 1) || !out) return -1;
+  lds_probe_kernel<<<blocks, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(iters, mode, out);
+  return (int)hipGetLastError();
+}
+
+// Bytes one isa_probe_lds launch reads from LDS.
+PROBE_API double isa_probe_lds_bytes(int blocks, int iters, int mode) {
+  return (double)blocks * 256.0 * iters * 16.0 * (mode == 0 ? 16.0 : 8.0);
 }
