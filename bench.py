@@ -10,7 +10,8 @@ context top-k, coarse rows + sharpness + split + exact sets, sharp attention,
 flat exact+Taylor attention. The step is issued as the five entry points on
 torch's current stream with HIP events between them (per-kernel durations
 for the roofline); the isa_forward entry point (same kernels in one call) is
-timed as well, as is the library's dense attention on the same inputs.
+timed as well, as is the library's dense attention on the same inputs, and,
+for context, PyTorch's flash scaled_dot_product_attention on them.
 
 Prints one JSON line. `value` is the forward latency in ms (lower is better).
 """
@@ -260,6 +261,27 @@ def backward_bench(isa, torch, p, Q, K, V, args):
             "forward_plus_backward": res["dense_same_engine"]["step_ms"] / res["isa"]["step_ms"]}
     print(json.dumps({"backward": res, "config": {"workload": "isa_fwd_64k_tokens_h40_d128"}}),
           flush=True)
+
+
+def torch_sdpa_ms(torch, Q, K, V, reps):
+    """Context: PyTorch's own fused attention (flash backend only, no math
+    fallback) on the same inputs, unmasked over all L tokens like the dense
+    baseline. None when that backend is unavailable on this build."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            o = torch.nn.functional.scaled_dot_product_attention(Q, K, V)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(max(reps, 1)):
+                o = torch.nn.functional.scaled_dot_product_attention(Q, K, V)
+            e1.record()
+            torch.cuda.synchronize()
+        del o
+        return e0.elapsed_time(e1) / max(reps, 1)
+    except RuntimeError:
+        return None
 
 
 def measured_peaks(torch, dev):
@@ -576,6 +598,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / args.dense_reps
+    sdpa_ms = None if args.no_dense else torch_sdpa_ms(torch, Q, K, V, args.dense_reps)
 
     sharp_tflops = flops["sharp"] / (per["sharp_attn"] * 1e-3) / 1e12
     rec = traffic_record()
@@ -617,6 +640,8 @@ def main():
         "dense_ms": dense_ms,
         "dense_tflops": (flops["dense"] / (dense_ms * 1e-3) / 1e12) if dense_ms else None,
         "speedup_vs_dense": (dense_ms / step_ms) if dense_ms else None,
+        "torch_sdpa_flash_ms": sdpa_ms,
+        "speedup_vs_torch_sdpa": (sdpa_ms / step_ms) if sdpa_ms else None,
         "roofline": roofline,
         "cpu_baseline": None,
     }
