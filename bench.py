@@ -581,6 +581,31 @@ def main():
     rope_ms = e0.elapsed_time(e1) / args.steps
     del Qr, Kr, ws_r
 
+    # residual gamma * O_coarse (gamma = 0.5, same workload): the step on its
+    # own (adds into O in place) and the whole forward with it
+    pg = isa.Params(p.B, p.H, p.L_src, p.L_ctx, p.D, p.b, p.alpha_s, p.alpha_f, p.alpha_ns, gamma=0.5)
+    pgc = pg.c()
+    ws_g = e(isa.plan(pg)["workspace_bytes"], dt=torch.uint8)
+
+    def residual():
+        chk("residual", lib.isa_coarse_residual(ctypes.byref(pgc), qc.data_ptr(), kc.data_ptr(), vcb.data_ptr(),
+                                                ctx.data_ptr() if ctx.numel() else None, O.data_ptr(),
+                                                ws_s.data_ptr(), ws_s.numel(), sp))
+
+    def forward_residual():
+        chk("fwd_residual", lib.isa_forward(ctypes.byref(pgc), Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                                            O.data_ptr(), ws_g.data_ptr(), ws_g.numel(), None, sp))
+    timings = {}
+    for name, fn in (("residual", residual), ("forward_residual", forward_residual)):
+        fn()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        timings[name] = e0.elapsed_time(e1) / args.steps
+    del ws_g
+
     flops = algorithmic_flops(p, pl, ctx.view(p.B, p.H, -1).cpu().numpy(),
                               si.view(p.B, p.H, -1).cpu().numpy(), fi.view(p.B, p.H, -1).cpu().numpy(),
                               ei.view(p.B, p.H, pl["n_flat"], pl["k_ns"]).cpu().numpy())
@@ -634,6 +659,8 @@ def main():
         "measured_peaks": peaks,
         "isa_backward_ms": bwd_ms,
         "rope_pool_ms": rope_ms,
+        "coarse_residual_ms": timings["residual"],
+        "isa_forward_residual_ms": timings["forward_residual"],
         "rope_pool_hbm_frac": (pool_bytes + 2 * BH * (p.L_src + p.L_ctx) * p.D * 2) /
                               (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "algorithmic_tflop": {k: v / 1e12 for k, v in flops.items()},
