@@ -362,10 +362,17 @@ __global__ __launch_bounds__(64 * kFlatTopkWaves) void flat_topk_kernel(IsaShape
 }
 
 // ------------------------------------------------ step (6) coarse residual
-// One workgroup per query block i: softmax of the coarse row S[i, J] (fp64),
-// O_coarse_i = sum_p w_p Vc[J[p]] / sum_p w_p, then gamma * O_coarse_i is
-// added to every token row of block i (bf16 read-modify-write).
+// O_coarse = softmax(S[:, J]) Vc[J] over the query blocks of a head is an
+// (N x N_kv) by (N_kv x D) product whose right operand every block shares.
+// One workgroup takes kResRows consecutive query blocks: it forms each row's
+// max and normaliser z_i in fp64 (one wave per row), then streams J in tiles
+// of kResTile pooled keys (the Vc rows staged in LDS, the weights
+// exp(S - max) formed once per tile) and accumulates in fp32; finally
+// gamma * O_coarse_i / z_i is added to every token row of block i (bf16
+// read-modify-write in 16-byte vectors).
 constexpr int kResThreads = 256;
+constexpr int kResRows = 16;
+constexpr int kResTile = 64;
 
 __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -375,62 +382,87 @@ __device__ inline uint16_t f32_to_bf16_rne_sel(float f) {
   return (uint16_t)(u >> 16);
 }
 
+template <int D>
 __global__ __launch_bounds__(kResThreads) void coarse_residual_kernel(IsaShape s, const double* __restrict__ srows,
                                                                       const uint16_t* __restrict__ vcb,
                                                                       const int32_t* __restrict__ ctx_idx,
                                                                       uint16_t* __restrict__ O) {
-  const int i = blockIdx.x, bh = blockIdx.y;
-  __shared__ double w[ISA_MAX_NKV];
-  __shared__ double red[kResThreads / 64];
-  __shared__ float part[kResThreads / 128][128];
-  __shared__ float oc[128];
-  const double* row = srows + ((size_t)bh * s.N + i) * s.N_kv;
+  constexpr int CPR = D / 8;                        // 16-byte chunks per row
+  constexpr int RPT = kResRows * D / kResThreads;   // rows accumulated per thread
+  const int i0 = blockIdx.x * kResRows, bh = blockIdx.y;
+  const int nr = min(kResRows, s.N - i0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ double rmax[kResRows], rz[kResRows];
+  __shared__ float w[kResRows][kResTile];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kResTile][D];
+  __shared__ float oc[kResRows][D];
+  const double* rows = srows + ((size_t)bh * s.N + i0) * s.N_kv;
   const int32_t* ctx_row = ctx_idx + (size_t)bh * s.k_ctx;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  double mx = -INFINITY;
-  for (int p = threadIdx.x; p < s.N_kv; p += kResThreads) mx = fmax(mx, row[p]);
-  mx = wave_max_f64(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  mx = red[0];
-  for (int x = 1; x < kResThreads / 64; ++x) mx = fmax(mx, red[x]);
-  __syncthreads();
-  double z = 0.0;
-  for (int p = threadIdx.x; p < s.N_kv; p += kResThreads) {
-    const double e = exp(row[p] - mx);
-    w[p] = e;
-    z += e;
-  }
-  z = wave_sum_f64(z);
-  if (lane == 0) red[wave] = z;
-  __syncthreads();
-  z = 0.0;
-  for (int x = 0; x < kResThreads / 64; ++x) z += red[x];
-  // weighted sum of the bf16 block means of V: thread (half, d)
-  const int D = s.D;
-  const int d = threadIdx.x % 128, half = threadIdx.x / 128;
-  float acc = 0.0f;
-  if (d < D) {
-    for (int p = half; p < s.N_kv; p += kResThreads / 128) {
-      const int j = kept_block_id(s, ctx_row, p);
-      if (j >= 0 && j < s.N)
-        acc += (float)w[p] * bf16_to_f32(vcb[((size_t)bh * s.N + j) * D + d]);
+  const uint16_t* vh = vcb + (size_t)bh * s.N * D;
+
+  for (int r = wave; r < nr; r += kResThreads / 64) {
+    const double* row = rows + (size_t)r * s.N_kv;
+    double mx = -INFINITY;
+    for (int p = lane; p < s.N_kv; p += 64) mx = fmax(mx, row[p]);
+    mx = wave_max_f64(mx);
+    double z = 0.0;
+    for (int p = lane; p < s.N_kv; p += 64) z += exp(row[p] - mx);
+    z = wave_sum_f64(z);
+    if (lane == 0) {
+      rmax[r] = mx;
+      rz[r] = z;
     }
   }
-  part[half][d] = acc;
+  const int d = tid % D, rg = tid / D;   // column d of rows rg*RPT .. rg*RPT+RPT-1
+  float acc[RPT];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) acc[u] = 0.0f;
   __syncthreads();
-  if (threadIdx.x < D) {
-    float t = 0.0f;
-    for (int x = 0; x < kResThreads / 128; ++x) t += part[x][threadIdx.x];
-    oc[threadIdx.x] = s.gamma * (float)((double)t / z);
+  for (int p0 = 0; p0 < s.N_kv; p0 += kResTile) {
+    for (int c = tid; c < kResTile * CPR; c += kResThreads) {
+      const int pp = c / CPR, k = c % CPR, p = p0 + pp;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (p < s.N_kv) {
+        const int j = kept_block_id(s, ctx_row, p);
+        if (j >= 0 && j < s.N) v = *reinterpret_cast<const uint4*>(vh + (size_t)j * D + 8 * k);
+      }
+      *reinterpret_cast<uint4*>(&vt[pp][8 * k]) = v;
+    }
+    for (int c = tid; c < kResRows * kResTile; c += kResThreads) {
+      const int r = c / kResTile, pp = c % kResTile, p = p0 + pp;
+      w[r][pp] = (r < nr && p < s.N_kv) ? (float)exp(rows[(size_t)r * s.N_kv + p] - rmax[r]) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int pp = 0; pp < kResTile; ++pp) {
+      const float v = bf16_to_f32(vt[pp][d]);
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) acc[u] += w[rg * RPT + u][pp] * v;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const int r = rg * RPT + u;
+    oc[r][d] = r < nr ? s.gamma * (float)((double)acc[u] / rz[r]) : 0.0f;
   }
   __syncthreads();
-  int start, n;
-  isa_block_range(s, i, start, n);
-  uint16_t* base = O + ((size_t)bh * s.L + start) * D;
-  for (int x = threadIdx.x; x < n * D; x += kResThreads) {
-    const float v = bf16_to_f32(base[x]) + oc[x % D];
-    base[x] = f32_to_bf16_rne_sel(v);
+  for (int r = 0; r < nr; ++r) {
+    int start, n;
+    isa_block_range(s, i0 + r, start, n);
+    uint16_t* base = O + ((size_t)bh * s.L + start) * D;
+    for (int c = tid; c < n * CPR; c += kResThreads) {
+      const int k = c % CPR;
+      const uint4 x = *reinterpret_cast<const uint4*>(base + (size_t)c * 8);
+      uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = bf16_to_f32((uint16_t)(wd[q] & 0xffffu)) + oc[r][8 * k + 2 * q];
+        const float hi = bf16_to_f32((uint16_t)(wd[q] >> 16)) + oc[r][8 * k + 2 * q + 1];
+        wd[q] = (uint32_t)f32_to_bf16_rne_sel(lo) | ((uint32_t)f32_to_bf16_rne_sel(hi) << 16);
+      }
+      *reinterpret_cast<uint4*>(base + (size_t)c * 8) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
   }
 }
 
@@ -440,8 +472,11 @@ hipError_t isa_launch_coarse_residual(const IsaShape& s, const double* srows,
                                       const uint16_t* vc_bf16, const int32_t* ctx_idx,
                                       uint16_t* O, hipStream_t st) {
   if (s.gamma == 0.0f) return hipSuccess;
-  dim3 grid(s.N, s.B * s.H);
-  coarse_residual_kernel<<<grid, kResThreads, 0, st>>>(s, srows, vc_bf16, ctx_idx, O);
+  dim3 grid((s.N + kResRows - 1) / kResRows, s.B * s.H);
+  if (s.D == 128)
+    coarse_residual_kernel<128><<<grid, kResThreads, 0, st>>>(s, srows, vc_bf16, ctx_idx, O);
+  else
+    coarse_residual_kernel<64><<<grid, kResThreads, 0, st>>>(s, srows, vc_bf16, ctx_idx, O);
   return hipGetLastError();
 }
 

@@ -276,11 +276,14 @@ def test_step_entry_points_compose_to_forward(dev):
         np.testing.assert_allclose(score[0, h].cpu().numpy(), r, rtol=1e-10, atol=1e-10)
 
 
-@pytest.mark.parametrize("gamma", [0.5, -0.25])
-def test_coarse_residual_gamma(dev, gamma):
+@pytest.mark.parametrize("gamma,D,b,Ls,Lc", [(0.5, 128, 64, 700, 451), (-0.25, 128, 64, 700, 451),
+                                            (0.5, 64, 32, 1000, 1100)])
+def test_coarse_residual_gamma(dev, gamma, D, b, Ls, Lc):
     """Step (6) residual: forward with gamma matches the oracle, and the
-    residual entry point composes with the other steps."""
-    p = isa.Params(1, 2, 700, 451, 128, 64, 0.25, 0.5, 0.125, gamma)
+    residual entry point composes with the other steps. 19 and 67 query
+    blocks: several 16-block workgroups of the residual kernel, the last
+    one partial."""
+    p = isa.Params(1, 2, Ls, Lc, D, b, 0.25, 0.5, 0.125, gamma)
     inp = _inputs(STREAM["tiny"], p)
     res = _run(p, inp, dev)
     plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
@@ -291,7 +294,7 @@ def test_coarse_residual_gamma(dev, gamma):
         log(f"residual gamma={gamma} h={h}: max-abs {e.max():.2e} mean-abs {e.mean():.2e}")
         assert e.max() <= 2e-2 and e.mean() <= 2e-3
     Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
-    p0 = isa.Params(1, 2, 700, 451, 128, 64, 0.25, 0.5, 0.125, 0.0)
+    p0 = isa.Params(1, 2, Ls, Lc, D, b, 0.25, 0.5, 0.125, 0.0)
     O0 = isa.forward(Q, K, V, p0)
     qc, kc, kcb, vcb = isa.pool_coarse(Q, K, V, p)
     ctx, _ = isa.ctx_topk(qc, kc, p)
