@@ -327,112 +327,220 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a, const uint16_t* _
 
 // ---------------------------------------------------------------- residual
 // Backward of gamma * O_coarse (O_coarse_i = softmax over J of S[i, J]
-// applied to Vc[J], broadcast to the tokens of block i). Per query block i
-// (one workgroup): dOc_i = gamma * sum of dO over the block's rows, the
+// applied to Vc[J], broadcast to the tokens of block i). Per query block i:
+// dOc_i = gamma * sum of dO over the block's rows (res_dosum_kernel), the
 // coarse softmax P_i (fp64, from the forward's coarse rows), O_coarse_i as
 // the forward computed it, Delta_i = dOc_i . O_coarse_i, the logit gradient
-// dS_i = P_i * (dOc_i . Vc_p - Delta_i) and dQc_i = sum_p dS_ip Kc_p / sqrt(D).
+// dS_i = P_i * (dOc_i . Vc_p - Delta_i) (the dot in fp32 as in the token-level
+// backward, P and the difference in fp64) and dQc_i = sum_p dS_ip Kc_p / sqrt(D)
+// (fp32).
+// A workgroup takes kResRows consecutive query blocks of a head; J streams
+// through LDS in tiles of kResTile pooled keys (Vc rows, and Kc rows for
+// the second pass), shared by the workgroup's rows.
 constexpr int kResThreads = 256;
-
-__device__ inline double block_sum_f64(double x, double* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  double t = 0.0;
-  for (int w = 0; w < kResThreads / 64; ++w) t += red[w];
-  return t;
-}
-
-__device__ inline double block_max_f64(double x, double* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o, 64));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  double t = red[0];
-  for (int w = 1; w < kResThreads / 64; ++w) t = fmax(t, red[w]);
-  return t;
-}
+constexpr int kResRows = 16;
+constexpr int kResTile = 64;
 
 __device__ inline float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// dOc_i = gamma * the sum of dO over the token rows of block i, one
+// workgroup per block: 16-byte loads, partial sums per token group, then a
+// fixed-order sum of the groups.
 template <int D>
-__global__ __launch_bounds__(kResThreads) void res_row_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kResThreads) void res_dosum_kernel(BwdArgs a) {
+  constexpr int CPR = D / 8, G = kResThreads / CPR;
   const IsaShape& s = a.s;
   const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  __shared__ double w[ISA_MAX_NKV];
-  __shared__ double red[kResThreads / 64];
-  __shared__ float part[2][D];
-  __shared__ float dov[D], ocv[D];
-  __shared__ int jid[ISA_MAX_NKV];
-  const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
-  const double* row = a.srows + ((size_t)bh * s.N + i) * s.N_kv;
-  const size_t nbase = ((size_t)bh * s.N) * D;
-  for (int p = tid; p < s.N_kv; p += kResThreads) jid[p] = kept_id(s, ctx_row, p);
-  double mx = -INFINITY;
-  for (int p = tid; p < s.N_kv; p += kResThreads) mx = fmax(mx, row[p]);
-  mx = block_max_f64(mx, red);
-  double z = 0.0;
-  for (int p = tid; p < s.N_kv; p += kResThreads) {
-    const double e = exp(row[p] - mx);
-    w[p] = e;
-    z += e;
-  }
-  z = block_sum_f64(z, red);
-  // gamma * sum of the block's dO rows; O_coarse as the forward formed it
-  const int d = tid % D, half = tid / D;
+  const int k = tid % CPR, tg = tid / CPR;
+  __shared__ float part[G][D];
   int st, n;
   isa_block_range(s, i, st, n);
-  float acc = 0.f, oacc = 0.f;
-  if (half < 2) {
-    for (int r = half; r < n; r += 2) acc += bf16f(a.dO[((size_t)bh * s.L + st + r) * D + d]);
-    for (int p = half; p < s.N_kv; p += 2) {
-      const int j = jid[p];
-      if (j >= 0) oacc += (float)w[p] * bf16f(a.vcb[nbase + (size_t)j * D + d]);
+  const uint16_t* src = a.dO + ((size_t)bh * s.L + st) * D + 8 * k;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int x = tg; x < n; x += G) {
+    const uint4 w = *reinterpret_cast<const uint4*>(src + (size_t)x * D);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += __uint_as_float(u[q] << 16);
+      acc[2 * q + 1] += __uint_as_float(u[q] & 0xffff0000u);
     }
-    part[half][d] = acc;
   }
-  __syncthreads();
-  if (tid < D) dov[tid] = s.gamma * (part[0][tid] + part[1][tid]);
-  __syncthreads();
-  if (half < 2) part[half][d] = oacc;
-  __syncthreads();
-  if (tid < D) ocv[tid] = (float)((double)(part[0][tid] + part[1][tid]) / z);
-  __syncthreads();
-  double dl = 0.0;
-  if (tid < D) dl = (double)dov[tid] * (double)ocv[tid];
-  dl = block_sum_f64(dl, red);
-  // dS over the kept blocks; the softmax goes to pc, dS to dsc and w
-  float* pc_row = a.pc + ((size_t)bh * s.N + i) * s.N_kv;
-  float* ds_row = a.dsc + ((size_t)bh * s.N + i) * s.N_kv;
-  for (int p = tid; p < s.N_kv; p += kResThreads) {
-    const int j = jid[p];
-    double dot = 0.0;
-    if (j >= 0)
-      for (int k = 0; k < D; ++k) dot += (double)dov[k] * (double)bf16f(a.vcb[nbase + (size_t)j * D + k]);
-    const double P = w[p] / z;
-    const double ds = P * (dot - dl);
-    w[p] = ds;
-    pc_row[p] = (float)P;
-    ds_row[p] = (float)ds;
-  }
-  __syncthreads();
-  double q = 0.0;
-  if (half < 2)
-    for (int p = half; p < s.N_kv; p += 2) {
-      const int j = jid[p];
-      if (j >= 0) q += w[p] * a.kc[nbase + (size_t)j * D + d];
-    }
-  __syncthreads();
-  if (half < 2) part[half][d] = (float)q;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[tg][8 * k + e] = acc[e];
   __syncthreads();
   if (tid < D) {
-    const size_t o = nbase + (size_t)i * D + tid;
-    a.dqc[o] = (part[0][tid] + part[1][tid]) / sqrtf((float)D);
-    a.doc[o] = dov[tid];
-    a.ocs[o] = ocv[tid];
+    float t = 0.f;
+    for (int g = 0; g < G; ++g) t += part[g][tid];
+    a.doc[((size_t)bh * s.N + i) * D + tid] = s.gamma * t;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kResThreads) void res_row_kernel(BwdArgs a) {
+  constexpr int VST = D + 2;                        // bf16 row stride: 4-byte stores, conflict-free column reads
+  constexpr int RPT = kResRows * D / kResThreads;   // rows per thread in the column-parallel phases
+  constexpr int RQ = kResRows / (kResThreads / kResTile);   // rows per thread in the key-parallel phase
+  const IsaShape& s = a.s;
+  const int i0 = blockIdx.x * kResRows, bh = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int nr = min(kResRows, s.N - i0);
+  __shared__ double rmax[kResRows], rz[kResRows], rdl[kResRows];
+  __shared__ float wf[kResRows][kResTile];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kResTile * VST];
+  __shared__ float kt[kResTile][D];
+  __shared__ float dov[kResRows][D], ocv[kResRows][D];
+  __shared__ int jt[kResTile];
+  const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
+  const double* rows = a.srows + ((size_t)bh * s.N + i0) * s.N_kv;
+  const size_t nbase = ((size_t)bh * s.N) * D;
+
+  // row max and normaliser of the coarse softmax, one wave per row
+  for (int r = wave; r < nr; r += kResThreads / 64) {
+    const double* row = rows + (size_t)r * s.N_kv;
+    double mx = -INFINITY;
+    for (int p = lane; p < s.N_kv; p += 64) mx = fmax(mx, row[p]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+    double z = 0.0;
+    for (int p = lane; p < s.N_kv; p += 64) z += exp(row[p] - mx);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+    if (lane == 0) {
+      rmax[r] = mx;
+      rz[r] = z;
+    }
+  }
+  // dOc (res_dosum_kernel); thread: column d of RPT rows
+  const int d = tid % D, rg = tid / D;
+  float acc[RPT];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const int r = rg * RPT + u;
+    dov[r][d] = r < nr ? a.doc[nbase + (size_t)(i0 + r) * D + d] : 0.f;
+    acc[u] = 0.f;
+  }
+
+  // stages the Vc (and Kc) rows of J positions p0 .. p0+63: all of a
+  // thread's 16-byte loads are issued before any LDS store
+  auto stage_keys = [&](int p0, bool with_k) {
+    constexpr int VC = kResTile * D / 8 / kResThreads;   // 16-byte Vc chunks per thread
+    constexpr int KC = kResTile * D / 2 / kResThreads;   // 16-byte Kc chunks (two fp64) per thread
+    if (tid < kResTile) jt[tid] = p0 + tid < s.N_kv ? kept_id(s, ctx_row, p0 + tid) : -1;
+    __syncthreads();
+    uint4 vr[VC];
+#pragma unroll
+    for (int x = 0; x < VC; ++x) {
+      const int c = tid + x * kResThreads, pp = c / (D / 8), k8 = c % (D / 8), j = jt[pp];
+      vr[x] = j >= 0 ? *reinterpret_cast<const uint4*>(a.vcb + nbase + (size_t)j * D + 8 * k8)
+                     : make_uint4(0, 0, 0, 0);
+    }
+    double2 kr[KC];
+    if (with_k) {
+#pragma unroll
+      for (int x = 0; x < KC; ++x) {
+        const int c = tid + x * kResThreads, pp = c / (D / 2), k2 = c % (D / 2), j = jt[pp];
+        kr[x] = j >= 0 ? *reinterpret_cast<const double2*>(a.kc + nbase + (size_t)j * D + 2 * k2)
+                       : make_double2(0.0, 0.0);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < VC; ++x) {
+      const int c = tid + x * kResThreads, pp = c / (D / 8), k8 = c % (D / 8);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&vt[pp * VST + 8 * k8]);
+      dst[0] = vr[x].x;
+      dst[1] = vr[x].y;
+      dst[2] = vr[x].z;
+      dst[3] = vr[x].w;
+    }
+    if (with_k) {
+#pragma unroll
+      for (int x = 0; x < KC; ++x) {
+        const int c = tid + x * kResThreads, pp = c / (D / 2), k2 = c % (D / 2);
+        kt[pp][2 * k2] = (float)kr[x].x;
+        kt[pp][2 * k2 + 1] = (float)kr[x].y;
+      }
+    }
+  };
+
+  // pass 1: O_coarse = sum_p exp(S - max) Vc_p / z, as the forward formed it
+  for (int p0 = 0; p0 < s.N_kv; p0 += kResTile) {
+    __syncthreads();
+    stage_keys(p0, false);
+    for (int c = tid; c < kResRows * kResTile; c += kResThreads) {
+      const int r = c / kResTile, pp = c % kResTile;
+      const bool ok = r < nr && p0 + pp < s.N_kv && jt[pp] >= 0;
+      wf[r][pp] = ok ? (float)exp(rows[(size_t)r * s.N_kv + p0 + pp] - rmax[r]) : 0.f;
+    }
+    __syncthreads();
+    for (int pp = 0; pp < kResTile; ++pp) {
+      const float v = bf16f(vt[pp * VST + d]);
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) acc[u] += wf[rg * RPT + u][pp] * v;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const int r = rg * RPT + u;
+    ocv[r][d] = r < nr ? (float)((double)acc[u] / rz[r]) : 0.f;
+  }
+  __syncthreads();
+  if (tid < kResRows) {
+    double dl = 0.0;
+    for (int k = 0; k < D; ++k) dl += (double)dov[tid][k] * (double)ocv[tid][k];
+    rdl[tid] = dl;
+  }
+
+  // pass 2: dS over the kept blocks (to pc and dsc), dQc = sum_p dS Kc_p
+  float* pc_rows = a.pc + ((size_t)bh * s.N + i0) * s.N_kv;
+  float* ds_rows = a.dsc + ((size_t)bh * s.N + i0) * s.N_kv;
+  const int pp = tid % kResTile, rq = tid / kResTile;   // key-parallel: key pp, rows rq*RQ ..
+  float q[RPT];
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) q[u] = 0.f;
+  for (int p0 = 0; p0 < s.N_kv; p0 += kResTile) {
+    __syncthreads();
+    stage_keys(p0, true);
+    __syncthreads();
+    const int p = p0 + pp;
+    float dot[RQ];
+#pragma unroll
+    for (int u = 0; u < RQ; ++u) dot[u] = 0.f;
+#pragma unroll 8
+    for (int k = 0; k < D; ++k) {
+      const float v = bf16f(vt[pp * VST + k]);
+#pragma unroll
+      for (int u = 0; u < RQ; ++u) dot[u] += dov[rq * RQ + u][k] * v;
+    }
+#pragma unroll
+    for (int u = 0; u < RQ; ++u) {
+      const int r = rq * RQ + u;
+      double ds = 0.0;
+      if (r < nr && p < s.N_kv) {
+        const double P = exp(rows[(size_t)r * s.N_kv + p] - rmax[r]) / rz[r];
+        ds = P * ((double)dot[u] - rdl[r]);
+        pc_rows[(size_t)r * s.N_kv + p] = (float)P;
+        ds_rows[(size_t)r * s.N_kv + p] = (float)ds;
+      }
+      wf[r][pp] = (float)ds;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int x = 0; x < kResTile; ++x) {
+      const float kv = kt[x][d];
+#pragma unroll
+      for (int u = 0; u < RPT; ++u) q[u] += wf[rg * RPT + u][x] * kv;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < RPT; ++u) {
+    const int r = rg * RPT + u;
+    if (r >= nr) continue;
+    const size_t o = nbase + (size_t)(i0 + r) * D + d;
+    a.dqc[o] = q[u] / sqrtf((float)D);
+    a.ocs[o] = ocv[r][d];
   }
 }
 
@@ -448,26 +556,56 @@ __global__ __launch_bounds__(256) void res_col_kernel(BwdArgs a, int accumulate)
   const int bh = blockIdx.y, p0 = blockIdx.x * PT, tid = threadIdx.x;
   const int pl = tid / 4, d0 = (tid % 4) * DPT;
   __shared__ float ds_t[IC][PT], p_t[IC][PT];
-  __shared__ float qc_t[IC][D], do_t[IC][D];
+  __shared__ __attribute__((aligned(16))) float qc_t[IC][D];
+  __shared__ __attribute__((aligned(16))) float do_t[IC][D];
   float dk[DPT], dv[DPT];
 #pragma unroll
   for (int x = 0; x < DPT; ++x) dk[x] = dv[x] = 0.f;
   const size_t rbase = (size_t)bh * s.N;
+  // per chunk of IC rows, every load of a thread is issued before its LDS
+  // stores (dS and P rows in 4-byte words: N_kv need not be a multiple of 4)
+  constexpr int NS = IC * PT / 256, NQ = IC * D / 2 / 256, ND = IC * D / 4 / 256;
   for (int i0 = 0; i0 < s.N; i0 += IC) {
-    __syncthreads();
-    for (int x = tid; x < IC * PT; x += 256) {
-      const int ii = x / PT, pp = x % PT;
+    float dsr[NS], pr[NS];
+    double2 qr[NQ];
+    float4 dr[ND];
+#pragma unroll
+    for (int x = 0; x < NS; ++x) {
+      const int c = tid + x * 256, ii = c / PT, pp = c % PT;
       const bool ok = i0 + ii < s.N && p0 + pp < s.N_kv;
       const size_t o = (rbase + i0 + ii) * s.N_kv + p0 + pp;
-      ds_t[ii][pp] = ok ? a.dsc[o] : 0.f;
-      p_t[ii][pp] = ok ? a.pc[o] : 0.f;
+      dsr[x] = ok ? a.dsc[o] : 0.f;
+      pr[x] = ok ? a.pc[o] : 0.f;
     }
-    for (int x = tid; x < IC * D; x += 256) {
-      const int ii = x / D, dd = x % D;
-      const bool ok = i0 + ii < s.N;
-      const size_t o = (rbase + i0 + ii) * D + dd;
-      qc_t[ii][dd] = ok ? (float)a.qc[o] : 0.f;
-      do_t[ii][dd] = ok ? a.doc[o] : 0.f;
+#pragma unroll
+    for (int x = 0; x < NQ; ++x) {
+      const int c = tid + x * 256, ii = c / (D / 2), k2 = c % (D / 2);
+      qr[x] = i0 + ii < s.N ? *reinterpret_cast<const double2*>(a.qc + (rbase + i0 + ii) * D + 2 * k2)
+                            : make_double2(0.0, 0.0);
+    }
+#pragma unroll
+    for (int x = 0; x < ND; ++x) {
+      const int c = tid + x * 256, ii = c / (D / 4), k4 = c % (D / 4);
+      dr[x] = i0 + ii < s.N ? *reinterpret_cast<const float4*>(a.doc + (rbase + i0 + ii) * D + 4 * k4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < NS; ++x) {
+      const int c = tid + x * 256;
+      ds_t[c / PT][c % PT] = dsr[x];
+      p_t[c / PT][c % PT] = pr[x];
+    }
+#pragma unroll
+    for (int x = 0; x < NQ; ++x) {
+      const int c = tid + x * 256, ii = c / (D / 2), k2 = c % (D / 2);
+      qc_t[ii][2 * k2] = (float)qr[x].x;
+      qc_t[ii][2 * k2 + 1] = (float)qr[x].y;
+    }
+#pragma unroll
+    for (int x = 0; x < ND; ++x) {
+      const int c = tid + x * 256, ii = c / (D / 4), k4 = c % (D / 4);
+      *reinterpret_cast<float4*>(&do_t[ii][4 * k4]) = dr[x];
     }
     __syncthreads();
 #pragma unroll 4
@@ -1116,7 +1254,10 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
   const bool residual = s.gamma != 0.0f;
   if (!residual) a.dqc = a.doc = a.ocs = nullptr;
   if (residual) {
-    res_row_kernel<D><<<dim3(s.N, BH), kResThreads, 0, st>>>(a);
+    res_dosum_kernel<D><<<dim3(s.N, BH), kResThreads, 0, st>>>(a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    res_row_kernel<D><<<dim3((s.N + kResRows - 1) / kResRows, BH), kResThreads, 0, st>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

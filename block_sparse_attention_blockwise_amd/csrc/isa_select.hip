@@ -419,14 +419,22 @@ __global__ __launch_bounds__(kResThreads) void coarse_residual_kernel(IsaShape s
   for (int u = 0; u < RPT; ++u) acc[u] = 0.0f;
   __syncthreads();
   for (int p0 = 0; p0 < s.N_kv; p0 += kResTile) {
-    for (int c = tid; c < kResTile * CPR; c += kResThreads) {
-      const int pp = c / CPR, k = c % CPR, p = p0 + pp;
-      uint4 v = make_uint4(0, 0, 0, 0);
+    // all of a thread's 16-byte loads are issued before its LDS stores
+    constexpr int VC = kResTile * CPR / kResThreads;
+    uint4 vr[VC];
+#pragma unroll
+    for (int x = 0; x < VC; ++x) {
+      const int c = tid + x * kResThreads, pp = c / CPR, k = c % CPR, p = p0 + pp;
+      vr[x] = make_uint4(0, 0, 0, 0);
       if (p < s.N_kv) {
         const int j = kept_block_id(s, ctx_row, p);
-        if (j >= 0 && j < s.N) v = *reinterpret_cast<const uint4*>(vh + (size_t)j * D + 8 * k);
+        if (j >= 0 && j < s.N) vr[x] = *reinterpret_cast<const uint4*>(vh + (size_t)j * D + 8 * k);
       }
-      *reinterpret_cast<uint4*>(&vt[pp][8 * k]) = v;
+    }
+#pragma unroll
+    for (int x = 0; x < VC; ++x) {
+      const int c = tid + x * kResThreads;
+      *reinterpret_cast<uint4*>(&vt[c / CPR][8 * (c % CPR)]) = vr[x];
     }
     for (int c = tid; c < kResRows * kResTile; c += kResThreads) {
       const int r = c / kResTile, pp = c % kResTile, p = p0 + pp;
