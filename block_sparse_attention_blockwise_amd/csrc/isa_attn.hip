@@ -333,12 +333,12 @@ __device__ __forceinline__ void pv_tile(const char* vb, const bf16x8_t (&pb)[QT]
   }
 }
 
-// LOOP: 0 = one LDS buffer per tile, 1 = double buffered, 2 = software
-// pipelined (scores of the next tile overlap the softmax of the current one).
-template <int D, int MODE, int QT, int NWAVES, int LOOP>
-__global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(LOOP == 0 ? 4 : 2)))
+// PIPE: software pipelined (scores of the next tile overlap the softmax of
+// the current one; K double-, V triple-buffered), else one LDS buffer per
+// tile with the latency hidden by the other resident workgroups.
+template <int D, int MODE, int QT, int NWAVES, bool PIPE>
+__global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(PIPE ? 2 : 4)))
 void attn_kernel(AttnArgs a) {
-  constexpr bool PIPE = LOOP == 2;
   constexpr int NT = NWAVES * 64;
   constexpr int KSTR = 2 * D + 32;
   constexpr int VSTR = 2 * D + 32;
@@ -351,8 +351,8 @@ void attn_kernel(AttnArgs a) {
   static_assert(CH >= 1 && (kKeyTile * CPR) % NT == 0, "tile split");
   static_assert(NT % CPR == 0, "chunk column must be fixed per thread");
 
-  constexpr int NKB = LOOP == 0 ? 1 : 2;    // K buffers
-  constexpr int NVB = LOOP == 0 ? 1 : (LOOP == 1 ? 2 : 3);   // V / logit-offset buffers
+  constexpr int NKB = PIPE ? 2 : 1;    // K buffers
+  constexpr int NVB = PIPE ? 3 : 1;    // V / logit-offset buffers
   static_assert(NVB == 1 || NVB == 2 || NVB == 3, "buffers");
   __shared__ __attribute__((aligned(16))) char k_lds[NKB][kKeyTile * KSTR];
   __shared__ __attribute__((aligned(16))) char v_lds[NVB][kKeyTile * VSTR];
@@ -542,27 +542,7 @@ void attn_kernel(AttnArgs a) {
   const int ntiles = a.ntiles;
   bf16x8_t pb[QT][2];
 
-  if (LOOP == 1) {
-    // Double buffered: the loads of tile t+1 are in flight during tile t.
-    ISA_LOAD_TILE(0)
-    ISA_STORE_TILE(0, 0)
-    for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
-      const bool more = t + 1 < ntiles;
-      if (more) { ISA_LOAD_TILE(t + 1) }
-      const bool hb = tile_has_bias<MODE>(tc, t);
-      __syncthreads();
-      float4_t sc[QT][4];
-      qk_tile<D, QT>(k_lds[buf], qf, sc, g, c16);
-      if (hb) apply_logit_offsets<QT>(sc, bias_lds[buf], cscale, g);
-      float mx[QT];
-      row_max<QT>(sc, hb ? 1.0f : cscale, mx);
-      rescale<D, QT>(mx, m, lsum, oacc);
-      exp_pack<QT>(sc, hb ? 1.0f : cscale, m, lsum, pb);
-      pv_tile<D, QT>(v_lds[buf], pb, oacc, g, c16);
-      if (more) { ISA_STORE_TILE(buf ^ 1, buf ^ 1) }
-    }
-  } else if (LOOP == 0) {
+  if (!PIPE) {
     // One LDS buffer; latency is hidden by the other workgroups resident on
     // the compute unit (small register and LDS footprint).
     for (int t = 0; t < ntiles; ++t) {
@@ -685,10 +665,10 @@ void attn_kernel(AttnArgs a) {
       *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = w;
     }
   }
-  if (LOOP != 0 && a.lse != nullptr) save_lse<QT>(a.lse, head, qtok, qval, m, lsum, g);
+  if (PIPE && a.lse != nullptr) save_lse<QT>(a.lse, head, qtok, qval, m, lsum, g);
 }
 
-template <int D, int MODE, int QT, int NWAVES, int LOOP>
+template <int D, int MODE, int QT, int NWAVES, bool PIPE>
 hipError_t launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
   size_t dyn = 0;
   if (MODE == kFlat) {
@@ -696,11 +676,11 @@ hipError_t launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
     // Raise the dynamic LDS limit once per instantiation (host-side only).
     static unsigned long long done = 0;
     const hipError_t attr = isa_ensure_dyn_lds(
-        reinterpret_cast<const void*>(&attn_kernel<D, MODE, QT, NWAVES, LOOP>),
+        reinterpret_cast<const void*>(&attn_kernel<D, MODE, QT, NWAVES, PIPE>),
         (int)(2 * ISA_MAX_NKV * sizeof(int)), &done);
     if (attr != hipSuccess) return attr;
   }
-  attn_kernel<D, MODE, QT, NWAVES, LOOP><<<grid, NWAVES * 64, dyn, st>>>(a);
+  attn_kernel<D, MODE, QT, NWAVES, PIPE><<<grid, NWAVES * 64, dyn, st>>>(a);
   return hipGetLastError();
 }
 
@@ -737,13 +717,10 @@ hipError_t isa_launch_sharp_attn(const IsaShape& s, const uint16_t* Q, const uin
   const int rows = 8 * 32;
   const int blocks_per_wg = rows / s.b;
   dim3 grid((s.n_sharp + blocks_per_wg - 1) / blocks_per_wg, s.B * s.H);
-  return s.D == 128 ? launch<128, kSharp, 2, 8, 2>(a, grid, st)
-                    : launch<64, kSharp, 2, 8, 2>(a, grid, st);
+  return s.D == 128 ? launch<128, kSharp, 2, 8, true>(a, grid, st)
+                    : launch<64, kSharp, 2, 8, true>(a, grid, st);
 }
 
-#ifndef FLAT_LOOP
-#define FLAT_LOOP 0
-#endif
 
 hipError_t isa_launch_flat_attn(const IsaShape& s, const uint16_t* Q, const uint16_t* K,
                                 const uint16_t* V, const uint16_t* kc_bf16,
@@ -765,10 +742,10 @@ hipError_t isa_launch_flat_attn(const IsaShape& s, const uint16_t* Q, const uint
   dim3 grid(s.n_flat, s.B * s.H);
   // one flat block per workgroup, 16 query rows per wave
   if (s.b == 64)
-    return s.D == 128 ? launch<128, kFlat, 1, 4, FLAT_LOOP>(a, grid, st)
-                      : launch<64, kFlat, 1, 4, FLAT_LOOP>(a, grid, st);
-  return s.D == 128 ? launch<128, kFlat, 1, 2, FLAT_LOOP>(a, grid, st)
-                    : launch<64, kFlat, 1, 2, FLAT_LOOP>(a, grid, st);
+    return s.D == 128 ? launch<128, kFlat, 1, 4, false>(a, grid, st)
+                      : launch<64, kFlat, 1, 4, false>(a, grid, st);
+  return s.D == 128 ? launch<128, kFlat, 1, 2, false>(a, grid, st)
+                    : launch<64, kFlat, 1, 2, false>(a, grid, st);
 }
 
 hipError_t isa_launch_dense_attn(int B, int H, int L, int D, const uint16_t* Q,
@@ -785,6 +762,6 @@ hipError_t isa_launch_dense_attn(int B, int H, int L, int D, const uint16_t* Q,
   a.ntiles = (L + kKeyTile - 1) / kKeyTile;
   a.ntiles_plain = L / kKeyTile;
   dim3 grid((L + 255) / 256, B * H);
-  return D == 128 ? launch<128, kDense, 2, 8, 2>(a, grid, st)
-                  : launch<64, kDense, 2, 8, 2>(a, grid, st);
+  return D == 128 ? launch<128, kDense, 2, 8, true>(a, grid, st)
+                  : launch<64, kDense, 2, 8, true>(a, grid, st);
 }
