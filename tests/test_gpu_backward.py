@@ -297,3 +297,59 @@ def test_forward_backward_tiny_edges(dev, L_src, L_ctx, b, a_s, a_f, a_ns):
         _compare("dQ", res["dQ"][0, h], gq)
         _compare("dK", res["dK"][0, h], gk)
         _compare("dV", res["dV"][0, h], gv)
+
+
+def _random_cases(n=24, seed=2024):
+    """Seeded draws over the whole parameter space: batch and heads, lengths
+    (ragged, and L_ctx = 0), D, b, the three ratios with their edge values,
+    gamma and RoPE."""
+    rng = np.random.default_rng(seed)
+    pick = lambda xs: xs[int(rng.integers(len(xs)))]
+    ratio = lambda: float(pick([0.0, 1.0, round(float(rng.uniform()), 3), round(float(rng.uniform()), 3)]))
+    cases = []
+    for k in range(n):
+        L_src = int(rng.integers(1, 1200))
+        L_ctx = int(pick([0, int(rng.integers(1, 1200)), int(rng.integers(1, 1200))]))
+        cases.append(dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), L_src=L_src, L_ctx=L_ctx,
+                          D=int(pick([64, 128])), b=int(pick([32, 64])), a_s=ratio(), a_f=ratio(),
+                          a_ns=ratio(), gamma=float(pick([0.0, 0.0, 0.4, -0.3])),
+                          rope=float(pick([0.0, 10000.0]))))
+    return cases
+
+
+@pytest.mark.parametrize("k,c", list(enumerate(_random_cases())))
+def test_random_shapes_forward_backward(dev, k, c):
+    """Seeded random shapes and options: the forward over every row (selections
+    checked up to the tie band) and every gradient element, the oracle's
+    backward taking the GPU's selections (validated by the forward check)."""
+    from parity_util import compare_head
+    log(f"random case {k}: {c}")
+    p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"], c["a_s"], c["a_f"], c["a_ns"],
+                   c["gamma"], c["rope"])
+    inp = isa_inputs.make_inputs(1000 + k, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    dO_bits, dO_vals = _dO(p, 100 + k)
+    res = _run(p, inp, dO_bits, dev)
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    for bi in range(p.B):
+        for h in range(p.H):
+            Qv, Kv, Vv = (inp[n][1][bi, h] for n in "QKV")
+            if p.rope_base:
+                Qv = isa_oracle.rope(Qv, plan.L_src, plan.L_ctx, p.rope_base)
+                Kv = isa_oracle.rope(Kv, plan.L_src, plan.L_ctx, p.rope_base)
+            gpu = {name: res["sel"][name][bi, h] for name in ("ctx_idx", "sharp_idx", "flat_idx", "flat_exact_idx")}
+            gpu["O"] = res["O"][bi, h]
+            rep = compare_head(plan, Qv, Kv, Vv, gpu,
+                               oracle_result=isa_oracle.isa_head(Qv, Kv, Vv, plan, gamma=p.gamma))
+            log(f"  head ({bi},{h}) forward max-abs {rep['max_abs']:.2e} excused {rep['excused']}")
+            sel = dict(ctx_idx=np.asarray(gpu["ctx_idx"], dtype=np.int64) - plan.N_src,
+                       sharp_idx=np.asarray(gpu["sharp_idx"], dtype=np.int64),
+                       flat_idx=np.asarray(gpu["flat_idx"], dtype=np.int64),
+                       flat_exact_idx=np.asarray(gpu["flat_exact_idx"], dtype=np.int64).reshape(plan.n_flat, plan.k_ns))
+            gq, gk, gv = isa_oracle.isa_head_backward(Qv, Kv, Vv, dO_vals[bi, h], plan, selections=sel,
+                                                      gamma=p.gamma)
+            if p.rope_base:
+                gq = isa_oracle.rope_backward(gq, plan.L_src, plan.L_ctx, p.rope_base)
+                gk = isa_oracle.rope_backward(gk, plan.L_src, plan.L_ctx, p.rope_base)
+            _compare("dQ", res["dQ"][bi, h], gq)
+            _compare("dK", res["dK"][bi, h], gk)
+            _compare("dV", res["dV"][bi, h], gv)
