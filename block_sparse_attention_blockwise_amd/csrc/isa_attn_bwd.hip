@@ -1284,7 +1284,7 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
   {
     BwdArgs k = a;
     if (!pooled && !residual) k.dkc = k.dvc = nullptr;
-const int kpb = 128 / s.b;   // 128 keys per workgroup
+    const int kpb = 128 / s.b;   // 128 keys per workgroup
     dim3 grid((s.N_kv + kpb - 1) / kpb, BH);
     if (s.b == 64) dkv_pc_kernel<D, 64><<<grid, 512, 0, st>>>(k);
     else dkv_pc_kernel<D, 32><<<grid, 512, 0, st>>>(k);
