@@ -137,37 +137,66 @@ __global__ __launch_bounds__(kCtxThreads) void ctx_topk_kernel(IsaShape s, const
                                                                int32_t* __restrict__ ctx_idx,
                                                                double* __restrict__ ctx_score) {
   const int bh = blockIdx.x;
-  __shared__ double part[kCtxThreads];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NW = kCtxThreads / 64;
+  __shared__ double part[kCtxThreads * 2];
   __shared__ double qbar[128];
+  __shared__ double score[ISA_MAX_SEG_BLOCKS];
   __shared__ int scratch[kCtxThreads / 64];
   const int D = s.D;
-  const int parts = kCtxThreads / D;
+  // qbar = sum of the source rows of Qc: 16-byte loads, one partial per
+  // group of rows, the groups then summed in a fixed order
   {
-    const int d = threadIdx.x % D, pp = threadIdx.x / D;
-    double acc = 0.0;
-    for (int i = pp; i < s.N_src; i += parts) acc += qc[((size_t)bh * s.N + i) * D + d];
-    part[threadIdx.x] = acc;
+    const int cpr = D / 2, groups = kCtxThreads / cpr;
+    const int c = tid % cpr, gq = tid / cpr;
+    const double* src = qc + (size_t)bh * s.N * D + 2 * c;
+    double a0 = 0.0, a1 = 0.0;
+#pragma unroll 8
+    for (int i = gq; i < s.N_src; i += groups) {
+      const double2 v = *reinterpret_cast<const double2*>(src + (size_t)i * D);
+      a0 += v.x;
+      a1 += v.y;
+    }
+    part[gq * D + 2 * c] = a0;
+    part[gq * D + 2 * c + 1] = a1;
+    __syncthreads();
+    if (tid < D) {
+      double acc = 0.0;
+      for (int g = 0; g < groups; ++g) acc += part[g * D + tid];
+      qbar[tid] = acc;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (threadIdx.x < D) {
-    double acc = 0.0;
-    for (int pp = 0; pp < parts; ++pp) acc += part[pp * D + threadIdx.x];
-    qbar[threadIdx.x] = acc;
-  }
-  __syncthreads();
+  // r_j = qbar . Kc_j / sqrt(D): D/2 lanes per context block (two fp64 each)
+  // and a butterfly sum across them
   const double sq = sqrt((double)D);
+  {
+    const int sub = D / 2, bpw = 64 / sub;
+    const int sl = lane % sub, sb = lane / sub;
+    const double q0 = qbar[2 * sl], q1 = qbar[2 * sl + 1];
+    const double* kbase = kc + ((size_t)bh * s.N + s.N_src) * D + 2 * sl;
+#pragma unroll 4
+    for (int j0 = wave * bpw; j0 < s.N_ctx; j0 += NW * bpw) {
+      const int j = j0 + sb;
+      double acc = 0.0;
+      if (j < s.N_ctx) {
+        const double2 k = *reinterpret_cast<const double2*>(kbase + (size_t)j * D);
+        acc = fma(q1, k.y, q0 * k.x);
+      }
+      for (int off = 1; off < sub; off <<= 1) acc += __shfl_xor(acc, off, 64);
+      if (sl == 0 && j < s.N_ctx) score[j] = acc / sq;
+    }
+  }
+  __syncthreads();
   unsigned long long key[kCtxIPT];
   bool valid[kCtxIPT], sel[kCtxIPT];
 #pragma unroll
   for (int u = 0; u < kCtxIPT; ++u) {
-    const int j = threadIdx.x * kCtxIPT + u;
+    const int j = tid * kCtxIPT + u;
     valid[u] = j < s.N_ctx;
     key[u] = 0;
     if (valid[u]) {
-      const double* krow = kc + ((size_t)bh * s.N + s.N_src + j) * D;
-      double acc = 0.0;
-      for (int d = 0; d < D; ++d) acc = fma(qbar[d], krow[d], acc);
-      const double r = acc / sq;
+      const double r = score[j];
       if (ctx_score) ctx_score[(size_t)bh * s.N_ctx + j] = r;
       key[u] = order_key(r);
     }
