@@ -353,3 +353,38 @@ def test_random_shapes_forward_backward(dev, k, c):
             _compare("dQ", res["dQ"][bi, h], gq)
             _compare("dK", res["dK"][bi, h], gk)
             _compare("dV", res["dV"][bi, h], gv)
+
+
+def test_maximum_block_counts(dev):
+    """The largest block counts the library accepts: N_kv = 4096 kept blocks
+    (all 3584 source blocks and 512 of the 4096 context blocks, the last one
+    partial), b = 32, D = 64, k_ns = 256 exact blocks per flat block. Every
+    selection and sampled output rows against the oracle, the closed-form
+    gradient sums, and dQ of the sampled rows."""
+    from parity_util import compare_head
+    Ls, Lc, D, b = 3584 * 32, 4096 * 32 - 5, 64, 32
+    p = isa.Params(1, 1, Ls, Lc, D, b, 0.125, 0.5, 0.0625)
+    pl = isa.plan(p)
+    assert pl["N_kv"] == 4096 and pl["N_ctx"] == 4096 and pl["N_src"] == 3584 and pl["k_ns"] == 256
+    log("maximum block counts: inputs")
+    inp = isa_inputs.make_inputs(7, p.B, p.H, Ls, Lc, D)
+    dO_bits, dO_vals = _dO(p, 12)
+    res = _run(p, inp, dO_bits, dev)
+    plan = isa_oracle.make_plan(Ls, Lc, b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    L = Ls + Lc
+    rng = np.random.default_rng(33)
+    rows = np.array(sorted(set(rng.choice(L, size=40, replace=False).tolist()) | {0, Ls - 1, Ls, L - 5, L - 1}))
+    Qv, Kv, Vv = (inp[n][1][0, 0] for n in "QKV")
+    gpu = {name: res["sel"][name][0, 0] for name in ("ctx_idx", "sharp_idx", "flat_idx", "flat_exact_idx")}
+    gpu["O"] = res["O"][0, 0]
+    log("maximum block counts: oracle")
+    rep = compare_head(plan, Qv, Kv, Vv, gpu, rows=rows)
+    log(f"  forward: max-abs {rep['max_abs']:.2e} mean-abs {rep['mean_abs']:.2e} excused {rep['excused']}")
+    sv, sk, so = res["dV"][0, 0].sum(0), res["dK"][0, 0].sum(0), dO_vals[0, 0].astype(np.float64).sum(0)
+    av, ak = np.abs(res["dV"][0, 0]).sum(0), np.abs(res["dK"][0, 0]).sum(0)
+    assert (np.abs(sv - so) <= 0.02 * av + 1e-3).all() and (np.abs(sk) <= 0.02 * ak + 1e-3).all()
+    if rep["excused"]:
+        log("  a selection lies inside the tie band: dQ rows not compared")
+        return
+    ref = isa_oracle.isa_head_dq_rows(Qv, Kv, Vv, dO_vals[0, 0], plan, rows)
+    _compare("dQ rows", res["dQ"][0, 0][rows], ref)
