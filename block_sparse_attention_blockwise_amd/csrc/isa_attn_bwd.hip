@@ -163,6 +163,23 @@ __device__ __forceinline__ void mm_tr(const char* lds, const bf16x8_t (&pk)[NF][
   }
 }
 
+// Scheduling pattern for one mm_rows (RD = 1 LDS read per step) or mm_tr
+// (RD = 2) call: the reads run PF steps ahead of the NF products per step.
+template <int NS, int NF, int RD, int PF, int ID>
+__device__ __forceinline__ void ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, RD * PF, ID);
+#pragma unroll
+  for (int i = 0; i < NS - PF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NF, ID);
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, ID);
+  }
+#pragma unroll
+  for (int i = 0; i < PF; ++i) __builtin_amdgcn_sched_group_barrier(0x008, NF, ID);
+}
+
+// LDS read distance of the dK/dV products (measured: 2 ahead beats 0, 3, 4)
+constexpr int kDkvAhead = 2;
+
 // Rounds an mm_rows result to bf16 in the operand layout mm_tr expects.
 template <int MT, int NF>
 __device__ __forceinline__ void pack_bf16(const float4_t (&x)[NF][MT], bf16x8_t (&pk)[NF][MT / 2]) {
@@ -1081,30 +1098,54 @@ void dkv_pc_kernel(BwdArgs a) {
             kbias[nf] = (kval[nf] && (act_cur < 0 || act_cur == kb[nf])) ? 0.0f : -INFINITY;
           float4_t sc[NF][MT];
           mm_rows<D, MT, NF>(q_lds[cur], fr, sc, g, c16);
+          ahead<KK * MT, NF, 1, kDkvAhead, 1>();
+          bool open = act_cur < 0;   // no key of this wave masked (sharp blocks, full kept blocks)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const float4_t lv = *reinterpret_cast<const float4_t*>(l_lds[cur] + 16 * mt + 4 * g);
+          for (int nf = 0; nf < NF; ++nf) open = open && kval[nf];
+          if (__all(open)) {
 #pragma unroll
-            for (int nf = 0; nf < NF; ++nf)
+            for (int mt = 0; mt < MT; ++mt) {
+              const float4_t lv = *reinterpret_cast<const float4_t*>(l_lds[cur] + 16 * mt + 4 * g);
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                sc[nf][mt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nf][mt][e], cscale, kbias[nf]) - lv[e]);
+              for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  sc[nf][mt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nf][mt][e], cscale, -lv[e]));
+            }
+          } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              const float4_t lv = *reinterpret_cast<const float4_t*>(l_lds[cur] + 16 * mt + 4 * g);
+#pragma unroll
+              for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  sc[nf][mt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nf][mt][e], cscale, kbias[nf]) - lv[e]);
+            }
           }
           bf16x8_t pp[NF][MT / 2];
           pack_bf16<MT, NF>(sc, pp);
+          // the consumer's copy of P: the operand words themselves. Word u of
+          // pp[nf][kc] holds the bf16 pair (2h, 2h+1), h = u % 2, of fragment
+          // mt = 2kc + u / 2: the word the consumer reads at 2 (nf MT + mt) + h.
           uint32_t* px = &pex[i & 1][pair][0][lane];
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              px[(2 * (nf * MT + mt)) * 64] = pack_bf16x2(sc[nf][mt][0], sc[nf][mt][1]);
-              px[(2 * (nf * MT + mt) + 1) * 64] = pack_bf16x2(sc[nf][mt][2], sc[nf][mt][3]);
+            for (int kc = 0; kc < MT / 2; ++kc) {
+              const uint4 w = __builtin_bit_cast(uint4, pp[nf][kc]);
+              px[(2 * nf * MT + 4 * kc) * 64] = w.x;
+              px[(2 * nf * MT + 4 * kc + 1) * 64] = w.y;
+              px[(2 * nf * MT + 4 * kc + 2) * 64] = w.z;
+              px[(2 * nf * MT + 4 * kc + 3) * 64] = w.w;
             }
           mm_tr<D, MT, NF>(d_lds[cur], pp, acc, g, c16);
+          ahead<DT * (MT / 2), NF, 2, kDkvAhead, 2>();
         }
       } else if (i > 0) {
         float4_t dp[NF][MT];
         mm_rows<D, MT, NF>(d_lds[prev], fr, dp, g, c16);
+        ahead<KK * MT, NF, 1, kDkvAhead, 3>();
         const uint32_t* px = &pex[(i - 1) & 1][pair][0][lane];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -1121,6 +1162,7 @@ void dkv_pc_kernel(BwdArgs a) {
         bf16x8_t pd[NF][MT / 2];
         pack_bf16<MT, NF>(dp, pd);
         mm_tr<D, MT, NF>(q_lds[prev], pd, acc, g, c16);
+        ahead<DT * (MT / 2), NF, 2, kDkvAhead, 4>();
       }
       if (more) stage.put(q_lds[next], d_lds[next], l_lds[next], dl_lds[next], tid);
       __syncthreads();
