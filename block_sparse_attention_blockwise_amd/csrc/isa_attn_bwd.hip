@@ -1056,7 +1056,7 @@ void dkv_pc_kernel(BwdArgs a) {
   for (int u = 0; u < KPB; ++u) {
     const int p = pb + u;
     const int c = (s.n_flat > 0 && p < s.N_kv) ? off[p + 1] - off[p] : 0;
-    fb[u + 1] = fb[u] + c;
+    fb[u + 1] = fb[u] + __builtin_amdgcn_readfirstlane(c);   // the same in every lane
   }
   const int total = fb[KPB];
   auto query_at = [&](int i, int& act) -> int {
