@@ -109,12 +109,6 @@ __device__ inline int kept_id(const IsaShape& s, const int32_t* ctx_row, int q) 
   return (j >= s.N_src && j < s.N) ? j : -1;
 }
 
-__device__ inline bool block_is_partial(const IsaShape& s, int j) {
-  int st, n;
-  isa_block_range(s, j, st, n);
-  return n < s.b;
-}
-
 // Where the keys of one tile come from (per workgroup, read-only).
 struct TileCtx {
   const uint16_t* K;      // token rows of this (batch, head)
