@@ -85,14 +85,20 @@ __device__ void block_topk(const unsigned long long (&key)[IPT], const bool (&va
     for (int u = 0; u < IPT; ++u) sel[u] = false;
     return;
   }
-  // Largest threshold T with #{key >= T} >= k: the k-th largest key.
+  // Largest threshold T with #{key >= T} >= k: the k-th largest key. Once
+  // exactly k keys are at or above a trial threshold they are the top k (the
+  // k-th key and everything equal to it lie above it), so the search stops.
   unsigned long long T = 0;
   for (int bit = 63; bit >= 0; --bit) {
     const unsigned long long trial = T | (1ull << bit);
     int c = 0;
 #pragma unroll
     for (int u = 0; u < IPT; ++u) c += (valid[u] && key[u] >= trial) ? 1 : 0;
-    if (block_sum_int<NT>(c, scratch) >= k) T = trial;
+    const int tot = block_sum_int<NT>(c, scratch);
+    if (tot >= k) {
+      T = trial;
+      if (tot == k) break;
+    }
   }
   int gt = 0, ties = 0;
 #pragma unroll
@@ -340,7 +346,10 @@ __device__ inline void wave_topk(const unsigned long long (&key)[IPL], int n, in
     int c = 0;
 #pragma unroll
     for (int u = 0; u < IPL; ++u) c += __popcll(__ballot(lane + 64 * u < n && key[u] >= trial));
-    if (c >= k) T = trial;
+    if (c >= k) {
+      T = trial;
+      if (c == k) break;   // exactly k at or above T: the top k (see block_topk)
+    }
   }
   int gt = 0;
 #pragma unroll
