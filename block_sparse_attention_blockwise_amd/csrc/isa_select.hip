@@ -242,17 +242,29 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(IsaShape s, const doub
     for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
   __syncthreads();
   const int lr = threadIdx.x >> 2, ld = (threadIdx.x & 3) * 4;   // loader: row, 4 dims
-  for (int d0 = 0; d0 < D; d0 += kCoarseDc) {
-    {
-      const int i = i0 + lr;
-      const int g = gid[lr];
+  // the next slice is loaded into registers while the current one is used
+  const int li = i0 + lr, lg = gid[lr];
+  const double* qrow = qc + ((size_t)bh * s.N + (li < s.N ? li : 0)) * D + ld;
+  const double* krow = kc + ((size_t)bh * s.N + (lg >= 0 ? lg : 0)) * D + ld;
+  double2 qn[2], kn[2];
+  auto load = [&](int d0) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        qs[ld + x][lr] = i < s.N ? qc[((size_t)bh * s.N + i) * D + d0 + ld + x] : 0.0;
-        ks[ld + x][lr] = g >= 0 ? kc[((size_t)bh * s.N + g) * D + d0 + ld + x] : 0.0;
-      }
+    for (int x = 0; x < 2; ++x) {
+      qn[x] = li < s.N ? *reinterpret_cast<const double2*>(qrow + d0 + 2 * x) : make_double2(0.0, 0.0);
+      kn[x] = lg >= 0 ? *reinterpret_cast<const double2*>(krow + d0 + 2 * x) : make_double2(0.0, 0.0);
+    }
+  };
+  load(0);
+  for (int d0 = 0; d0 < D; d0 += kCoarseDc) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      qs[ld + 2 * x][lr] = qn[x].x;
+      qs[ld + 2 * x + 1][lr] = qn[x].y;
+      ks[ld + 2 * x][lr] = kn[x].x;
+      ks[ld + 2 * x + 1][lr] = kn[x].y;
     }
     __syncthreads();
+    if (d0 + kCoarseDc < D) load(d0 + kCoarseDc);
 #pragma unroll
     for (int dd = 0; dd < kCoarseDc; ++dd) {
       double a[4], bv[4];
