@@ -140,6 +140,29 @@ __device__ __forceinline__ void mm_rows(const char* lds, const bf16x8_t (&f)[NF]
   }
 }
 
+// mm_rows whose sums start from a per-row value c0[row] (LDS) instead of 0.
+template <int D, int MT, int NF>
+__device__ __forceinline__ void mm_rows_from(const char* lds, const bf16x8_t (&f)[NF][D / 32],
+                                             float4_t (&s)[NF][MT], const float* c0, int g, int c16) {
+  constexpr int STR = 2 * D + 32;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const float4_t c = *reinterpret_cast<const float4_t*>(c0 + 16 * mt + 4 * g);
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) s[nf][mt] = c;
+  }
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(lds + (16 * mt + c16) * STR + (32 * kk + 8 * g) * 2);
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf)
+        s[nf][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, f[nf][kk], s[nf][mt], 0, 0, 0);
+    }
+  }
+}
+
 // acc[nf][dt] += (LDS rows)^T . pk[nf]: the LDS tile (16*MT rows) is read
 // transposed, its rows being the contraction index in the order pack_bf16
 // produces.
@@ -934,7 +957,7 @@ struct QueryStage {
     }
     if (tid < BR) {
       l_lds[tid] = lv;
-      dl_lds[tid] = dv;
+      dl_lds[tid] = -dv;   // stored negated: the dP sums start from it
     }
   }
 };
@@ -961,7 +984,7 @@ __device__ __forceinline__ void kv_block(const char* q_lds, const char* d_lds, c
       for (int e = 0; e < 4; ++e) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nf][mt][e], cscale, kbias[nf]) - lv[e]);
         sc[nf][mt][e] = p;
-        dp[nf][mt][e] = p * (dp[nf][mt][e] - dl[e]);
+        dp[nf][mt][e] = p * (dp[nf][mt][e] + dl[e]);
       }
     }
   }
@@ -1086,7 +1109,10 @@ void dkv_pc_kernel(BwdArgs a) {
     stage.put(q_lds[0], d_lds[0], l_lds[0], dl_lds[0], tid);
     __syncthreads();
     for (int i = 0; i <= total; ++i) {
-      const int cur = i % 3, prev = (i + 2) % 3, next = (i + 1) % 3;
+      int cur = i % 3, prev = (i + 2) % 3, next = (i + 1) % 3, par = i & 1;
+      // opaque buffer indices: one base per buffer and iteration, the rest as
+      // immediate offsets
+      asm volatile("" : "+s"(cur), "+s"(prev), "+s"(next), "+s"(par));
       int act_next = -1;
       const bool more = i + 1 < total;
       if (more) stage.fetch(a, head, query_at(i + 1, act_next), tid);
@@ -1128,7 +1154,7 @@ void dkv_pc_kernel(BwdArgs a) {
           // the consumer's copy of P: the operand words themselves. Word u of
           // pp[nf][kc] holds the bf16 pair (2h, 2h+1), h = u % 2, of fragment
           // mt = 2kc + u / 2: the word the consumer reads at 2 (nf MT + mt) + h.
-          uint32_t* px = &pex[i & 1][pair][0][lane];
+          uint32_t* px = &pex[par][pair][0][lane];
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
@@ -1143,20 +1169,20 @@ void dkv_pc_kernel(BwdArgs a) {
           ahead<DT * (MT / 2), NF, 2, kDkvAhead, 2>();
         }
       } else if (i > 0) {
+        // dP - Delta: the sums start from -Delta of each row
         float4_t dp[NF][MT];
-        mm_rows<D, MT, NF>(d_lds[prev], fr, dp, g, c16);
+        mm_rows_from<D, MT, NF>(d_lds[prev], fr, dp, dl_lds[prev], g, c16);
         ahead<KK * MT, NF, 1, kDkvAhead, 3>();
-        const uint32_t* px = &pex[(i - 1) & 1][pair][0][lane];
+        const uint32_t* px = &pex[par ^ 1][pair][0][lane];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const float4_t dl = *reinterpret_cast<const float4_t*>(dl_lds[prev] + 16 * mt + 4 * g);
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf) {
             const uint32_t u0 = px[(2 * (nf * MT + mt)) * 64], u1 = px[(2 * (nf * MT + mt) + 1) * 64];
             const float p[4] = {__uint_as_float(u0 << 16), __uint_as_float(u0 & 0xffff0000u),
                                 __uint_as_float(u1 << 16), __uint_as_float(u1 & 0xffff0000u)};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dp[nf][mt][e] = p[e] * (dp[nf][mt][e] - dl[e]);
+            for (int e = 0; e < 4; ++e) dp[nf][mt][e] = p[e] * dp[nf][mt][e];
           }
         }
         bf16x8_t pd[NF][MT / 2];
