@@ -48,7 +48,12 @@
  *              allocates or frees memory and never synchronises the host.
  *              All work is enqueued on `stream` (a hipStream_t; NULL = the
  *              default stream); results are valid once the caller
- *              synchronises that stream.
+ *              synchronises that stream. Only kernels are enqueued (no
+ *              memset; copies only for isa_forward's optional debug
+ *              outputs), so a caller may capture isa_forward and
+ *              isa_backward in a HIP graph and replay it on new contents
+ *              of the same buffers, after one call outside the capture
+ *              on the device (that first call sets kernel attributes).
  *   Errors:    every call returns ISA_OK (0) or a negative code. Arguments
  *              are validated on the host before anything is enqueued; on
  *              error nothing is launched or written. No call aborts, throws
