@@ -123,6 +123,9 @@ def plan(p: Params) -> dict:
 
 
 # ------------------------------------------------------------- torch glue
+# Every tensor handed to the library is checked here (device, dtype,
+# contiguity, exact shape): the C entry points receive bare pointers and
+# cannot tell a wrong-sized buffer from a right one.
 def _torch():
     import torch
     return torch
@@ -133,20 +136,56 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _ptr(t) -> int | None:
-    return None if t is None else t.data_ptr()
-
-
-def _check_qkv(p: Params, *ts):
+def _req(name: str, t, shape, dtype, device=None):
+    """Raise unless `t` is a contiguous `dtype` tensor of exactly `shape` on
+    a HIP device (on `device` when given)."""
     torch = _torch()
-    shape = (p.B, p.H, p.L_src + p.L_ctx, p.D)
-    for t in ts:
-        if not (t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous()):
-            raise ValueError("Q, K, V must be contiguous bfloat16 tensors on a HIP device")
-        if tuple(t.shape) != shape:
-            raise ValueError(f"expected shape {shape}, got {tuple(t.shape)}")
-        if t.data_ptr() % 16:
-            raise ValueError("tensor base must be 16-byte aligned")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _req_bytes(name: str, t, nbytes: int, device):
+    """Raise unless `t` is a contiguous device buffer of at least `nbytes`."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes, {nbytes} needed")
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _qkv_shape(p: Params):
+    return (p.B, p.H, p.L_src + p.L_ctx, p.D)
+
+
+def _check_qkv(p: Params, *ts, names="QKV"):
+    torch = _torch()
+    shape = _qkv_shape(p)
+    dev = ts[0].device if ts and isinstance(ts[0], torch.Tensor) else None
+    for name, t in zip(names if len(names) == len(ts) else [f"tensor {k}" for k in range(len(ts))], ts):
+        _req(name, t, shape, torch.bfloat16, dev)
+    return dev
+
+
+def _nz(t) -> int | None:
+    return t.data_ptr() if t.numel() else None
 
 
 def _empty(shape, dtype, device):
@@ -154,16 +193,20 @@ def _empty(shape, dtype, device):
 
 
 def forward(Q, K, V, p: Params, debug: bool = False, out=None, workspace=None):
-    """ISA forward (steps 1-6). Returns O, or (O, debug dict) when debug=True."""
+    """ISA forward (steps 1-6). Returns O, or (O, debug dict) when debug=True.
+    `out` (bf16, Q's shape) and `workspace` (at least plan()["workspace_bytes"]
+    bytes) may be given to avoid allocation."""
     torch = _torch()
-    _check_qkv(p, Q, K, V)
+    dev = _check_qkv(p, Q, K, V)
     pl = plan(p)
-    dev = Q.device
+    if out is not None:
+        _req("out", out, _qkv_shape(p), torch.bfloat16, dev)
     O = out if out is not None else torch.empty_like(Q)
+    if workspace is not None:
+        _req_bytes("workspace", workspace, pl["workspace_bytes"], dev)
     ws = workspace if workspace is not None else _empty((pl["workspace_bytes"],), torch.uint8, dev)
     dbg_t, dbg_c = None, None
     if debug:
-        BH = p.B * p.H
         dbg_t = {
             "qc": _empty((p.B, p.H, pl["N"], p.D), torch.float64, dev),
             "kc": _empty((p.B, p.H, pl["N"], p.D), torch.float64, dev),
@@ -174,10 +217,9 @@ def forward(Q, K, V, p: Params, debug: bool = False, out=None, workspace=None):
             "flat_idx": _empty((p.B, p.H, pl["n_flat"]), torch.int32, dev),
             "flat_exact_idx": _empty((p.B, p.H, pl["n_flat"], pl["k_ns"]), torch.int32, dev),
         }
-        assert BH >= 1
         dbg_c = IsaDebug(**{k: v.data_ptr() for k, v in dbg_t.items()})
     rc = lib().isa_forward(ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(), V.data_ptr(),
-                           O.data_ptr(), ws.data_ptr(), ws.numel(),
+                           O.data_ptr(), ws.data_ptr(), _nbytes(ws),
                            ctypes.byref(dbg_c) if dbg_c is not None else None, _stream(dev))
     _check("isa_forward", rc)
     return (O, dbg_t) if debug else O
@@ -192,25 +234,29 @@ def workspace(p: Params, device):
 def backward(Q, K, V, O, dO, p: Params, workspace, out=None):
     """Gradients (dQ, dK, dV) of sum(dO * O), selections held fixed. Q, K, V, O
     and `workspace` must be those of the forward() call that produced O (its
-    workspace argument, unmodified since)."""
+    workspace argument, unmodified since). `out` = (dQ, dK, dV) buffers, or
+    None to allocate them."""
     torch = _torch()
-    _check_qkv(p, Q, K, V, O, dO)
-    if workspace.numel() < plan(p)["workspace_bytes"]:
-        raise ValueError("workspace smaller than plan()['workspace_bytes']")
+    dev = _check_qkv(p, Q, K, V, O, dO, names=("Q", "K", "V", "O", "dO"))
+    _req_bytes("workspace", workspace, plan(p)["workspace_bytes"], dev)
+    if out is not None:
+        if len(out) != 3:
+            raise ValueError("out must be a (dQ, dK, dV) triple")
+        for name, t in zip(("dQ", "dK", "dV"), out):
+            _req(name, t, _qkv_shape(p), torch.bfloat16, dev)
     dQ, dK, dV = out if out is not None else (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
     _check("isa_backward", lib().isa_backward(
         ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), dO.data_ptr(),
-        dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), workspace.data_ptr(), workspace.numel(),
-        _stream(Q.device)))
+        dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), workspace.data_ptr(), _nbytes(workspace),
+        _stream(dev)))
     return dQ, dK, dV
 
 
 def pool_coarse(Q, K, V, p: Params):
     """Step (1) pooling: returns (qc, kc fp64, kc_bf16, vc_bf16)."""
     torch = _torch()
-    _check_qkv(p, Q, K, V)
+    dev = _check_qkv(p, Q, K, V)
     pl = plan(p)
-    dev = Q.device
     qc = _empty((p.B, p.H, pl["N"], p.D), torch.float64, dev)
     kc = _empty((p.B, p.H, pl["N"], p.D), torch.float64, dev)
     kcb = _empty((p.B, p.H, pl["N"], p.D), torch.bfloat16, dev)
@@ -224,9 +270,8 @@ def pool_coarse(Q, K, V, p: Params):
 def rope_pool_coarse(Q, K, V, p: Params):
     """Decoupled RoPE fused with step (1): returns (Qr, Kr, qc, kc, kc_bf16, vc_bf16)."""
     torch = _torch()
-    _check_qkv(p, Q, K, V)
+    dev = _check_qkv(p, Q, K, V)
     pl = plan(p)
-    dev = Q.device
     Qr = _empty(tuple(Q.shape), torch.bfloat16, dev)
     Kr = _empty(tuple(K.shape), torch.bfloat16, dev)
     qc = _empty((p.B, p.H, pl["N"], p.D), torch.float64, dev)
@@ -237,20 +282,31 @@ def rope_pool_coarse(Q, K, V, p: Params):
     _check("isa_rope_pool_coarse", lib().isa_rope_pool_coarse(
         ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(), V.data_ptr(), Qr.data_ptr(),
         Kr.data_ptr(), qc.data_ptr(), kc.data_ptr(), kcb.data_ptr(), vcb.data_ptr(),
-        ws.data_ptr(), ws.numel(), _stream(dev)))
+        ws.data_ptr(), _nbytes(ws), _stream(dev)))
     return Qr, Kr, qc, kc, kcb, vcb
+
+
+def _check_coarse(p: Params, pl: dict, qc, kc):
+    torch = _torch()
+    shape = (p.B, p.H, pl["N"], p.D)
+    _req("qc", qc, shape, torch.float64)
+    _req("kc", kc, shape, torch.float64, qc.device)
+    return qc.device
+
+
+def _check_ctx(p: Params, pl: dict, ctx_idx, dev):
+    _req("ctx_idx", ctx_idx, (p.B, p.H, pl["k_ctx"]), _torch().int32, dev)
 
 
 def ctx_topk(qc, kc, p: Params):
     """Step (2): returns (ctx_idx int32 global ids, ctx_score fp64)."""
     torch = _torch()
     pl = plan(p)
-    dev = qc.device
+    dev = _check_coarse(p, pl, qc, kc)
     idx = _empty((p.B, p.H, pl["k_ctx"]), torch.int32, dev)
     score = _empty((p.B, p.H, pl["N_ctx"]), torch.float64, dev)
     _check("isa_ctx_topk", lib().isa_ctx_topk(ctypes.byref(p.c()), qc.data_ptr(), kc.data_ptr(),
-                                              _ptr(idx) if idx.numel() else None,
-                                              _ptr(score) if score.numel() else None, _stream(dev)))
+                                              _nz(idx), _nz(score), _stream(dev)))
     return idx, score
 
 
@@ -259,28 +315,32 @@ def sharpness_split(qc, kc, ctx_idx, p: Params):
     (sharpness, sharp_idx, flat_idx, flat_exact_idx)."""
     torch = _torch()
     pl = plan(p)
-    dev = qc.device
+    dev = _check_coarse(p, pl, qc, kc)
+    _check_ctx(p, pl, ctx_idx, dev)
     sharp = _empty((p.B, p.H, pl["N"]), torch.float64, dev)
     si = _empty((p.B, p.H, pl["n_sharp"]), torch.int32, dev)
     fi = _empty((p.B, p.H, pl["n_flat"]), torch.int32, dev)
     ei = _empty((p.B, p.H, pl["n_flat"], pl["k_ns"]), torch.int32, dev)
     ws = _empty((pl["scores_bytes"],), torch.uint8, dev)
-    nz = lambda t: t.data_ptr() if t.numel() else None
     _check("isa_sharpness_split", lib().isa_sharpness_split(
-        ctypes.byref(p.c()), qc.data_ptr(), kc.data_ptr(), nz(ctx_idx), sharp.data_ptr(),
-        nz(si), nz(fi), nz(ei), ws.data_ptr(), ws.numel(), _stream(dev)))
+        ctypes.byref(p.c()), qc.data_ptr(), kc.data_ptr(), _nz(ctx_idx), sharp.data_ptr(),
+        _nz(si), _nz(fi), _nz(ei), ws.data_ptr(), _nbytes(ws), _stream(dev)))
     return sharp, si, fi, ei
 
 
 def sharp_attn(Q, K, V, ctx_idx, sharp_idx, p: Params, out=None):
     """Step (4): writes the sharp rows of `out` (allocated zero if None)."""
     torch = _torch()
-    _check_qkv(p, Q, K, V)
+    dev = _check_qkv(p, Q, K, V)
+    pl = plan(p)
+    _check_ctx(p, pl, ctx_idx, dev)
+    _req("sharp_idx", sharp_idx, (p.B, p.H, pl["n_sharp"]), torch.int32, dev)
+    if out is not None:
+        _req("out", out, _qkv_shape(p), torch.bfloat16, dev)
     O = out if out is not None else torch.zeros_like(Q)
-    nz = lambda t: t.data_ptr() if t.numel() else None
     _check("isa_sharp_attn", lib().isa_sharp_attn(ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(),
-                                                  V.data_ptr(), nz(ctx_idx), nz(sharp_idx),
-                                                  O.data_ptr(), _stream(Q.device)))
+                                                  V.data_ptr(), _nz(ctx_idx), _nz(sharp_idx),
+                                                  O.data_ptr(), _stream(dev)))
     return O
 
 
@@ -288,13 +348,20 @@ def flat_taylor_attn(Q, K, V, kc_bf16, vc_bf16, ctx_idx, flat_idx, flat_exact_id
                      out=None):
     """Step (5): writes the flat rows of `out` (allocated zero if None)."""
     torch = _torch()
-    _check_qkv(p, Q, K, V)
+    dev = _check_qkv(p, Q, K, V)
+    pl = plan(p)
+    _req("kc_bf16", kc_bf16, (p.B, p.H, pl["N"], p.D), torch.bfloat16, dev)
+    _req("vc_bf16", vc_bf16, (p.B, p.H, pl["N"], p.D), torch.bfloat16, dev)
+    _check_ctx(p, pl, ctx_idx, dev)
+    _req("flat_idx", flat_idx, (p.B, p.H, pl["n_flat"]), torch.int32, dev)
+    _req("flat_exact_idx", flat_exact_idx, (p.B, p.H, pl["n_flat"], pl["k_ns"]), torch.int32, dev)
+    if out is not None:
+        _req("out", out, _qkv_shape(p), torch.bfloat16, dev)
     O = out if out is not None else torch.zeros_like(Q)
-    nz = lambda t: t.data_ptr() if t.numel() else None
     _check("isa_flat_taylor_attn", lib().isa_flat_taylor_attn(
         ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(), V.data_ptr(), kc_bf16.data_ptr(),
-        vc_bf16.data_ptr(), nz(ctx_idx), nz(flat_idx), nz(flat_exact_idx), O.data_ptr(),
-        _stream(Q.device)))
+        vc_bf16.data_ptr(), _nz(ctx_idx), _nz(flat_idx), _nz(flat_exact_idx), O.data_ptr(),
+        _stream(dev)))
     return O
 
 
@@ -302,21 +369,27 @@ def coarse_residual(qc, kc, vc_bf16, ctx_idx, O, p: Params):
     """Step (6): adds gamma * O_coarse to every token row of O in place."""
     torch = _torch()
     pl = plan(p)
-    ws = _empty((pl["scores_bytes"],), torch.uint8, O.device)
-    nz = lambda t: t.data_ptr() if t.numel() else None
+    dev = _check_coarse(p, pl, qc, kc)
+    _req("vc_bf16", vc_bf16, (p.B, p.H, pl["N"], p.D), torch.bfloat16, dev)
+    _check_ctx(p, pl, ctx_idx, dev)
+    _req("O", O, _qkv_shape(p), torch.bfloat16, dev)
+    ws = _empty((pl["scores_bytes"],), torch.uint8, dev)
     _check("isa_coarse_residual", lib().isa_coarse_residual(
-        ctypes.byref(p.c()), qc.data_ptr(), kc.data_ptr(), vc_bf16.data_ptr(), nz(ctx_idx),
-        O.data_ptr(), ws.data_ptr(), ws.numel(), _stream(O.device)))
+        ctypes.byref(p.c()), qc.data_ptr(), kc.data_ptr(), vc_bf16.data_ptr(), _nz(ctx_idx),
+        O.data_ptr(), ws.data_ptr(), _nbytes(ws), _stream(dev)))
     return O
 
 
 def dense_attn(Q, K, V, out=None):
     """Dense softmax attention baseline over all tokens, [B,H,L,D] bf16."""
     torch = _torch()
+    if not isinstance(Q, torch.Tensor) or Q.dim() != 4:
+        raise ValueError("Q must be a [B, H, L, D] tensor")
     B, H, L, D = Q.shape
-    for t in (Q, K, V):
-        if not (t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous()) or t.shape != Q.shape:
-            raise ValueError("Q, K, V must be contiguous bfloat16 [B,H,L,D] tensors on a HIP device")
+    for name, t in zip("QKV", (Q, K, V)):
+        _req(name, t, Q.shape, torch.bfloat16, Q.device)
+    if out is not None:
+        _req("out", out, Q.shape, torch.bfloat16, Q.device)
     O = out if out is not None else torch.empty_like(Q)
     _check("isa_dense_attn", lib().isa_dense_attn(B, H, L, D, Q.data_ptr(), K.data_ptr(),
                                                   V.data_ptr(), O.data_ptr(), _stream(Q.device)))

@@ -168,6 +168,23 @@ def test_strerror(isa):
     assert "workspace" in isa.strerror(-3)
 
 
+def test_binding_refuses_host_tensors(isa):
+    """The binding checks every tensor before any library call: host
+    tensors, non-tensors and wrong shapes are refused with an exception."""
+    torch = pytest.importorskip("torch")
+    p = isa.Params(1, 2, 128, 64, 64, 64)
+    x = torch.zeros(1, 2, 192, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        isa.forward(x, x, x, p)
+    with pytest.raises(ValueError, match="HIP device"):
+        isa.dense_attn(x, x, x)
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        isa.forward(x.float().numpy(), x, x, p)
+    with pytest.raises(ValueError, match="HIP device"):
+        isa.ctx_topk(torch.zeros(1, 2, 4, 64, dtype=torch.float64),
+                     torch.zeros(1, 2, 4, 64, dtype=torch.float64), p)
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     import block_sparse_attention_blockwise_amd as isa
     monkeypatch.setattr(isa, "_lib", None)
