@@ -355,6 +355,54 @@ def test_random_shapes_forward_backward(dev, k, c):
             _compare("dV", res["dV"][bi, h], gv)
 
 
+def test_element_offsets_beyond_32_bits(dev):
+    """H = 160 heads of 131072 tokens at D = 128: 2.7e9 elements (5.4 GB) per
+    tensor, so the heads from 128 on start past element 2^31 and byte 2^32.
+    Heads 0, 130 and 159 hold generated data (the others zeros); for each,
+    every selection and sampled output rows against the oracle, the
+    closed-form gradient sums, and dQ of the sampled rows."""
+    from parity_util import compare_head
+    Ls = Lc = 65536
+    D, b, H = 128, 64, 160
+    L = Ls + Lc
+    checked = (0, 130, 159)
+    assert checked[1] * L * D > 2 ** 31 and H * L * D * 2 > 2 ** 32
+    p = isa.Params(1, H, Ls, Lc, D, b, 0.125, 0.5, 0.0625)
+    plan = isa_oracle.make_plan(Ls, Lc, b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    log(f"offsets past 2^31: H={H} L={L} D={D} ({H * L * D / 1e9:.2f}e9 elements per tensor)")
+    Q, K, V, dO = (torch.zeros(1, H, L, D, dtype=torch.bfloat16, device=dev) for _ in range(4))
+    host = {}
+    rng = np.random.default_rng(77)
+    for h in checked:
+        qkv = [isa_inputs.round_to_bf16(x) for x in isa_inputs.make_head(9, 0, h, Ls, Lc, D)]
+        go = isa_inputs.round_to_bf16(rng.standard_normal((L, D)).astype(np.float32))
+        for t, (bits, _) in zip((Q, K, V, dO), qkv + [go]):
+            t[0, h].copy_(bf16_tensor(bits, dev))
+        host[h] = ([v for _, v in qkv], go[1])
+    ws = isa.workspace(p, dev)
+    O, dbg = isa.forward(Q, K, V, p, debug=True, workspace=ws)
+    dQ, dK, dV = isa.backward(Q, K, V, O, dO, p, ws)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy()
+    for h in checked:
+        (Qv, Kv, Vv), dO_vals = host[h]
+        r = np.random.default_rng([34, h])
+        rows = np.array(sorted(set(r.choice(L, size=24, replace=False).tolist()) | {0, Ls - 1, Ls, L - 1}))
+        gpu = {k: dbg[k][0, h].cpu().numpy() for k in ("ctx_idx", "sharp_idx", "flat_idx", "flat_exact_idx")}
+        gpu["O"] = f(O[0, h])
+        rep = compare_head(plan, Qv, Kv, Vv, gpu, rows=rows)
+        log(f"  head {h}: max-abs {rep['max_abs']:.2e} mean-abs {rep['mean_abs']:.2e} excused {rep['excused']}")
+        gv, gk = f(dV[0, h]), f(dK[0, h])
+        sv, sk, so = gv.sum(0), gk.sum(0), dO_vals.astype(np.float64).sum(0)
+        assert (np.abs(sv - so) <= 0.02 * np.abs(gv).sum(0) + 1e-3).all()
+        assert (np.abs(sk) <= 0.02 * np.abs(gk).sum(0) + 1e-3).all()
+        if rep["excused"]:
+            log("  a selection lies inside the tie band: dQ rows not compared")
+            continue
+        ref = isa_oracle.isa_head_dq_rows(Qv, Kv, Vv, dO_vals, plan, rows)
+        _compare(f"head {h} dQ rows", f(dQ[0, h])[rows], ref)
+
+
 def test_maximum_block_counts(dev):
     """The largest block counts the library accepts: N_kv = 4096 kept blocks
     (all 3584 source blocks and 512 of the 4096 context blocks, the last one
