@@ -397,15 +397,29 @@ def sweep_128k(isa, torch, dev, args):
                     pl = isa.plan(p)
                     ws = isa.workspace(p, dev)
                     ms = timed(lambda: isa.forward(Q, K, V, p, out=O, workspace=ws), 3)
+                    # the two attention kernels alone, on this point's selections
+                    _, sel = isa.forward(Q, K, V, p, debug=True, out=O, workspace=ws)
                     del ws
+                    _, _, kcb, vcb = isa.pool_coarse(Q, K, V, p)
+                    sharp_ms = timed(lambda: isa.sharp_attn(Q, K, V, sel["ctx_idx"], sel["sharp_idx"],
+                                                            p, out=O), 3)
+                    flat_ms = timed(lambda: isa.flat_taylor_attn(
+                        Q, K, V, kcb, vcb, sel["ctx_idx"], sel["flat_idx"], sel["flat_exact_idx"],
+                        p, out=O), 3)
+                    del sel, kcb, vcb
                     nf, ns, nkv, kns = pl["n_flat"], pl["n_sharp"], pl["N_kv"], pl["k_ns"]
-                    flop = H * (4 * D * (ns * b) * (nkv * b) + 4 * D * (nf * b) * (kns * b)
-                                + 4 * D * (nf * b) * (nkv - kns) + 2 * D * pl["N"] * nkv)
+                    sharp_flop = H * 4 * D * (ns * b) * (nkv * b)
+                    flat_flop = H * (4 * D * (nf * b) * (kns * b) + 4 * D * (nf * b) * (nkv - kns))
+                    flop = sharp_flop + flat_flop + H * 2 * D * pl["N"] * nkv
                     rows.append({"b": b, "alpha_s": a_s, "alpha_ns": a_ns, "alpha_f": a_f, "ms": ms,
                                  "alg_tflop": flop / 1e12, "tflops": flop / (ms * 1e-3) / 1e12,
-                                 "speedup_vs_dense": dense_ms / ms, "ceiling": dense_flop / flop})
+                                 "speedup_vs_dense": dense_ms / ms, "ceiling": dense_flop / flop,
+                                 "sharp_ms": sharp_ms, "sharp_tflops": sharp_flop / (sharp_ms * 1e-3) / 1e12,
+                                 "flat_ms": flat_ms, "flat_tflops": flat_flop / (flat_ms * 1e-3) / 1e12})
                     log(f"sweep b={b} a_s={a_s} a_ns={a_ns} a_f={a_f}: {ms:.1f} ms, "
-                        f"{dense_ms / ms:.2f}x (ceiling {dense_flop / flop:.2f}x)")
+                        f"{dense_ms / ms:.2f}x (ceiling {dense_flop / flop:.2f}x); sharp {sharp_ms:.1f} ms "
+                        f"{sharp_flop / (sharp_ms * 1e-3) / 1e12:.0f} TFLOP/s, flat {flat_ms:.1f} ms "
+                        f"{flat_flop / (flat_ms * 1e-3) / 1e12:.0f} TFLOP/s")
     print(json.dumps({"sweep_128k": rows, "dense_ms": dense_ms,
                       "dense_tflops": dense_flop / (dense_ms * 1e-3) / 1e12,
                       "config": {"workload": "isa_fwd_128k_tokens_h40_d128_grid"}}), flush=True)

@@ -189,20 +189,20 @@ __device__ inline bool tile_has_bias(const TileCtx& c, int t) {
 }
 
 // ---------------------------------------------------------------- tile math
-// S^T tile: s[qt][mt][j] = K[16mt + 4g + j] . Q[16qt + c] for the 64 keys of
-// the LDS tile at `kb` (raw dot products).
-template <int D, int QT>
+// S^T tile: s[qt][mt][j] = K[16mt + 4g + j] . Q[16qt + c] for the 16*NMT
+// keys of the LDS tile at `kb` (raw dot products).
+template <int D, int QT, int NMT = 4>
 __device__ __forceinline__ void qk_tile(const char* kb, const bf16x8_t (&qf)[QT][D / 32],
-                                        float4_t (&s)[QT][4], int g, int c16) {
+                                        float4_t (&s)[QT][NMT], int g, int c16) {
   constexpr int KSTR = 2 * D + 32;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) s[qt][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < NMT; ++mt) s[qt][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < NMT; ++mt) {
       const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kb + (16 * mt + c16) * KSTR + (32 * kk + 8 * g) * 2);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
@@ -212,11 +212,11 @@ __device__ __forceinline__ void qk_tile(const char* kb, const bf16x8_t (&qf)[QT]
 }
 
 // Turns raw scores into log2-unit logits with the per-key offsets.
-template <int QT>
-__device__ __forceinline__ void apply_logit_offsets(float4_t (&s)[QT][4], const float* bias,
+template <int QT, int NMT = 4>
+__device__ __forceinline__ void apply_logit_offsets(float4_t (&s)[QT][NMT], const float* bias,
                                                     float cscale, int g) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < NMT; ++mt) {
     const float4_t bv = *reinterpret_cast<const float4_t*>(bias + 16 * mt + 4 * g);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
@@ -225,19 +225,31 @@ __device__ __forceinline__ void apply_logit_offsets(float4_t (&s)[QT][4], const 
   }
 }
 
-// Row maximum over the 64 keys of the tile, times `xs` (log2 units).
-template <int QT>
-__device__ __forceinline__ void row_max(const float4_t (&s)[QT][4], float xs, float (&mx)[QT]) {
+// Row maximum over the 16*NMT keys of the tile, times `xs` (log2 units).
+template <int QT, int NMT = 4>
+__device__ __forceinline__ void row_max(const float4_t (&s)[QT][NMT], float xs, float (&mx)[QT]) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float a = __builtin_fmaxf(s[qt][0][0], __builtin_fmaxf(s[qt][0][1], s[qt][0][2]));
-    a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][0][3], s[qt][1][0]));
-    a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][1][1], s[qt][1][2]));
-    a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][1][3], s[qt][2][0]));
-    a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][2][1], s[qt][2][2]));
-    a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][2][3], s[qt][3][0]));
-    a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][3][1], s[qt][3][2]));
-    a = __builtin_fmaxf(a, s[qt][3][3]);
+    float a;
+    if (NMT == 4) {
+      a = __builtin_fmaxf(s[qt][0][0], __builtin_fmaxf(s[qt][0][1], s[qt][0][2]));
+      a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][0][3], s[qt][1][0]));
+      a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][1][1], s[qt][1][2]));
+      a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][1][3], s[qt][2][0]));
+      a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][2][1], s[qt][2][2]));
+      a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][2][3], s[qt][3][0]));
+      a = __builtin_fmaxf(a, __builtin_fmaxf(s[qt][3][1], s[qt][3][2]));
+      a = __builtin_fmaxf(a, s[qt][3][3]);
+    } else {
+      // pairs (i, i+1) of the 4*NMT held values, one three-way max each
+      a = s[qt][0][0];
+#pragma unroll
+      for (int i = 1; i < 4 * NMT; i += 2) {
+        const float x = s[qt][i >> 2][i & 3];
+        a = (i + 1 < 4 * NMT) ? __builtin_fmaxf(a, __builtin_fmaxf(x, s[qt][(i + 1) >> 2][(i + 1) & 3]))
+                              : __builtin_fmaxf(a, x);
+      }
+    }
     a = xor16_max(a);
     a = xor32_max(a);
     mx[qt] = a * xs;
@@ -267,15 +279,15 @@ __device__ __forceinline__ void rescale(const float (&mx)[QT], float (&m)[QT], f
 
 // p = exp2(s*xs - m), rounded to bf16 and packed as the B operand of the PV
 // product; the per-lane partial row sums accumulate the rounded values.
-template <int QT>
-__device__ __forceinline__ void exp_pack(const float4_t (&s)[QT][4], float xs, const float (&m)[QT],
-                                         float (&lsum)[QT], bf16x8_t (&pb)[QT][2]) {
+template <int QT, int NMT = 4>
+__device__ __forceinline__ void exp_pack(const float4_t (&s)[QT][NMT], float xs, const float (&m)[QT],
+                                         float (&lsum)[QT], bf16x8_t (&pb)[QT][NMT / 2]) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const float negm = -m[qt];
     float ps = lsum[qt];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < NMT / 2; ++kc) {
       bf16x2_t h[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -306,9 +318,9 @@ __device__ __forceinline__ void save_lse(float* lse, size_t head, const int (&qt
   }
 }
 
-// O^T += V^T P^T for the 64 keys of the LDS tile at `vb`.
-template <int D, int QT>
-__device__ __forceinline__ void pv_tile(const char* vb, const bf16x8_t (&pb)[QT][2],
+// O^T += V^T P^T for the 16*NMT keys of the LDS tile at `vb`.
+template <int D, int QT, int NMT = 4>
+__device__ __forceinline__ void pv_tile(const char* vb, const bf16x8_t (&pb)[QT][NMT / 2],
                                         float4_t (&o)[QT][D / 16], int g, int c16) {
   constexpr int VSTR = 2 * D + 32;
   const int tr_row = 4 * g + (c16 >> 2);
@@ -316,7 +328,7 @@ __device__ __forceinline__ void pv_tile(const char* vb, const bf16x8_t (&pb)[QT]
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < NMT / 2; ++kc) {
       const short4_t lo = lds_read_tr(vb + (32 * kc + tr_row) * VSTR + (16 * dt + tr_col) * 2);
       const short4_t hi = lds_read_tr(vb + (32 * kc + 16 + tr_row) * VSTR + (16 * dt + tr_col) * 2);
       const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -330,16 +342,23 @@ __device__ __forceinline__ void pv_tile(const char* vb, const bf16x8_t (&pb)[QT]
 // PIPE: software pipelined (scores of the next tile overlap the softmax of
 // the current one; K double-, V triple-buffered), else one LDS buffer per
 // tile with the latency hidden by the other resident workgroups.
-template <int D, int MODE, int QT, int NWAVES, bool PIPE>
-__global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(PIPE ? 2 : 4)))
+// KS = 2 (flat path only): the waves split each key tile in two halves of 32
+// keys, each half with its own online-softmax state for the same rows, merged
+// at the end; twice the waves per workgroup for the same LDS.
+// (The key-split flat kernel is held to three workgroups per compute unit
+// by its LDS, so it may use the registers of three waves per SIMD.)
+template <int D, int MODE, int QT, int NWAVES, bool PIPE, int KS = 1>
+__global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(PIPE ? 2 : (KS == 2 ? 3 : 4))))
 void attn_kernel(AttnArgs a) {
+  static_assert(KS == 1 || (KS == 2 && !PIPE && MODE == kFlat && NWAVES % 2 == 0), "key split");
   constexpr int NT = NWAVES * 64;
   constexpr int KSTR = 2 * D + 32;
   constexpr int VSTR = 2 * D + 32;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int CH = kKeyTile * CPR / NT;    // chunks per thread per tensor
   constexpr int ROWS_W = 16 * QT;
-  constexpr int ROWS = NWAVES * ROWS_W;
+  constexpr int RW = NWAVES / KS;            // waves per key-split half
+  constexpr int ROWS = RW * ROWS_W;
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;
   static_assert(CH >= 1 && (kKeyTile * CPR) % NT == 0, "tile split");
@@ -360,6 +379,7 @@ void attn_kernel(AttnArgs a) {
   const IsaShape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
+  const int rwave = wave % RW, kh = wave / RW;   // row group, key half
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
   // L2). For the sharp and dense paths, whose workgroups of one head stream
   // the same K/V, the dispatch index is remapped so that each XCD receives a
@@ -384,7 +404,7 @@ void attn_kernel(AttnArgs a) {
   bool qval[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const int lr = wave * ROWS_W + 16 * qt + c16;
+    const int lr = rwave * ROWS_W + 16 * qt + c16;
     qval[qt] = false;
     qtok[qt] = 0;
     if (MODE == kDense) {
@@ -538,24 +558,31 @@ void attn_kernel(AttnArgs a) {
 
   if (!PIPE) {
     // One LDS buffer; latency is hidden by the other workgroups resident on
-    // the compute unit (small register and LDS footprint).
+    // the compute unit (small register and LDS footprint). With the key
+    // split each wave takes NMT 16-key sub-tiles of every tile.
+    constexpr int NMT = 4 / KS;
+    const char* kb = k_lds[0] + kh * 16 * NMT * KSTR;
+    const char* vb = v_lds[0] + kh * 16 * NMT * VSTR;
+    const float* bb = bias_lds[0] + kh * 16 * NMT;
     for (int t = 0; t < ntiles; ++t) {
       ISA_LOAD_TILE(t)
       const bool hb = tile_has_bias<MODE>(tc, t);
       if (t > 0) __syncthreads();   // previous tile fully consumed
       ISA_STORE_TILE(0, 0)
       __syncthreads();
-      float4_t sc[QT][4];
-      qk_tile<D, QT>(k_lds[0], qf, sc, g, c16);
-      if (hb) apply_logit_offsets<QT>(sc, bias_lds[0], cscale, g);
+      float4_t sc[QT][NMT];
+      bf16x8_t pk[QT][NMT / 2];
+      qk_tile<D, QT, NMT>(kb, qf, sc, g, c16);
+      if (hb) apply_logit_offsets<QT, NMT>(sc, bb, cscale, g);
       float mx[QT];
-      row_max<QT>(sc, hb ? 1.0f : cscale, mx);
+      row_max<QT, NMT>(sc, hb ? 1.0f : cscale, mx);
       rescale<D, QT>(mx, m, lsum, oacc);
-      exp_pack<QT>(sc, hb ? 1.0f : cscale, m, lsum, pb);
+      exp_pack<QT, NMT>(sc, hb ? 1.0f : cscale, m, lsum, pk);
       // the row statistics are final after the last tile's probabilities:
       // saving them here keeps m from living through the last PV product
-      if (t == ntiles - 1 && a.lse != nullptr) save_lse<QT>(a.lse, head, qtok, qval, m, lsum, g);
-      pv_tile<D, QT>(v_lds[0], pb, oacc, g, c16);
+      if (KS == 1 && t == ntiles - 1 && a.lse != nullptr)
+        save_lse<QT>(a.lse, head, qtok, qval, m, lsum, g);
+      pv_tile<D, QT, NMT>(vb, pk, oacc, g, c16);
     }
   } else {
     // Steady state: the leading tiles, which carry no additive logits.
@@ -643,13 +670,43 @@ void attn_kernel(AttnArgs a) {
 #undef ISA_LOAD_PLAIN
 #undef ISA_STORE_PLAIN
 
+  float ltot[QT];   // softmax denominator of each owned row
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) ltot[qt] = xor32_sum(xor16_sum(lsum[qt]));
+  if (KS == 2) {
+    // merge the two key halves: the second half's waves hand (m, sum, O^T)
+    // over through the K/V buffers, no longer read, and leave
+    __syncthreads();
+    float4_t* xo = reinterpret_cast<float4_t*>(&k_lds[0][0]);
+    float2_t* xm = reinterpret_cast<float2_t*>(&v_lds[0][0]);
+    if (kh == 1) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) xo[((rwave * QT + qt) * DT + dt) * 64 + lane] = oacc[qt][dt];
+        xm[(rwave * QT + qt) * 64 + lane] = float2_t{m[qt], ltot[qt]};
+      }
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float2_t o2 = xm[(rwave * QT + qt) * 64 + lane];
+      const float mm = fmaxf(m[qt], o2.x);
+      const float a1 = __builtin_amdgcn_exp2f(m[qt] - mm), a2 = __builtin_amdgcn_exp2f(o2.x - mm);
+      ltot[qt] = ltot[qt] * a1 + o2.y * a2;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        oacc[qt][dt] = oacc[qt][dt] * a1 + xo[((rwave * QT + qt) * DT + dt) * 64 + lane] * a2;
+      m[qt] = mm;
+    }
+  }
+
   // ---- normalise and write the owned rows
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float lt = xor16_sum(lsum[qt]);
-    lt = xor32_sum(lt);
     if (!qval[qt]) continue;
-    const float inv = 1.0f / lt;
+    const float inv = 1.0f / ltot[qt];
     uint16_t* orow = a.O + (head + qtok[qt]) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -659,10 +716,14 @@ void attn_kernel(AttnArgs a) {
       *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = w;
     }
   }
-  if (PIPE && a.lse != nullptr) save_lse<QT>(a.lse, head, qtok, qval, m, lsum, g);
+  if ((PIPE || KS == 2) && a.lse != nullptr) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+      if (qval[qt] && g == 0) a.lse[head + qtok[qt]] = m[qt] + __log2f(ltot[qt]);
+  }
 }
 
-template <int D, int MODE, int QT, int NWAVES, bool PIPE>
+template <int D, int MODE, int QT, int NWAVES, bool PIPE, int KS = 1>
 hipError_t launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
   size_t dyn = 0;
   if (MODE == kFlat) {
@@ -670,11 +731,11 @@ hipError_t launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
     // Raise the dynamic LDS limit once per instantiation (host-side only).
     static unsigned long long done = 0;
     const hipError_t attr = isa_ensure_dyn_lds(
-        reinterpret_cast<const void*>(&attn_kernel<D, MODE, QT, NWAVES, PIPE>),
+        reinterpret_cast<const void*>(&attn_kernel<D, MODE, QT, NWAVES, PIPE, KS>),
         (int)(2 * ISA_MAX_NKV * sizeof(int)), &done);
     if (attr != hipSuccess) return attr;
   }
-  attn_kernel<D, MODE, QT, NWAVES, PIPE><<<grid, NWAVES * 64, dyn, st>>>(a);
+  attn_kernel<D, MODE, QT, NWAVES, PIPE, KS><<<grid, NWAVES * 64, dyn, st>>>(a);
   return hipGetLastError();
 }
 
@@ -734,12 +795,13 @@ hipError_t isa_launch_flat_attn(const IsaShape& s, const uint16_t* Q, const uint
   const int pooled = s.k_ns < s.N_kv ? (s.N_kv + kKeyTile - 1) / kKeyTile : 0;
   a.ntiles = a.ntiles_exact + pooled;
   dim3 grid(s.n_flat, s.B * s.H);
-  // one flat block per workgroup, 16 query rows per wave
+  // one flat block per workgroup, 16 query rows per wave; a 32-token block
+  // takes two waves per key half
   if (s.b == 64)
     return s.D == 128 ? launch<128, kFlat, 1, 4, false>(a, grid, st)
                       : launch<64, kFlat, 1, 4, false>(a, grid, st);
-  return s.D == 128 ? launch<128, kFlat, 1, 2, false>(a, grid, st)
-                    : launch<64, kFlat, 1, 2, false>(a, grid, st);
+  return s.D == 128 ? launch<128, kFlat, 1, 4, false, 2>(a, grid, st)
+                    : launch<64, kFlat, 1, 4, false, 2>(a, grid, st);
 }
 
 hipError_t isa_launch_dense_attn(int B, int H, int L, int D, const uint16_t* Q,
