@@ -677,12 +677,15 @@ __global__ __launch_bounds__(256) void res_col_kernel(BwdArgs a, int accumulate)
 // blocks all read the tokens of J, so a workgroup takes NWAVES*16*QT rows
 // (several blocks) and the key tiles stream through two LDS buffers (PIPE);
 // a flat block has its own key set (the tokens of E_i, then the pooled keys
-// of J), so it gets a workgroup of its own (NWAVES*16*QT = b).
+// of J), so it gets a workgroup of its own (NWAVES*16*QT/KS = b).
 enum : int { kSharp = 1, kFlat = 2 };
 
-template <int D, int MODE, int QT, int NWAVES, bool PIPE>
+// KS = 2 (flat path, 32-token blocks): the waves split each key tile in two
+// 32-key halves for the same rows; the halves' dQ sums are added at the end.
+template <int D, int MODE, int QT, int NWAVES, bool PIPE, int KS = 1>
 __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(PIPE ? 2 : 3)))
 void dq_kernel(BwdArgs a) {
+  static_assert(KS == 1 || (KS == 2 && !PIPE && MODE == kFlat && NWAVES % 2 == 0), "key split");
   constexpr int NT = NWAVES * 64;
   constexpr int STR = 2 * D + 32;
   constexpr int CPR = D / 8;
@@ -690,7 +693,9 @@ void dq_kernel(BwdArgs a) {
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;
   constexpr int ROWS_W = 16 * QT;
-  constexpr int ROWS = NWAVES * ROWS_W;
+  constexpr int RW = NWAVES / KS;     // waves per key half
+  constexpr int ROWS = RW * ROWS_W;
+  constexpr int MTW = 4 / KS;         // 16-key sub-tiles per wave and tile
   constexpr int NB = PIPE ? 2 : 1;
   static_assert(CH >= 1 && NT % CPR == 0, "tile split");
   __shared__ __attribute__((aligned(16))) char k_lds[NB][kKeyTile * STR];
@@ -701,6 +706,7 @@ void dq_kernel(BwdArgs a) {
   const IsaShape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
+  const int rwave = wave % RW, kh = wave / RW;   // row group, key half
   const int qx = blockIdx.x, bh = blockIdx.y;
   const size_t head = (size_t)bh * s.L;
   const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
@@ -713,7 +719,7 @@ void dq_kernel(BwdArgs a) {
   bf16x8_t qf[QT][KK], df[QT][KK];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const int lr = wave * ROWS_W + 16 * qt + c16;
+    const int lr = rwave * ROWS_W + 16 * qt + c16;
     const int e = MODE == kSharp ? qx * (ROWS >> lb) + (lr >> lb) : qx;
     const int o = MODE == kSharp ? (lr & (b - 1)) : lr;
     qval[qt] = false;
@@ -833,15 +839,18 @@ void dq_kernel(BwdArgs a) {
     }
   };
   auto consume = [&](int buf) {
-    float4_t sc[QT][4], dp[QT][4];
-    mm_rows<D, 4, QT>(k_lds[buf], qf, sc, g, c16);
+    const char* kb = k_lds[buf] + kh * 16 * MTW * STR;   // this wave's keys
+    const char* vb = v_lds[buf] + kh * 16 * MTW * STR;
+    const float* bb = bias_lds[buf] + kh * 16 * MTW;
+    float4_t sc[QT][MTW], dp[QT][MTW];
+    mm_rows<D, MTW, QT>(kb, qf, sc, g, c16);
     // the probabilities need only S: the vector ALUs form them while the
     // matrix cores compute dP (group barriers interleave one MFMA with six
     // VALU ops)
-    mm_rows<D, 4, QT>(v_lds[buf], df, dp, g, c16);
+    mm_rows<D, MTW, QT>(vb, df, dp, g, c16);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const float4_t bv = *reinterpret_cast<const float4_t*>(bias_lds[buf] + 16 * mt + 4 * g);
+    for (int mt = 0; mt < MTW; ++mt) {
+      const float4_t bv = *reinterpret_cast<const float4_t*>(bb + 16 * mt + 4 * g);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -849,19 +858,19 @@ void dq_kernel(BwdArgs a) {
           sc[qt][mt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qt][mt][e], cscale, bv[e]) - lse2[qt]);
     }
 #pragma unroll
-    for (int i = 0; i < 4 * QT * 4 / 2; ++i) {
+    for (int i = 0; i < MTW * QT * 4 / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[qt][mt][e] = sc[qt][mt][e] * (dp[qt][mt][e] - dl[qt]);
-    bf16x8_t pk[QT][2];
-    pack_bf16<4, QT>(sc, pk);
-    mm_tr<D, 4, QT>(k_lds[buf], pk, dq, g, c16);
+    bf16x8_t pk[QT][MTW / 2];
+    pack_bf16<MTW, QT>(sc, pk);
+    mm_tr<D, MTW, QT>(kb, pk, dq, g, c16);
   };
 
   if (PIPE) {
@@ -883,6 +892,25 @@ void dq_kernel(BwdArgs a) {
       __syncthreads();
       consume(0);
     }
+  }
+  if constexpr (KS == 2) {
+    // the second key half's waves hand their dQ sums over through the K
+    // buffer (no longer read) and leave; the first half adds them
+    float4_t* xq = reinterpret_cast<float4_t*>(&k_lds[0][0]);
+    static_assert(RW * QT * DT * 64 * sizeof(float4_t) <= sizeof(k_lds[0]), "merge buffer");
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) xq[((rwave * QT + qt) * DT + dt) * 64 + lane] = dq[qt][dt];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dq[qt][dt] += xq[((rwave * QT + qt) * DT + dt) * 64 + lane];
   }
 
   const float rs = 1.0f / sqrtf((float)D);
@@ -1395,9 +1423,9 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
       dq_kernel<D, kFlat, 1, 4, false><<<grid, 256, dyn, st>>>(q);
     } else {
       static unsigned long long done = 0;
-      const hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 1, 2, false>, max_dyn, &done);
+      const hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 1, 4, false, 2>, max_dyn, &done);
       if (attr != hipSuccess) return attr;
-      dq_kernel<D, kFlat, 1, 2, false><<<grid, 128, dyn, st>>>(q);
+      dq_kernel<D, kFlat, 1, 4, false, 2><<<grid, 256, dyn, st>>>(q);
     }
     e = hipGetLastError();
   }
