@@ -153,6 +153,18 @@ def test_small_shapes_all_rows(dev, D, b):
     _check(p, inp, res, {(0, 0), (0, 1)}, None)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_flat_key_half_without_keys(dev, D):
+    """b = 32 flat blocks split each 64-key tile between two wave pairs. With
+    N_kv = 9 kept blocks and k_ns = 1, the second half of every tile is
+    padding (one 32-token exact block; 9 pooled positions), so that half's
+    softmax state stays empty and must merge with weight 0: every row."""
+    p, inp, res = _small(dev, 256, 256, D, 32, 0.125, 0.5, 0.0625)
+    pl = isa.plan(p)
+    assert pl["N_kv"] == 9 and pl["k_ns"] == 1 and pl["n_flat"] > 0
+    _check(p, inp, res, {(0, 0), (0, 1)}, None)
+
+
 @pytest.mark.parametrize("B,H", [(2, 3), (3, 5)])
 def test_batch_and_odd_head_counts(dev, B, H):
     """B > 1 and head counts that do not fill the XCD remap evenly."""
