@@ -14,7 +14,9 @@
 //   * dense baseline: every token attends every token.
 //
 // Work decomposition (CDNA4, wave64):
-//   * a workgroup owns ROWS query rows; each wave owns 16*QT rows;
+//   * a workgroup owns ROWS query rows; each wave owns 16*QT rows (for
+//     32-token flat blocks two waves share each row group, one per 32-key
+//     half of every tile, and merge their softmax states at the end);
 //   * key tiles of 64 keys are staged in LDS; global loads of a later tile
 //     are in flight while the current one is consumed;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q
