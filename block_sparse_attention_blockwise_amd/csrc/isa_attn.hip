@@ -385,9 +385,12 @@ void attn_kernel(AttnArgs a) {
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
   // L2). For the sharp and dense paths, whose workgroups of one head stream
   // the same K/V, the dispatch index is remapped so that each XCD receives a
-  // contiguous run of tiles, i.e. mostly one head at a time.
+  // contiguous run of tiles, i.e. mostly one head at a time. The flat
+  // kernel for 32-token blocks (twice the blocks, each gathering its own
+  // exact set) takes the same order: it doubles its L2 hit rate when the
+  // exact sets are large; the 64-token flat kernel keeps the plain order.
   int tile_x = blockIdx.x, bh = blockIdx.y;
-  if (MODE != kFlat) {
+  if (MODE != kFlat || KS == 2) {
     const int total = gridDim.x * gridDim.y;
     if ((total & 7) == 0) {
       const int id = blockIdx.x + gridDim.x * blockIdx.y;
