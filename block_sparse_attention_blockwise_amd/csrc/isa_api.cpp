@@ -101,7 +101,8 @@ int make_shape(const isa_params_t* p, IsaShape* s) {
   if (p->B < 1 || p->H < 1 || p->L_src < 1 || p->L_ctx < 0 || p->D < 1 || p->b < 1)
     return ISA_ERR_ARG;
   if (!ratio_ok(p->alpha_s) || !ratio_ok(p->alpha_f) || !ratio_ok(p->alpha_ns)) return ISA_ERR_ARG;
-  if (!std::isfinite(p->gamma)) return ISA_ERR_ARG;
+  // gamma is applied in fp32: it must be finite there too
+  if (!std::isfinite(p->gamma) || std::fabs(p->gamma) > 3.0e38) return ISA_ERR_ARG;
   if (!(p->rope_base == 0.0 || (std::isfinite(p->rope_base) && p->rope_base > 1.0))) return ISA_ERR_ARG;
   if (p->D != 64 && p->D != 128) return ISA_ERR_UNSUPPORTED;
   if ((int64_t)p->B * p->H > kMaxHeads) return ISA_ERR_UNSUPPORTED;

@@ -68,7 +68,8 @@
  *   Limits:    D in {64, 128}; b in {32, 64}; L_src >= 1; L_ctx >= 0;
  *              B, H >= 1; B * H <= 65535; N_src <= 4096; N_ctx <= 4096;
  *              N_kv <= 4096;
- *              ratios in [0, 1] (NaN rejected); gamma finite; rope_base 0 or
+ *              ratios in [0, 1] (NaN rejected); gamma finite with
+ *              |gamma| <= 3e38 (it is applied in fp32); rope_base 0 or
  *              finite and > 1.
  */
 #ifndef ISA_H

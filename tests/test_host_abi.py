@@ -94,7 +94,7 @@ def _params(isa, **kw):
     (dict(L_src=0), -1), (dict(L_ctx=-1), -1), (dict(B=0), -1), (dict(H=0), -1),
     (dict(D=0), -1), (dict(b=0), -1),
     (dict(alpha_s=float("nan")), -1), (dict(alpha_f=1.5), -1), (dict(alpha_ns=-0.1), -1),
-    (dict(gamma=float("nan")), -1), (dict(gamma=float("inf")), -1),
+    (dict(gamma=float("nan")), -1), (dict(gamma=float("inf")), -1), (dict(gamma=1e300), -1),
     (dict(rope_base=float("nan")), -1), (dict(rope_base=float("inf")), -1),
     (dict(rope_base=-10000.0), -1), (dict(rope_base=1.0), -1), (dict(rope_base=0.5), -1),
     (dict(D=96), -2), (dict(D=256), -2), (dict(b=16), -2), (dict(b=128), -2),
