@@ -162,7 +162,8 @@ int isa_pool_coarse(const isa_params_t* p, const void* Q, const void* K, const v
   IsaShape s;
   int rc = make_shape(p, &s);
   if (rc != ISA_OK) return rc;
-  if (!Q || !K || !V || !qc || !kc || !aligned16({Q, K, V})) return ISA_ERR_ARG;
+  if (!Q || !K || !V || !qc || !kc || !aligned16({Q, K, V, qc, kc, kc_bf16, vc_bf16}))
+    return ISA_ERR_ARG;
   return hip_status(isa_launch_pool(s, (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V,
                                     qc, kc, (uint16_t*)kc_bf16, (uint16_t*)vc_bf16,
                                     as_stream(stream)));
@@ -175,7 +176,7 @@ int isa_rope_pool_coarse(const isa_params_t* p, const void* Q, const void* K, co
   int rc = make_shape(p, &s);
   if (rc != ISA_OK) return rc;
   if (!Q || !K || !V || !Qr || !Kr || !qc || !kc || !ws || s.rope_base == 0.0) return ISA_ERR_ARG;
-  if (!aligned16({Q, K, V, Qr, Kr, ws})) return ISA_ERR_ARG;
+  if (!aligned16({Q, K, V, Qr, Kr, ws, qc, kc, kc_bf16, vc_bf16})) return ISA_ERR_ARG;
   if (ws_bytes < rope_table_bytes(s)) return ISA_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
   float2* table = (float2*)ws;
@@ -192,7 +193,7 @@ int isa_ctx_topk(const isa_params_t* p, const double* qc, const double* kc, int3
   IsaShape s;
   int rc = make_shape(p, &s);
   if (rc != ISA_OK) return rc;
-  if (!qc || !kc || (!ctx_idx && s.k_ctx > 0)) return ISA_ERR_ARG;
+  if (!qc || !kc || (!ctx_idx && s.k_ctx > 0) || !aligned16({qc, kc})) return ISA_ERR_ARG;
   return hip_status(isa_launch_ctx_topk(s, qc, kc, ctx_idx, ctx_score, as_stream(stream)));
 }
 
@@ -204,7 +205,8 @@ int isa_sharpness_split(const isa_params_t* p, const double* qc, const double* k
   int rc = make_shape(p, &s);
   if (rc != ISA_OK) return rc;
   if (!qc || !kc || (!ctx_idx && s.k_ctx > 0) || (!sharp_idx && s.n_sharp > 0) ||
-      (!flat_idx && s.n_flat > 0) || (!flat_exact_idx && s.n_flat > 0 && s.k_ns > 0) || !ws)
+      (!flat_idx && s.n_flat > 0) || (!flat_exact_idx && s.n_flat > 0 && s.k_ns > 0) || !ws ||
+      !aligned16({qc, kc, ws}))
     return ISA_ERR_ARG;
   if (ws_bytes < scores_bytes(s)) return ISA_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
@@ -254,7 +256,9 @@ int isa_coarse_residual(const isa_params_t* p, const double* qc, const double* k
   IsaShape s;
   int rc = make_shape(p, &s);
   if (rc != ISA_OK) return rc;
-  if (!qc || !kc || !vc_bf16 || (!ctx_idx && s.k_ctx > 0) || !O || !ws) return ISA_ERR_ARG;
+  if (!qc || !kc || !vc_bf16 || (!ctx_idx && s.k_ctx > 0) || !O || !ws ||
+      !aligned16({qc, kc, vc_bf16, O, ws}))
+    return ISA_ERR_ARG;
   if (ws_bytes < scores_rows_bytes(s)) return ISA_ERR_WORKSPACE;
   if (s.gamma == 0.0f) return ISA_OK;
   hipStream_t st = as_stream(stream);

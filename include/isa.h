@@ -62,9 +62,9 @@
  *              bf16 MFMA with fp32 accumulation; outputs are bf16
  *              (round-to-nearest-even). Identical inputs give bitwise
  *              identical outputs and selections.
- *   Alignment: Q, K, V, O, dO, dQ, dK, dV, Qr, Kr, the bf16 block means and
- *              every workspace must start on a 16-byte boundary (the kernels
- *              move 16-byte vectors); otherwise ISA_ERR_ARG.
+ *   Alignment: Q, K, V, O, dO, dQ, dK, dV, Qr, Kr, the fp64 and bf16 block
+ *              means and every workspace must start on a 16-byte boundary
+ *              (the kernels move 16-byte vectors); otherwise ISA_ERR_ARG.
  *   Limits:    D in {64, 128}; b in {32, 64}; L_src >= 1; L_ctx >= 0;
  *              B, H >= 1; B * H <= 65535; N_src <= 4096; N_ctx <= 4096;
  *              N_kv <= 4096;

@@ -157,6 +157,15 @@ def test_calls_fail_before_launch(isa):
     assert L.isa_sharp_attn(ctypes.byref(p), fake, fake, fake, fake, fake, odd, None) == -1
     assert L.isa_dense_attn(1, 1, 16, 128, fake, odd, fake, fake, None) == -1
     assert L.isa_pool_coarse(ctypes.byref(p), fake, fake, odd, fake, fake, None, None, None) == -1
+    assert L.isa_pool_coarse(ctypes.byref(p), fake, fake, fake, odd, fake, None, None, None) == -1
+    assert L.isa_pool_coarse(ctypes.byref(p), fake, fake, fake, fake, fake, None, odd, None) == -1
+    assert L.isa_ctx_topk(ctypes.byref(p), fake, odd, fake, None, None) == -1
+    assert L.isa_sharpness_split(ctypes.byref(p), odd, fake, fake, fake, fake, fake, fake, fake,
+                                 1 << 40, None) == -1
+    assert L.isa_sharpness_split(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, odd,
+                                 1 << 40, None) == -1
+    assert L.isa_coarse_residual(ctypes.byref(p), fake, fake, fake, fake, odd, fake, 1 << 40, None) == -1
+    assert L.isa_coarse_residual(ctypes.byref(p), fake, fake, odd, fake, fake, fake, 1 << 40, None) == -1
     bad = _params(isa, D=96)
     assert L.isa_forward(ctypes.byref(bad), fake, fake, fake, fake, fake, 1 << 40, None, None) == -2
 
