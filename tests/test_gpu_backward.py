@@ -299,7 +299,7 @@ def test_forward_backward_tiny_edges(dev, L_src, L_ctx, b, a_s, a_f, a_ns):
         _compare("dV", res["dV"][0, h], gv)
 
 
-def _random_cases(n=24, seed=2024):
+def _random_cases(n=24, seed=2024, max_len=1200, max_b=2, max_h=3):
     """Seeded draws over the whole parameter space: batch and heads, lengths
     (ragged, and L_ctx = 0), D, b, the three ratios with their edge values,
     gamma and RoPE."""
@@ -308,16 +308,23 @@ def _random_cases(n=24, seed=2024):
     ratio = lambda: float(pick([0.0, 1.0, round(float(rng.uniform()), 3), round(float(rng.uniform()), 3)]))
     cases = []
     for k in range(n):
-        L_src = int(rng.integers(1, 1200))
-        L_ctx = int(pick([0, int(rng.integers(1, 1200)), int(rng.integers(1, 1200))]))
-        cases.append(dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), L_src=L_src, L_ctx=L_ctx,
+        L_src = int(rng.integers(1, max_len))
+        L_ctx = int(pick([0, int(rng.integers(1, max_len)), int(rng.integers(1, max_len))]))
+        cases.append(dict(B=int(rng.integers(1, max_b + 1)), H=int(rng.integers(1, max_h + 1)),
+                          L_src=L_src, L_ctx=L_ctx,
                           D=int(pick([64, 128])), b=int(pick([32, 64])), a_s=ratio(), a_f=ratio(),
                           a_ns=ratio(), gamma=float(pick([0.0, 0.0, 0.4, -0.3])),
                           rope=float(pick([0.0, 10000.0]))))
     return cases
 
 
-@pytest.mark.parametrize("k,c", list(enumerate(_random_cases())))
+# 24 draws of up to 1200 tokens per segment, and 12 longer ones (up to 3000,
+# one batch, at most two heads, so that the fp64 oracle stays in seconds)
+RANDOM_CASES = (list(enumerate(_random_cases()))
+                + [(100 + k, c) for k, c in enumerate(_random_cases(12, 7, 3000, 1, 2))])
+
+
+@pytest.mark.parametrize("k,c", RANDOM_CASES)
 def test_random_shapes_forward_backward(dev, k, c):
     """Seeded random shapes and options: the forward over every row (selections
     checked up to the tie band) and every gradient element, the oracle's
