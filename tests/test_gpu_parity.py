@@ -165,6 +165,20 @@ def test_flat_key_half_without_keys(dev, D):
     _check(p, inp, res, {(0, 0), (0, 1)}, None)
 
 
+def test_flat_grid_order_with_distinct_heads(dev):
+    """The 32-token flat kernel takes an XCD-contiguous grid order when its
+    workgroup count is a multiple of 8. Here B*H = 8 distinct heads (no tiled
+    copies), b = 32, a large exact set: every selection of every head and
+    every output row of every head against the oracle."""
+    p = isa.Params(2, 4, 1536, 1600, 128, 32, 0.25, 0.75, 0.25)
+    pl = isa.plan(p)
+    assert (pl["n_flat"] * p.B * p.H) % 8 == 0 and pl["k_ns"] > 1
+    inp = _inputs(STREAM["23768_ragged"], p)
+    res = _run(p, inp, dev)
+    heads = {(bi, h) for bi in range(p.B) for h in range(p.H)}
+    _check(p, inp, res, heads, None)
+
+
 @pytest.mark.parametrize("B,H", [(2, 3), (3, 5)])
 def test_batch_and_odd_head_counts(dev, B, H):
     """B > 1 and head counts that do not fill the XCD remap evenly."""
