@@ -266,7 +266,7 @@ def backward_bench(isa, torch, p, Q, K, V, args):
 def torch_sdpa_ms(torch, Q, K, V, reps):
     """Context: PyTorch's own fused attention (flash backend only, no math
     fallback) on the same inputs, unmasked over all L tokens like the dense
-    baseline. None when that backend is unavailable on this build."""
+    baseline. None when the installed PyTorch lacks that backend."""
     from torch.nn.attention import SDPBackend, sdpa_kernel
     try:
         with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
@@ -428,7 +428,8 @@ def sweep_128k(isa, torch, dev, args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU (the operator has no "
+                                   "multi-GPU path); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
