@@ -728,16 +728,22 @@ void attn_kernel(AttnArgs a) {
   }
 }
 
+// The flat kernels take their block tables in dynamic LDS: their limit is
+// raised once per instantiation and device (host-side only).
+template <int D, int MODE, int QT, int NWAVES, bool PIPE, int KS = 1>
+hipError_t prepare() {
+  if (MODE != kFlat) return hipSuccess;
+  static unsigned long long done = 0;
+  return isa_ensure_dyn_lds(reinterpret_cast<const void*>(&attn_kernel<D, MODE, QT, NWAVES, PIPE, KS>),
+                            (int)(2 * ISA_MAX_NKV * sizeof(int)), &done);
+}
+
 template <int D, int MODE, int QT, int NWAVES, bool PIPE, int KS = 1>
 hipError_t launch(const AttnArgs& a, dim3 grid, hipStream_t st) {
   size_t dyn = 0;
   if (MODE == kFlat) {
     dyn = (size_t)(a.s.k_ns + a.s.N_kv) * sizeof(int);
-    // Raise the dynamic LDS limit once per instantiation (host-side only).
-    static unsigned long long done = 0;
-    const hipError_t attr = isa_ensure_dyn_lds(
-        reinterpret_cast<const void*>(&attn_kernel<D, MODE, QT, NWAVES, PIPE, KS>),
-        (int)(2 * ISA_MAX_NKV * sizeof(int)), &done);
+    const hipError_t attr = prepare<D, MODE, QT, NWAVES, PIPE, KS>();
     if (attr != hipSuccess) return attr;
   }
   attn_kernel<D, MODE, QT, NWAVES, PIPE, KS><<<grid, NWAVES * 64, dyn, st>>>(a);
@@ -756,6 +762,14 @@ AttnArgs base_args(const IsaShape& s, const uint16_t* Q, const uint16_t* K, cons
 }
 
 }  // namespace
+
+hipError_t isa_attn_prepare_device() {
+  hipError_t e = prepare<128, kFlat, 1, 4, false>();
+  if (e == hipSuccess) e = prepare<64, kFlat, 1, 4, false>();
+  if (e == hipSuccess) e = prepare<128, kFlat, 1, 4, false, 2>();
+  if (e == hipSuccess) e = prepare<64, kFlat, 1, 4, false, 2>();
+  return e;
+}
 
 hipError_t isa_launch_sharp_attn(const IsaShape& s, const uint16_t* Q, const uint16_t* K,
                                  const uint16_t* V, const int32_t* ctx_idx,

@@ -32,6 +32,8 @@
 //     J, over every flat block; writes dKc, dVc (fp32).
 // With decoupled RoPE the gradients of the rotated Q and K are turned back by
 // the transposed rotation in the epilogues.
+#include <initializer_list>
+
 #include "isa_internal.h"
 
 namespace {
@@ -726,7 +728,7 @@ void dq_kernel(BwdArgs a) {
     qtok[qt] = 0;
     if (e < a.n_q) {
       int st, n;
-      isa_block_range(s, a.qlist[(size_t)bh * a.n_q + e], st, n);
+      isa_block_range_checked(s, a.qlist[(size_t)bh * a.n_q + e], st, n);
       qval[qt] = o < n;
       qtok[qt] = st + (qval[qt] ? o : 0);
     }
@@ -955,7 +957,7 @@ struct QueryStage {
 
   __device__ __forceinline__ void fetch(const BwdArgs& a, size_t head, int jq, int tid) {
     int st, n;
-    isa_block_range(a.s, jq, st, n);
+    isa_block_range_checked(a.s, jq, st, n);
 #pragma unroll
     for (int i = 0; i < CHQ; ++i) {
       const int ch = tid + i * NT, r = ch / CPR, c = ch % CPR;
@@ -1333,9 +1335,13 @@ __global__ __launch_bounds__(256) void dkv_pooled_kernel(BwdArgs a) {
   }
 }
 
-template <typename F>
-hipError_t set_dyn_lds(F* kernel, int bytes, unsigned long long* done) {
-  return isa_ensure_dyn_lds(reinterpret_cast<const void*>(kernel), bytes, done);
+// The dQ kernels take their block tables in dynamic LDS: their limit is
+// raised once per instantiation and device (host-side only).
+template <int D, int MODE, int QT, int NWAVES, bool PIPE, int KS = 1>
+hipError_t prepare_dq() {
+  static unsigned long long done = 0;
+  return isa_ensure_dyn_lds(reinterpret_cast<const void*>(&dq_kernel<D, MODE, QT, NWAVES, PIPE, KS>),
+                            2 * ISA_MAX_NKV * (int)sizeof(int), &done);
 }
 
 template <int D>
@@ -1392,7 +1398,6 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
       if (e != hipSuccess) return e;
     }
   }
-  const int max_dyn = 2 * ISA_MAX_NKV * (int)sizeof(int);
   if (s.n_sharp > 0) {
     BwdArgs q = a;
     q.qlist = a.sharp_idx;
@@ -1401,8 +1406,7 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
     constexpr int ROWS = 8 * 32;   // 8 waves of 32 rows
     dim3 grid((s.n_sharp + ROWS / s.b - 1) / (ROWS / s.b), BH);
     const size_t dyn = (size_t)s.N_kv * sizeof(int);
-    static unsigned long long done = 0;
-    const hipError_t attr = set_dyn_lds(&dq_kernel<D, kSharp, 2, 8, true>, max_dyn, &done);
+    const hipError_t attr = prepare_dq<D, kSharp, 2, 8, true>();
     if (attr != hipSuccess) return attr;
     dq_kernel<D, kSharp, 2, 8, true><<<grid, 512, dyn, st>>>(q);
     e = hipGetLastError();
@@ -1417,13 +1421,11 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
     dim3 grid(s.n_flat, BH);
     const size_t dyn = (size_t)(s.k_ns + s.N_kv) * sizeof(int);
     if (s.b == 64) {
-      static unsigned long long done = 0;
-      const hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 1, 4, false>, max_dyn, &done);
+      const hipError_t attr = prepare_dq<D, kFlat, 1, 4, false>();
       if (attr != hipSuccess) return attr;
       dq_kernel<D, kFlat, 1, 4, false><<<grid, 256, dyn, st>>>(q);
     } else {
-      static unsigned long long done = 0;
-      const hipError_t attr = set_dyn_lds(&dq_kernel<D, kFlat, 1, 4, false, 2>, max_dyn, &done);
+      const hipError_t attr = prepare_dq<D, kFlat, 1, 4, false, 2>();
       if (attr != hipSuccess) return attr;
       dq_kernel<D, kFlat, 1, 4, false, 2><<<grid, 256, dyn, st>>>(q);
     }
@@ -1433,6 +1435,15 @@ hipError_t launch_all(const IsaShape& s, BwdArgs a, const uint16_t* O, hipStream
 }
 
 }  // namespace
+
+hipError_t isa_bwd_prepare_device() {
+  hipError_t e = hipSuccess;
+  for (hipError_t x : {prepare_dq<128, kSharp, 2, 8, true>(), prepare_dq<64, kSharp, 2, 8, true>(),
+                       prepare_dq<128, kFlat, 1, 4, false>(), prepare_dq<64, kFlat, 1, 4, false>(),
+                       prepare_dq<128, kFlat, 1, 4, false, 2>(), prepare_dq<64, kFlat, 1, 4, false, 2>()})
+    if (e == hipSuccess) e = x;
+  return e;
+}
 
 hipError_t isa_launch_backward(const IsaShape& s, const IsaBwdBuffers& w, hipStream_t st) {
   BwdArgs a{};

@@ -30,6 +30,18 @@ __host__ __device__ inline void isa_block_range(const IsaShape& s, int j, int& s
   }
 }
 
+// As isa_block_range, for a block id read from memory (a selection list in
+// a workspace): an id outside [0, N) gives the empty range (start 0, n 0),
+// so no token row of it is ever read.
+__host__ __device__ inline void isa_block_range_checked(const IsaShape& s, int j, int& start, int& n) {
+  if (j < 0 || j >= s.N) {
+    start = 0;
+    n = 0;
+    return;
+  }
+  isa_block_range(s, j, start, n);
+}
+
 // Raises a kernel's dynamic-LDS limit on the current device, once per device
 // (the attribute is per device; `done` is a per-kernel bit set of devices).
 inline hipError_t isa_ensure_dyn_lds(const void* kernel, int bytes, unsigned long long* done) {
@@ -46,6 +58,11 @@ inline hipError_t isa_ensure_dyn_lds(const void* kernel, int bytes, unsigned lon
 // Hard limits of the kernels (see isa.h).
 constexpr int ISA_MAX_SEG_BLOCKS = 4096;
 constexpr int ISA_MAX_NKV = 4096;
+
+// One-time set-up of the current device (dynamic-LDS limits of the
+// attention and dQ kernels); idempotent.
+hipError_t isa_attn_prepare_device();
+hipError_t isa_bwd_prepare_device();
 
 // Launchers: each returns the first HIP error met while enqueueing.
 hipError_t isa_launch_pool(const IsaShape& s, const uint16_t* Q, const uint16_t* K,

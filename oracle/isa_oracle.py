@@ -234,11 +234,29 @@ def exact_sets(S: np.ndarray, J: np.ndarray, flat_idx: np.ndarray, plan: Plan) -
 
 def _topk_gap(scores: np.ndarray, k: int) -> float:
     """Score of the k-th kept element minus the best dropped one (inf if
-    nothing is dropped or nothing kept)."""
+    nothing is dropped or nothing kept). This is the margin by which a top-k
+    selection is decided: below the parity tie band two valid selections may
+    differ."""
     if k <= 0 or k >= scores.size:
         return math.inf
     s = np.sort(np.asarray(scores, dtype=np.float64))[::-1]
     return float(s[k - 1] - s[k])
+
+
+def _split_gap(M: np.ndarray, plan: Plan) -> float:
+    """Margin of the sharp/flat split ([RB] step (3)): the top-n_sharp gap of
+    the normalised sharpness N_src^2 * M_i (0 for a uniform softmax row,
+    N_src - 1 for a one-hot row), inf when every block is on one path."""
+    if plan.n_flat in (0, plan.N):
+        return math.inf
+    return _topk_gap(np.asarray(M, dtype=np.float64) * plan.N_src ** 2, plan.n_sharp)
+
+
+def _exact_gaps(S: np.ndarray, J: np.ndarray, flat_idx: np.ndarray, plan: Plan) -> np.ndarray:
+    """Margin of each flat block's exact-set choice ([RB] step (5)): the
+    top-k_ns gap of its coarse row over the kept blocks J, aligned with
+    flat_idx."""
+    return np.array([_topk_gap(S[i, J], plan.k_ns) for i in flat_idx], dtype=np.float64)
 
 
 # --------------------------------------------------------------- attention
@@ -249,11 +267,14 @@ def _token_range(plan: Plan, j: int) -> np.ndarray:
 
 def _sharp_block_out(Qi, K, V, key_tok, D):
     """Exact softmax attention of Qi over the listed key tokens
-    ([RB] step (4)), two-pass max-shifted."""
-    logits = (Qi @ K[key_tok].T) / math.sqrt(D)
+    ([RB] step (4)), two-pass max-shifted. key_tok None: K and V already hold
+    exactly the listed key rows."""
+    Kx = K if key_tok is None else K[key_tok]
+    Vx = V if key_tok is None else V[key_tok]
+    logits = (Qi @ Kx.T) / math.sqrt(D)
     m = logits.max(axis=1, keepdims=True)
     w = np.exp(logits - m)
-    return (w @ V[key_tok]) / w.sum(axis=1, keepdims=True)
+    return (w @ Vx) / w.sum(axis=1, keepdims=True)
 
 
 def _flat_block_out(Qi, K, V, Kc, Vc, exact_tok, taylor_blocks, n_taylor, D):
@@ -333,11 +354,8 @@ def isa_head(Q, K, V, plan: Plan, selections: dict | None = None, rows=None,
     E = (np.asarray(sel["flat_exact_idx"], dtype=np.int64) if "flat_exact_idx" in sel
          else exact_sets(S, J, flat_idx, plan))
 
-    Mn = M * plan.N_src ** 2
-    ordM = np.sort(Mn)[::-1]
-    split_gap = (math.inf if plan.n_flat in (0, plan.N) else
-                 float(ordM[plan.n_sharp - 1] - ordM[plan.n_sharp]))
-    exact_gaps = np.array([_topk_gap(S[i, J], plan.k_ns) for i in flat_idx])
+    split_gap = _split_gap(M, plan)
+    exact_gaps = _exact_gaps(S, J, flat_idx, plan)
 
     O = np.full((L, D), np.nan)
     if compute_output:
@@ -346,12 +364,13 @@ def isa_head(Q, K, V, plan: Plan, selections: dict | None = None, rows=None,
             want[np.asarray(rows, dtype=np.int64)] = True
         counts = np.asarray(plan.counts, dtype=np.float64)
         J_tok = np.concatenate([_token_range(plan, j) for j in J])
+        KJ, VJ = K[J_tok], V[J_tok]          # the key rows of J, gathered once
         for i in sharp_idx:
             tok = _token_range(plan, i)
             if want is not None:
                 tok = tok[want[tok]]
             if tok.size:
-                O[tok] = _sharp_block_out(Q[tok], K, V, J_tok, D)
+                O[tok] = _sharp_block_out(Q[tok], KJ, VJ, None, D)
         for rix, i in enumerate(flat_idx):
             tok = _token_range(plan, i)
             if want is not None:

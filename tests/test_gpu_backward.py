@@ -327,8 +327,11 @@ RANDOM_CASES = (list(enumerate(_random_cases()))
 @pytest.mark.parametrize("k,c", RANDOM_CASES)
 def test_random_shapes_forward_backward(dev, k, c):
     """Seeded random shapes and options: the forward over every row (selections
-    checked up to the tie band) and every gradient element, the oracle's
-    backward taking the GPU's selections (validated by the forward check)."""
+    checked up to the tie band) and every gradient element. The oracle's
+    backward runs on its own selections; a head whose selections differ
+    inside the tie band (its gradients then have no unique expected value)
+    is left out of the gradient check, and every case compares at least one
+    head."""
     from parity_util import compare_head
     log(f"random case {k}: {c}")
     p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"], c["a_s"], c["a_f"], c["a_ns"],
@@ -337,6 +340,7 @@ def test_random_shapes_forward_backward(dev, k, c):
     dO_bits, dO_vals = _dO(p, 100 + k)
     res = _run(p, inp, dO_bits, dev)
     plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    graded = 0
     for bi in range(p.B):
         for h in range(p.H):
             Qv, Kv, Vv = (inp[n][1][bi, h] for n in "QKV")
@@ -348,18 +352,18 @@ def test_random_shapes_forward_backward(dev, k, c):
             rep = compare_head(plan, Qv, Kv, Vv, gpu,
                                oracle_result=isa_oracle.isa_head(Qv, Kv, Vv, plan, gamma=p.gamma))
             log(f"  head ({bi},{h}) forward max-abs {rep['max_abs']:.2e} excused {rep['excused']}")
-            sel = dict(ctx_idx=np.asarray(gpu["ctx_idx"], dtype=np.int64) - plan.N_src,
-                       sharp_idx=np.asarray(gpu["sharp_idx"], dtype=np.int64),
-                       flat_idx=np.asarray(gpu["flat_idx"], dtype=np.int64),
-                       flat_exact_idx=np.asarray(gpu["flat_exact_idx"], dtype=np.int64).reshape(plan.n_flat, plan.k_ns))
-            gq, gk, gv = isa_oracle.isa_head_backward(Qv, Kv, Vv, dO_vals[bi, h], plan, selections=sel,
-                                                      gamma=p.gamma)
+            if rep["excused"]:
+                log("  a selection lies inside the tie band: gradients of this head not compared")
+                continue
+            gq, gk, gv = isa_oracle.isa_head_backward(Qv, Kv, Vv, dO_vals[bi, h], plan, gamma=p.gamma)
             if p.rope_base:
                 gq = isa_oracle.rope_backward(gq, plan.L_src, plan.L_ctx, p.rope_base)
                 gk = isa_oracle.rope_backward(gk, plan.L_src, plan.L_ctx, p.rope_base)
             _compare("dQ", res["dQ"][bi, h], gq)
             _compare("dK", res["dK"][bi, h], gk)
             _compare("dV", res["dV"][bi, h], gv)
+            graded += 1
+    assert graded > 0, "every head of this case was excused"
 
 
 def test_element_offsets_beyond_32_bits(dev):
@@ -443,3 +447,30 @@ def test_maximum_block_counts(dev):
         return
     ref = isa_oracle.isa_head_dq_rows(Qv, Kv, Vv, dO_vals[0, 0], plan, rows)
     _compare("dQ rows", res["dQ"][0, 0][rows], ref)
+
+
+def test_backward_reads_no_row_of_out_of_range_block_ids(dev):
+    """isa_backward takes the selections the forward saved in the workspace.
+    On a workspace no forward filled (every word -1), every block id it reads
+    is out of range: such ids give empty token ranges, so the call reads no
+    row outside the tensors and completes; a forward then refills the
+    workspace and the backward gives the usual gradients."""
+    p = isa.Params(1, 2, 700, 451, 128, 64, 0.25, 0.5, 0.125)
+    inp = isa_inputs.make_inputs(1, p.B, p.H, p.L_src, p.L_ctx, p.D)
+    Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
+    dO_bits, _ = _dO(p, 3)
+    dO = bf16_tensor(dO_bits, dev)
+    O = torch.zeros_like(Q)
+    ws = isa.workspace(p, dev)
+    ws.fill_(255)
+    log("backward on a workspace of -1 words")
+    isa.backward(Q, K, V, O, dO, p, ws)
+    torch.cuda.synchronize()
+    O = isa.forward(Q, K, V, p, workspace=ws)
+    dQ, dK, dV = isa.backward(Q, K, V, O, dO, p, ws)
+    ws2 = isa.workspace(p, dev)
+    O2 = isa.forward(Q, K, V, p, workspace=ws2)
+    ref = isa.backward(Q, K, V, O2, dO, p, ws2)
+    torch.cuda.synchronize()
+    for a, b in zip((dQ, dK, dV), ref):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -14,7 +14,7 @@ import pytest
 
 import isa_inputs
 from oracle import isa_oracle
-from parity_util import bf16_tensor, compare_head
+from parity_util import OraclePool, bf16_tensor, compare_head
 
 STREAM = {name: w["stream"] for name, w in isa_inputs.WORKLOADS.items()}
 
@@ -88,10 +88,83 @@ def _check(p, inp, res, out_heads, rows_per_head, seed=0, all_sel=True):
             rep = compare_head(plan, Qv, Kv, Vv, _gpu_head(res, bi, h), rows=rows)
             worst = max(worst, rep["max_abs"])
             log(f"  head ({bi},{h}): max-abs {rep['max_abs']:.2e} mean-abs {rep['mean_abs']:.2e} "
-                f"rel-L2 {rep['rel_l2']:.2e} excused {rep['excused']}")
+                f"rel-L2 {rep['rel_l2']:.2e} rows {rep['n_compared'] // p.D} "
+                f"(skipped {rep['n_rows_skipped']}) excused {rep['excused']}")
+            assert rep["n_compared"] > 0, f"head ({bi},{h}): no output row compared"
         else:
             # selections only
             compare_head(plan, Qv, Kv, Vv, _gpu_head(res, bi, h), rows=np.zeros(0, dtype=np.int64))
+    return worst
+
+
+@pytest.fixture(scope="module")
+def pool():
+    with OraclePool() as pl:
+        yield pl
+
+
+def _gpu_inputs(stream, p, dev, gen_heads=None):
+    """Device Q, K, V [B,H,L,D] bf16 of the seeded generator. With gen_heads,
+    only those heads are generated and the other head slots repeat them
+    round-robin (the launch keeps its full shape)."""
+    L = p.L_src + p.L_ctx
+    T = [torch.empty((p.B, p.H, L, p.D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    heads = gen_heads or [(bi, h) for bi in range(p.B) for h in range(p.H)]
+    for (bi, h) in heads:
+        qkv = isa_inputs.make_head(stream, bi, h, p.L_src, p.L_ctx, p.D)
+        for t, x in zip(T, qkv):
+            t[bi, h].copy_(bf16_tensor(isa_inputs.round_to_bf16(x)[0], dev))
+    if gen_heads:
+        for bi in range(p.B):
+            for h in range(p.H):
+                if (bi, h) not in gen_heads:
+                    src = gen_heads[h % len(gen_heads)]
+                    for t in T:
+                        t[bi, h].copy_(t[src])
+    return T
+
+
+def _check_pool(pool, stream, p, Q, K, V, full_heads=(), sampled_heads=(), rows_per_head=0,
+                seed=0, sel_heads=None):
+    """Runs the forward and compares with the oracle in worker processes:
+    every row of `full_heads`, sampled rows of `sampled_heads`, and the
+    selections of `sel_heads` (default: every head). Heads are regenerated
+    by the workers from the seed `stream`."""
+    O, dbg = isa.forward(Q, K, V, p, debug=True)
+    torch.cuda.synchronize()
+    plan = isa_oracle.make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
+    sel = {k: v.cpu().numpy() for k, v in dbg.items()}
+    all_heads = [(bi, h) for bi in range(p.B) for h in range(p.H)]
+    heads = list(dict.fromkeys(list(full_heads) + list(sampled_heads) +
+                               list(all_heads if sel_heads is None else sel_heads)))
+    jobs = []
+    for (bi, h) in heads:
+        gpu = {k: sel[k][bi, h] for k in ("ctx_idx", "sharp_idx", "flat_idx", "flat_exact_idx")}
+        if (bi, h) in full_heads:
+            rows = None
+            gpu["O"] = O[bi, h].float().cpu().numpy()
+        elif (bi, h) in sampled_heads:
+            rows = _sample_rows(plan, rows_per_head, seed + h)
+            gpu["O_rows"] = O[bi, h, torch.from_numpy(rows).to(O.device)].float().cpu().numpy()
+        else:
+            rows = np.zeros(0, dtype=np.int64)
+        jobs.append(dict(stream=stream, bi=bi, h=h, L_src=p.L_src, L_ctx=p.L_ctx, D=p.D, b=p.b,
+                         ratios=(p.alpha_s, p.alpha_f, p.alpha_ns), gpu=gpu, rows=rows))
+    del O
+    out_heads = set(full_heads) | set(sampled_heads)
+    worst, n_rows = 0.0, 0
+    for job, rep in zip(jobs, pool.run(jobs)):
+        hd = (job["bi"], job["h"])
+        if hd in out_heads:
+            assert rep["n_compared"] > 0, f"head {hd}: no output row compared"
+            worst = max(worst, rep["max_abs"])
+            n_rows += rep["n_compared"] // p.D
+            log(f"  head {hd}: max-abs {rep['max_abs']:.2e} mean-abs {rep['mean_abs']:.2e} "
+                f"rel-L2 {rep['rel_l2']:.2e} rows {rep['n_compared'] // p.D} "
+                f"(skipped {rep['n_rows_skipped']}) excused {rep['excused']}")
+        elif rep["excused"]:
+            log(f"  head {hd}: selections excused {rep['excused']}")
+    log(f"  {len(jobs)} heads' selections, {n_rows} output rows compared; worst max-abs {worst:.2e}")
     return worst
 
 
@@ -105,36 +178,46 @@ def test_tiny_all_rows(dev):
     _check(p, inp, res, {(0, 0), (0, 1)}, None)
 
 
+# every row of these heads (all 40 at 16384 tokens), every selection of every head
+FULL_ROW_HEADS = {"16k": [(0, h) for h in range(40)],
+                  "23768_ragged": [(0, h) for h in (0, 7, 17, 23, 31, 39)],
+                  "64k": [(0, h) for h in (0, 13, 26, 39)]}
+
+
 @pytest.mark.parametrize("name", ["16k", "23768_ragged", "64k"])
-def test_workloads(dev, name):
+def test_workloads(dev, pool, name):
     c = isa_inputs.WORKLOADS[name]
     p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"])
     log(f"{name}: generating inputs")
-    inp = _inputs(c["stream"], p)
-    log(f"{name}: forward")
-    res = _run(p, inp, dev)
-    log(f"{name}: checking selections of {p.H} heads, outputs of 3 heads")
-    _check(p, inp, res, {(0, 0), (0, 17), (0, p.H - 1)}, 384, seed=c["stream"])
+    Q, K, V = _gpu_inputs(c["stream"], p, dev)
+    log(f"{name}: forward; every selection of {p.H} heads, every row of {len(FULL_ROW_HEADS[name])}")
+    _check_pool(pool, c["stream"], p, Q, K, V, full_heads=FULL_ROW_HEADS[name])
 
 
-SWEEP = [  # (b, alpha_s, alpha_ns, alpha_f) points of the 131072-token sweep
-    (64, 0.125, 0.0625, 0.5),
-    (32, 0.125, 0.0625, 0.5),
-    (64, 0.25, 0.125, 0.25),
-    (32, 0.25, 0.125, 0.75),
-]
+# the 131072-token grid: every (b, alpha_s, alpha_ns, alpha_f) point
+SWEEP = [(b, a_s, a_ns, a_f) for b in (64, 32) for a_s in (0.125, 0.25) for a_ns in (0.0625, 0.125)
+         for a_f in (0.25, 0.5, 0.75)]
+SWEEP_HEADS = [(0, 3), (0, 29)]
+
+
+@pytest.fixture(scope="module")
+def inputs_128k(dev):
+    c = isa_inputs.WORKLOADS["128k"]
+    p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], c["b"])
+    log("128k: generating two heads, tiled over 40")
+    return _gpu_inputs(c["stream"], p, dev, gen_heads=SWEEP_HEADS)
 
 
 @pytest.mark.parametrize("b,a_s,a_ns,a_f", SWEEP)
-def test_128k_sweep_points(dev, b, a_s, a_ns, a_f):
+def test_128k_sweep_points(dev, pool, inputs_128k, b, a_s, a_ns, a_f):
+    """Full H = 40 launch at 131072 tokens; both generated heads: every
+    selection and sampled output rows against the oracle."""
     c = isa_inputs.WORKLOADS["128k"]
     p = isa.Params(c["B"], c["H"], c["L_src"], c["L_ctx"], c["D"], b, a_s, a_f, a_ns)
-    heads = [(0, 3), (0, 29)]
-    log(f"128k b={b} a_s={a_s} a_ns={a_ns} a_f={a_f}: inputs")
-    inp = _inputs(STREAM["128k"], p, heads=heads, tile_heads=True)
-    log("128k: forward")
-    res = _run(p, inp, dev)
-    _check(p, inp, res, set(heads), 128, seed=b, all_sel=False)
+    log(f"128k b={b} a_s={a_s} a_ns={a_ns} a_f={a_f}: forward")
+    Q, K, V = inputs_128k
+    _check_pool(pool, c["stream"], p, Q, K, V, sampled_heads=SWEEP_HEADS, rows_per_head=128, seed=b,
+                sel_heads=SWEEP_HEADS)
 
 
 # -------------------------------------------------------- special cases
