@@ -21,10 +21,12 @@ ISA_ERR_ARG = -1
 ISA_ERR_UNSUPPORTED = -2
 ISA_ERR_WORKSPACE = -3
 ISA_ERR_HIP = -4
+ISA_ERR_SCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 64 << 20   # ISA_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = ("isa_plan", "isa_pool_coarse", "isa_rope_pool_coarse", "isa_ctx_topk", "isa_sharpness_split",
             "isa_sharp_attn", "isa_flat_taylor_attn", "isa_coarse_residual", "isa_forward",
-            "isa_backward", "isa_dense_attn", "isa_strerror")
+            "isa_backward", "isa_dense_attn", "isa_forward_noalloc", "isa_init", "isa_strerror")
 
 
 class IsaParams(ctypes.Structure):
@@ -40,7 +42,7 @@ class IsaPlan(ctypes.Structure):
                 ("k_ctx", ctypes.c_int32), ("N_kv", ctypes.c_int32), ("n_flat", ctypes.c_int32),
                 ("n_sharp", ctypes.c_int32), ("k_ns", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t), ("scores_bytes", ctypes.c_size_t),
-                ("rope_bytes", ctypes.c_size_t)]
+                ("rope_bytes", ctypes.c_size_t), ("noalloc_bytes", ctypes.c_size_t)]
 
 
 class IsaDebug(ctypes.Structure):
@@ -79,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.isa_forward.argtypes = [P, vp, vp, vp, vp, vp, sz, ctypes.POINTER(IsaDebug), vp]
         L.isa_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.isa_dense_attn.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.isa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(IsaDebug), vp]
+        L.isa_init.argtypes = []
         L.isa_strerror.argtypes = [ctypes.c_int]
         L.isa_strerror.restype = ctypes.c_char_p
         for n in EXPORTED[:-1]:
@@ -223,6 +227,26 @@ def forward(Q, K, V, p: Params, debug: bool = False, out=None, workspace=None):
                            ctypes.byref(dbg_c) if dbg_c is not None else None, _stream(dev))
     _check("isa_forward", rc)
     return (O, dbg_t) if debug else O
+
+
+def forward_noalloc(Q, K, V, p: Params, out=None):
+    """isa_forward_noalloc: the forward with the library's static device
+    scratch as its workspace (nothing allocated by the library; `out` may be
+    given so that nothing is allocated here either). Raises IsaError with
+    ISA_ERR_SCRATCH when plan()["noalloc_bytes"] exceeds the scratch size."""
+    torch = _torch()
+    dev = _check_qkv(p, Q, K, V)
+    if out is not None:
+        _req("out", out, _qkv_shape(p), torch.bfloat16, dev)
+    O = out if out is not None else torch.empty_like(Q)
+    _check("isa_forward_noalloc", lib().isa_forward_noalloc(
+        ctypes.byref(p.c()), Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), None, _stream(dev)))
+    return O
+
+
+def init():
+    """isa_init: one-time set-up of the current device (optional)."""
+    _check("isa_init", lib().isa_init())
 
 
 def workspace(p: Params, device):

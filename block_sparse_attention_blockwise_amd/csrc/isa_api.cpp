@@ -43,7 +43,9 @@ size_t rope_table_bytes(const IsaShape& s) {
   return align256(P * (size_t)(s.D / 2) * sizeof(float2));
 }
 
-Layout make_layout(const IsaShape& s) {
+// with_backward = false: only what the forward's steps read and write (no
+// saved log-sum-exp, no backward scratch), the layout of the static scratch.
+Layout make_layout(const IsaShape& s, bool with_backward = true) {
   const size_t bh = (size_t)s.B * s.H;
   const size_t nd = bh * s.N * s.D;
   auto at_least1 = [](size_t x) { return x ? x : (size_t)1; };
@@ -64,6 +66,12 @@ Layout make_layout(const IsaShape& s) {
   l.qr = o;        o = align256(o + qkr);
   l.kr = o;        o = align256(o + qkr);
   l.rope = o;      o = align256(o + rope_table_bytes(s));
+  if (!with_backward) {
+    l.lse = l.delta = l.dkc = l.dvc = l.ebits = l.inv_off = l.inv_list = 0;
+    l.dqc = l.doc = l.ocs = l.dsc = l.pc = 0;
+    l.total = o;
+    return l;
+  }
   l.lse = o;       o = align256(o + bh * s.L * 4);
   l.delta = o;     o = align256(o + bh * s.L * 4);
   l.dkc = o;       o = align256(o + bh * s.N * s.D * 4);
@@ -131,6 +139,31 @@ int make_shape(const isa_params_t* p, IsaShape* s) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ISA_OK : ISA_ERR_HIP; }
 
+// Workspace of isa_forward_noalloc: a device array of the library, one copy
+// per device (each holds it until the process ends). Host code never passes
+// `scratch` itself to a kernel: its name is a host-side stand-in, and the
+// device copy's address comes from hipGetSymbolAddress, resolved once per
+// device with that device current.
+static __device__ __align__(256) unsigned char scratch[ISA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_addr[kMaxDevices];   // device address of `scratch`, per device (null until resolved)
+
+// The current device's copy of `scratch`.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ISA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return ISA_ERR_UNSUPPORTED;
+  void* ptr = __atomic_load_n(&g_scratch_addr[dev], __ATOMIC_ACQUIRE);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return ISA_ERR_HIP;
+    __atomic_store_n(&g_scratch_addr[dev], ptr, __ATOMIC_RELEASE);   // same value from any thread
+  }
+  *out = ptr;
+  return ISA_OK;
+}
+
 hipStream_t as_stream(void* st) { return reinterpret_cast<hipStream_t>(st); }
 
 // The kernels move token rows and workspace data in 16-byte vectors.
@@ -154,6 +187,7 @@ int isa_plan(const isa_params_t* p, isa_plan_t* out) {
   out->workspace_bytes = make_layout(s).total;
   out->scores_bytes = scores_bytes(s);
   out->rope_bytes = rope_table_bytes(s);
+  out->noalloc_bytes = make_layout(s, false).total;
   return ISA_OK;
 }
 
@@ -269,16 +303,14 @@ int isa_coarse_residual(const isa_params_t* p, const double* qc, const double* k
   return hip_status(e);
 }
 
-int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void* V, void* O,
-                void* ws, size_t ws_bytes, const isa_debug_t* dbg, void* stream) {
-  IsaShape s;
-  int rc = make_shape(p, &s);
-  if (rc != ISA_OK) return rc;
-  if (!Q || !K || !V || !O || !ws || !aligned16({Q, K, V, O, ws})) return ISA_ERR_ARG;
-  const Layout l = make_layout(s);
-  if (ws_bytes < l.total) return ISA_ERR_WORKSPACE;
-  hipStream_t st = as_stream(stream);
-  char* w = (char*)ws;
+}  // extern "C"
+
+namespace {
+
+// Steps (1)-(6) on a validated shape, intermediate data in `w` laid out as
+// `l`; the row log-sum-exp is saved only when the layout has room for it.
+int forward_impl(const IsaShape& s, const void* Q, const void* K, const void* V, void* O, char* w,
+                 const Layout& l, const isa_debug_t* dbg, hipStream_t st) {
   double* qc = (double*)(w + l.qc);
   double* kc = (double*)(w + l.kc);
   uint16_t* kcb = (uint16_t*)(w + l.kcb);
@@ -311,7 +343,7 @@ int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void*
   if (e == hipSuccess) e = isa_launch_sharpness(s, srows, sharp, st);
   if (e == hipSuccess) e = isa_launch_split(s, sharp, sharp_idx, flat_idx, st);
   if (e == hipSuccess) e = isa_launch_flat_topk(s, srows, ctx_idx, flat_idx, exact, st);
-  float* lse = (float*)(w + l.lse);
+  float* lse = l.lse ? (float*)(w + l.lse) : nullptr;
   if (e == hipSuccess) e = isa_launch_sharp_attn(s, q, k, v, ctx_idx, sharp_idx, (uint16_t*)O, lse, st);
   if (e == hipSuccess)
     e = isa_launch_flat_attn(s, q, k, v, kcb, vcb, ctx_idx, flat_idx, exact, (uint16_t*)O, lse, st);
@@ -335,6 +367,43 @@ int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void*
     }
   }
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void* V, void* O,
+                void* ws, size_t ws_bytes, const isa_debug_t* dbg, void* stream) {
+  IsaShape s;
+  int rc = make_shape(p, &s);
+  if (rc != ISA_OK) return rc;
+  if (!Q || !K || !V || !O || !ws || !aligned16({Q, K, V, O, ws})) return ISA_ERR_ARG;
+  const Layout l = make_layout(s);
+  if (ws_bytes < l.total) return ISA_ERR_WORKSPACE;
+  return forward_impl(s, Q, K, V, O, (char*)ws, l, dbg, as_stream(stream));
+}
+
+int isa_forward_noalloc(const isa_params_t* p, const void* Q, const void* K, const void* V,
+                        void* O, const isa_debug_t* dbg, void* stream) {
+  IsaShape s;
+  int rc = make_shape(p, &s);
+  if (rc != ISA_OK) return rc;
+  if (!Q || !K || !V || !O || !aligned16({Q, K, V, O})) return ISA_ERR_ARG;
+  const Layout l = make_layout(s, false);
+  if (l.total > ISA_NOALLOC_SCRATCH_BYTES) return ISA_ERR_SCRATCH;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != ISA_OK) return rc;
+  return forward_impl(s, Q, K, V, O, (char*)ws, l, dbg, as_stream(stream));
+}
+
+int isa_init(void) {
+  hipError_t e = isa_attn_prepare_device();
+  if (e == hipSuccess) e = isa_bwd_prepare_device();
+  if (e != hipSuccess) return ISA_ERR_HIP;
+  void* ws = nullptr;
+  return scratch_address(&ws);
 }
 
 int isa_backward(const isa_params_t* p, const void* Q, const void* K, const void* V,
@@ -400,6 +469,9 @@ const char* isa_strerror(int status) {
     case ISA_ERR_UNSUPPORTED: return "unsupported configuration (D, b or block counts outside the limits)";
     case ISA_ERR_WORKSPACE: return "workspace too small";
     case ISA_ERR_HIP: return "HIP launch or copy failed";
+    case ISA_ERR_SCRATCH:
+      return "request needs more than the library's static scratch (ISA_NOALLOC_SCRATCH_BYTES); "
+             "use isa_forward with a caller workspace";
     default: return "unknown status";
   }
 }

@@ -52,12 +52,20 @@
  *              memset; copies only for isa_forward's optional debug
  *              outputs), so a caller may capture isa_forward and
  *              isa_backward in a HIP graph and replay it on new contents
- *              of the same buffers, after one call outside the capture
- *              on the device (that first call sets kernel attributes).
+ *              of the same buffers, after isa_init() or one call outside
+ *              the capture on the device (that sets kernel attributes).
  *   Errors:    every call returns ISA_OK (0) or a negative code. Arguments
  *              are validated on the host before anything is enqueued; on
- *              error nothing is launched or written. No call aborts, throws
- *              or keeps global mutable state.
+ *              error nothing is launched or written. No call aborts or
+ *              throws.
+ *   State:     the library keeps two things per device, each set once and
+ *              never changed after: that the attention kernels' dynamic-LDS
+ *              limit has been raised, and the device address of its static
+ *              scratch array (used only by isa_forward_noalloc, whose
+ *              contents persist from one such call to the next). Both are set
+ *              by isa_init() or by the first call that needs them on that
+ *              device; the flags are atomic, so calls from several host
+ *              threads are safe. Nothing else persists between calls.
  *   Numerics:  pooling and every selection score run in fp64; attention uses
  *              bf16 MFMA with fp32 accumulation; outputs are bf16
  *              (round-to-nearest-even). Identical inputs give bitwise
@@ -93,6 +101,12 @@ extern "C" {
 #define ISA_ERR_UNSUPPORTED (-2)  /* valid request outside the limits above */
 #define ISA_ERR_WORKSPACE (-3)    /* workspace smaller than isa_plan says */
 #define ISA_ERR_HIP (-4)          /* a HIP launch or copy failed */
+#define ISA_ERR_SCRATCH (-5)      /* isa_forward_noalloc: the request needs more
+                                     than ISA_NOALLOC_SCRATCH_BYTES */
+
+/* Size of the device array that isa_forward_noalloc uses as its workspace
+ * (one copy per device, held until the process ends): 64 MiB. */
+#define ISA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef struct {
   int32_t B, H;        /* batch, heads */
@@ -115,6 +129,8 @@ typedef struct {
   size_t workspace_bytes; /* device workspace isa_forward needs */
   size_t scores_bytes;    /* workspace isa_sharpness_split needs */
   size_t rope_bytes;      /* workspace isa_rope_pool_coarse needs (0 if RoPE off) */
+  size_t noalloc_bytes;   /* scratch isa_forward_noalloc needs (it refuses the
+                             call when this exceeds ISA_NOALLOC_SCRATCH_BYTES) */
 } isa_plan_t;
 
 /* Optional device buffers isa_forward fills when non-NULL (debug and tests). */
@@ -198,6 +214,30 @@ ISA_API int isa_coarse_residual(const isa_params_t* p, const double* qc, const d
  * plan.workspace_bytes of device memory; `dbg` may be NULL. */
 ISA_API int isa_forward(const isa_params_t* p, const void* Q, const void* K, const void* V, void* O,
                 void* ws, size_t ws_bytes, const isa_debug_t* dbg, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): isa_forward
+ * with the workspace taken from a device array inside the library,
+ * ISA_NOALLOC_SCRATCH_BYTES bytes per device, instead of a caller buffer. The
+ * caller still passes Q, K, V and O (and optional dbg buffers). The call
+ * allocates nothing (no hipMalloc/hipFree; only kernels, plus copies when dbg
+ * is given). Refused with ISA_ERR_SCRATCH when plan.noalloc_bytes exceeds
+ * ISA_NOALLOC_SCRATCH_BYTES (e.g. B = 1, H = 40, D = 128, b = 64 fits up to
+ * 16384 tokens). The row log-sum-exp is not saved, so isa_backward cannot
+ * follow this call. Every call on one device shares that device's array:
+ * calls that overlap in time on one device (different streams, or host
+ * threads without ordering) race and give undefined results; calls ordered
+ * on one stream are safe. Nothing in the array needs to start at zero (every
+ * value a step reads was written by an earlier step of the same call). */
+ISA_API int isa_forward_noalloc(const isa_params_t* p, const void* Q, const void* K,
+                                const void* V, void* O, const isa_debug_t* dbg, void* stream);
+
+/* Optional one-time set-up of the current device (see State above): raises
+ * the kernels' dynamic-LDS limits and resolves the static scratch address.
+ * Idempotent. Returns ISA_ERR_HIP when no device is usable. Calling it before
+ * capturing library calls in a HIP graph makes the first captured call
+ * equivalent to later ones. */
+ISA_API int isa_init(void);
 
 /* Backward pass (the operator is trainable end to end: rainbus.top summary,
  * Core method and Novelty (c)). Gradients of sum(dO * O) with respect to

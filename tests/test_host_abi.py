@@ -46,7 +46,8 @@ def test_binding_declares_every_signature(isa):
     for name, args in re.findall(r"ISA_API\s+[\w\s\*]+?\b(isa_\w+)\s*\(([^)]*)\)", txt):
         fn = getattr(isa.lib(), name)
         assert fn.argtypes is not None, name
-        assert len(fn.argtypes) == len([a for a in args.split(",") if a.strip()]), name
+        params = [a for a in args.split(",") if a.strip() and a.strip() != "void"]
+        assert len(fn.argtypes) == len(params), name
 
 
 def test_plan_matches_oracle_counts(isa):
@@ -168,10 +169,46 @@ def test_calls_fail_before_launch(isa):
     assert L.isa_coarse_residual(ctypes.byref(p), fake, fake, odd, fake, fake, fake, 1 << 40, None) == -1
     bad = _params(isa, D=96)
     assert L.isa_forward(ctypes.byref(bad), fake, fake, fake, fake, fake, 1 << 40, None, None) == -2
+    # the allocation-free forward: arguments first, then the static scratch size
+    assert L.isa_forward_noalloc(ctypes.byref(p), fake, None, fake, fake, None, None) == -1
+    assert L.isa_forward_noalloc(ctypes.byref(p), fake, fake, odd, fake, None, None) == -1
+    assert L.isa_forward_noalloc(ctypes.byref(bad), fake, fake, fake, fake, None, None) == -2
+
+
+def test_noalloc_scratch_limit(isa):
+    """isa_plan reports the scratch the allocation-free forward needs (the
+    forward's own buffers, no backward state); requests beyond
+    ISA_NOALLOC_SCRATCH_BYTES are refused with ISA_ERR_SCRATCH before any
+    HIP call."""
+    L = isa.lib()
+    fake = 0x1000
+    hdr = open(os.path.join(ROOT, "include", "isa.h")).read()
+    m = re.search(r"#define ISA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == isa.NOALLOC_SCRATCH_BYTES
+    small = isa.plan(isa.Params(1, 40, 8192, 8192, 128, 64))          # 16384 tokens fit
+    assert small["noalloc_bytes"] <= isa.NOALLOC_SCRATCH_BYTES
+    assert small["noalloc_bytes"] < small["workspace_bytes"]
+    big = _params(isa, B=1, H=40, L_src=32768, L_ctx=32768)          # 65536 tokens do not
+    pl = isa.IsaPlan()
+    assert L.isa_plan(ctypes.byref(big), ctypes.byref(pl)) == 0
+    assert pl.noalloc_bytes > isa.NOALLOC_SCRATCH_BYTES
+    assert L.isa_forward_noalloc(ctypes.byref(big), fake, fake, fake, fake, None, None) == isa.ISA_ERR_SCRATCH
+    assert "scratch" in isa.strerror(isa.ISA_ERR_SCRATCH)
+
+
+def test_init_without_device(isa):
+    """isa_init sets up the current device; on a host without a usable HIP
+    device it reports ISA_ERR_HIP instead of failing in another way."""
+    torch = pytest.importorskip("torch")
+    rc = isa.lib().isa_init()
+    if torch.cuda.device_count() == 0:
+        assert rc == isa.ISA_ERR_HIP
+    else:
+        assert rc == isa.ISA_OK
 
 
 def test_strerror(isa):
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -5, 7):
         s = isa.strerror(code)
         assert isinstance(s, str) and s
     assert "workspace" in isa.strerror(-3)
