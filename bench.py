@@ -85,12 +85,23 @@ def make_inputs(dev):
     return out, host
 
 
+def block_counts(p, pl):
+    """Valid tokens n_j of every global block, by the library's block-cut rule
+    (each segment cut on its own; a tail block holds the remainder)."""
+    src = [min(p.b, p.L_src - j * p.b) for j in range(pl["N_src"])]
+    ctx = [min(p.b, p.L_ctx - j * p.b) for j in range(pl["N_ctx"])]
+    return np.asarray(src + ctx, dtype=np.float64)
+
+
+def block_starts(p, pl):
+    return np.asarray([j * p.b for j in range(pl["N_src"])] +
+                      [p.L_src + j * p.b for j in range(pl["N_ctx"])], dtype=np.int64)
+
+
 def algorithmic_flops(p, pl, ctx_idx, sharp_idx, flat_idx, exact_idx):
     """FLOPs of the method from the actual selections (4*D per query-key pair
     for the exact terms and the pooled terms, 2*D per coarse score)."""
-    from oracle.isa_oracle import make_plan   # block token counts only
-    plan = make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
-    n = np.asarray(plan.counts, dtype=np.float64)
+    n = block_counts(p, pl)
     D = p.D
     f_sharp = f_flat = f_taylor = 0.0
     for bi in range(p.B):
@@ -119,6 +130,19 @@ def traffic_record():
     if rec.get("source_sha256") != sha:
         return None
     return rec.get("bytes_per_launch")
+
+
+def host_cpu():
+    """Cores this process may run on and the CPU model name."""
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return len(os.sched_getaffinity(0)), model
 
 
 def cpu_baseline(host, budget_s):
@@ -168,7 +192,9 @@ def cpu_baseline(host, budget_s):
     per_flat = max(np.mean(done["flat"]) - t_fixed, 0.0)
     per_head = t_sel + per_sharp * plan.n_sharp + per_flat * plan.n_flat
     total_ms = per_head * w["B"] * w["H"] * 1e3
-    return {"value": total_ms, "unit": "ms", "cores": int(threads), "kind": "oracle",
+    host_cores, model = host_cpu()
+    return {"value": total_ms, "unit": "ms", "cores": int(threads), "host_cores": host_cores,
+            "cpu_model": model, "kind": "oracle",
             "sample": (f"head (0,0) of {w['B'] * w['H']}: selections in full ({t_sel:.2f} s), outputs of "
                        f"{len(done['sharp'])} sharp and {len(done['flat'])} flat query blocks "
                        f"(of {plan.n_sharp}/{plan.n_flat}); per-block times extrapolated to all "
@@ -182,7 +208,6 @@ def fig6(isa, torch, p, Q, K, V, args):
     alpha_f = 1, alpha_ns = 0 (every block on the pooled keys only)."""
     import dataclasses
     from scipy.stats import spearmanr
-    from oracle.isa_oracle import make_plan   # block boundaries only
     pe = dataclasses.replace(p, alpha_f=0.0)
     pt = dataclasses.replace(p, alpha_f=1.0, alpha_ns=0.0)
     times = {}
@@ -197,15 +222,14 @@ def fig6(isa, torch, p, Q, K, V, args):
         torch.cuda.synchronize()
         times[name] = e0.elapsed_time(e1) / max(args.steps // 4, 2)
         outs[name] = (O.float(), dbg["sharpness"])
-    plan = make_plan(p.L_src, p.L_ctx, p.b, p.alpha_s, p.alpha_f, p.alpha_ns)
-    starts = torch.tensor(plan.starts, device=Q.device)
-    counts = torch.tensor(plan.counts, device=Q.device)
-    tok_block = torch.repeat_interleave(torch.arange(plan.N, device=Q.device), counts)
+    pl = isa.plan(p)
+    counts = torch.tensor(block_counts(p, pl).astype(np.int64), device=Q.device)
+    tok_block = torch.repeat_interleave(torch.arange(pl["N"], device=Q.device), counts)
     diff = (outs["all_taylor"][0] - outs["exact_over_J"][0]).abs().mean(dim=-1)   # [B,H,L]
     rhos = []
     for bi in range(p.B):
         for h in range(p.H):
-            err = torch.zeros(plan.N, device=Q.device, dtype=torch.float32)
+            err = torch.zeros(pl["N"], device=Q.device, dtype=torch.float32)
             err.index_add_(0, tok_block, diff[bi, h])
             err = (err / counts).cpu().numpy()
             rhos.append(spearmanr(outs["all_taylor"][1][bi, h].cpu().numpy(), err).correlation)
@@ -217,7 +241,6 @@ def fig6(isa, torch, p, Q, K, V, args):
         "speedup_vs_exact_over_J": {"default": times["exact_over_J"] / times["default"],
                                     "all_taylor": times["exact_over_J"] / times["all_taylor"]},
         "config": {"workload": "isa_fwd_64k_tokens_h40_d128", "alpha_s": p.alpha_s}}}), flush=True)
-    del starts
 
 
 def backward_bench(isa, torch, p, Q, K, V, args):
@@ -261,6 +284,62 @@ def backward_bench(isa, torch, p, Q, K, V, args):
             "forward_plus_backward": res["dense_same_engine"]["step_ms"] / res["isa"]["step_ms"]}
     print(json.dumps({"backward": res, "config": {"workload": "isa_fwd_64k_tokens_h40_d128"}}),
           flush=True)
+
+
+# Algorithmic HBM bytes per launch of the selection kernels and pooling
+# (B*H heads): what each kernel must read and write once, nothing re-read.
+def selection_bytes(p, pl):
+    BH, D, N = p.B * p.H, p.D, pl["N"]
+    L = p.L_src + p.L_ctx
+    return {
+        "pool_kernel": 3 * BH * L * D * 2 + BH * N * D * (8 + 8 + 2 + 2),
+        "ctx_topk_kernel": BH * ((pl["N_src"] + pl["N_ctx"]) * D * 8 + pl["k_ctx"] * 4 + pl["N_ctx"] * 8),
+        "sharpness_kernel": BH * ((N + pl["N_src"]) * D * 8 + N * 8),
+        "split_kernel": BH * N * (8 + 4),
+        "flat_topk_kernel": BH * ((pl["n_flat"] + pl["N_kv"]) * D * 8 + pl["k_ctx"] * 4 + pl["n_flat"] * 4
+                                  + pl["n_flat"] * pl["k_ns"] * 4),
+    }
+
+
+def kernel_times(torch, fn, reps):
+    """Mean device duration (ms) of every kernel `fn` launches, from torch's
+    profiler, which traces all HIP kernels of the process (the library's
+    included). None when the profiler has no device activity here."""
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        fn()
+        torch.cuda.synchronize()
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for _ in range(reps):
+                fn()
+            torch.cuda.synchronize()
+        tot, cnt = {}, {}
+        for ev in prof.events():
+            if str(ev.device_type).endswith("CUDA") and ev.device_time_total > 0:
+                tot[ev.name] = tot.get(ev.name, 0.0) + ev.device_time_total
+                cnt[ev.name] = cnt.get(ev.name, 0) + 1
+        return {k: tot[k] / cnt[k] / 1e3 for k in tot} or None
+    except Exception as exc:   # the profiler is context, never a reason to fail the benchmark
+        log(f"kernel profiler unavailable: {exc}")
+        return None
+
+
+def selection_rates(torch, p, pl, fn, reps):
+    """Achieved HBM GB/s of pooling and each selection kernel: algorithmic
+    bytes per launch over its mean device duration (profiler), and the
+    fraction of the 8 TB/s HBM peak."""
+    times = kernel_times(torch, fn, reps)
+    if not times:
+        return None
+    out = {}
+    for kern, nbytes in selection_bytes(p, pl).items():
+        hits = [v for k, v in times.items() if kern in k]
+        if not hits:
+            continue
+        ms = float(np.mean(hits))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[kern] = {"ms": ms, "bytes": nbytes, "gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
+    return out
 
 
 def torch_sdpa_ms(torch, Q, K, V, reps):
@@ -601,11 +680,12 @@ def main():
     pg = isa.Params(p.B, p.H, p.L_src, p.L_ctx, p.D, p.b, p.alpha_s, p.alpha_f, p.alpha_ns, gamma=0.5)
     pgc = pg.c()
     ws_g = e(isa.plan(pg)["workspace_bytes"], dt=torch.uint8)
+    ws_res = e(isa.plan(pg)["scores_bytes"], dt=torch.uint8)   # the residual's coarse rows
 
     def residual():
         chk("residual", lib.isa_coarse_residual(ctypes.byref(pgc), qc.data_ptr(), kc.data_ptr(), vcb.data_ptr(),
                                                 ctx.data_ptr() if ctx.numel() else None, O.data_ptr(),
-                                                ws_s.data_ptr(), ws_s.numel(), sp))
+                                                ws_res.data_ptr(), ws_res.numel(), sp))
 
     def forward_residual():
         chk("fwd_residual", lib.isa_forward(ctypes.byref(pgc), Q.data_ptr(), K.data_ptr(), V.data_ptr(),
@@ -619,7 +699,17 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         timings[name] = e0.elapsed_time(e1) / args.steps
-    del ws_g
+    del ws_g, ws_res
+
+    # pooling and the selection kernels one by one (per-kernel durations)
+    def selection_step():
+        chk("pool", lib.isa_pool_coarse(pr, Q.data_ptr(), K.data_ptr(), V.data_ptr(), qc.data_ptr(),
+                                        kc.data_ptr(), kcb.data_ptr(), vcb.data_ptr(), sp))
+        chk("ctx", lib.isa_ctx_topk(pr, qc.data_ptr(), kc.data_ptr(), ctx.data_ptr(), score.data_ptr(), sp))
+        chk("split", lib.isa_sharpness_split(pr, qc.data_ptr(), kc.data_ptr(), ctx.data_ptr(),
+                                             sharp.data_ptr(), si.data_ptr(), fi.data_ptr(),
+                                             ei.data_ptr(), ws_s.data_ptr(), ws_s.numel(), sp))
+    sel_rates = selection_rates(torch, p, pl, selection_step, 5)
 
     flops = algorithmic_flops(p, pl, ctx.view(p.B, p.H, -1).cpu().numpy(),
                               si.view(p.B, p.H, -1).cpu().numpy(), fi.view(p.B, p.H, -1).cpu().numpy(),
@@ -672,6 +762,7 @@ def main():
         "pool_hbm_frac": pool_bytes / (per["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "pool_hbm_frac_of_measured_read": pool_bytes / (per["pool"] * 1e-3) / 1e9 / peaks["hbm_read_gbs"],
         "measured_peaks": peaks,
+        "selection_hbm": sel_rates,
         "isa_backward_ms": bwd_ms,
         "rope_pool_ms": rope_ms,
         "coarse_residual_ms": timings["residual"],

@@ -61,7 +61,8 @@ Layout make_layout(const IsaShape& s, bool with_backward = true) {
   l.sharp_idx = o; o = align256(o + at_least1(bh * s.n_sharp) * 4);
   l.flat_idx = o;  o = align256(o + at_least1(bh * s.n_flat) * 4);
   l.exact = o;     o = align256(o + at_least1(bh * s.n_flat * (size_t)s.k_ns) * 4);
-  l.srows = o;     o = align256(o + bh * s.N * (size_t)s.N_kv * 8);
+  // coarse rows S[i, J]: only the gamma residual stores them
+  l.srows = o;     o = align256(o + (s.gamma != 0.0f ? bh * s.N * (size_t)s.N_kv * 8 : 0));
   const size_t qkr = s.rope_base != 0.0 ? bh * (size_t)s.L * s.D * 2 : 0;
   l.qr = o;        o = align256(o + qkr);
   l.kr = o;        o = align256(o + qkr);
@@ -91,13 +92,17 @@ Layout make_layout(const IsaShape& s, bool with_backward = true) {
   return l;
 }
 
-// Workspace of isa_sharpness_split: the coarse rows S[i, J] of every query
-// block, then room for the sharpness values when the caller passes none.
-size_t scores_rows_bytes(const IsaShape& s) {
-  return align256((size_t)s.B * s.H * s.N * (size_t)s.N_kv * 8);
+// Workspace of isa_sharpness_split: room for the sharpness values when the
+// caller passes none (the coarse scores are never stored). Workspace of
+// isa_coarse_residual: the coarse rows S[i, J] of every query block (gamma
+// != 0 only). The plan reports the larger of the two.
+size_t sharp_ws_bytes(const IsaShape& s) { return align256((size_t)s.B * s.H * s.N * 8); }
+size_t residual_ws_bytes(const IsaShape& s) {
+  return s.gamma != 0.0f ? align256((size_t)s.B * s.H * s.N * (size_t)s.N_kv * 8) : 0;
 }
 size_t scores_bytes(const IsaShape& s) {
-  return scores_rows_bytes(s) + align256((size_t)s.B * s.H * s.N * 8);
+  const size_t a = sharp_ws_bytes(s), b = residual_ws_bytes(s);
+  return a > b ? a : b;
 }
 
 // Validates the parameters and derives every count. Makes no HIP call.
@@ -242,14 +247,12 @@ int isa_sharpness_split(const isa_params_t* p, const double* qc, const double* k
       (!flat_idx && s.n_flat > 0) || (!flat_exact_idx && s.n_flat > 0 && s.k_ns > 0) || !ws ||
       !aligned16({qc, kc, ws}))
     return ISA_ERR_ARG;
-  if (ws_bytes < scores_bytes(s)) return ISA_ERR_WORKSPACE;
+  if (ws_bytes < sharp_ws_bytes(s)) return ISA_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
-  double* srows = (double*)ws;
-  double* sharp = sharpness ? sharpness : (double*)((char*)ws + scores_rows_bytes(s));
-  hipError_t e = isa_launch_coarse_rows(s, qc, kc, ctx_idx, srows, st);
-  if (e == hipSuccess) e = isa_launch_sharpness(s, srows, sharp, st);
+  double* sharp = sharpness ? sharpness : (double*)ws;
+  hipError_t e = isa_launch_sharpness(s, qc, kc, sharp, st);
   if (e == hipSuccess) e = isa_launch_split(s, sharp, sharp_idx, flat_idx, st);
-  if (e == hipSuccess) e = isa_launch_flat_topk(s, srows, ctx_idx, flat_idx, flat_exact_idx, st);
+  if (e == hipSuccess) e = isa_launch_flat_topk(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
   return hip_status(e);
 }
 
@@ -293,8 +296,8 @@ int isa_coarse_residual(const isa_params_t* p, const double* qc, const double* k
   if (!qc || !kc || !vc_bf16 || (!ctx_idx && s.k_ctx > 0) || !O || !ws ||
       !aligned16({qc, kc, vc_bf16, O, ws}))
     return ISA_ERR_ARG;
-  if (ws_bytes < scores_rows_bytes(s)) return ISA_ERR_WORKSPACE;
   if (s.gamma == 0.0f) return ISA_OK;
+  if (ws_bytes < residual_ws_bytes(s)) return ISA_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
   double* srows = (double*)ws;
   hipError_t e = isa_launch_coarse_rows(s, qc, kc, ctx_idx, srows, st);
@@ -339,16 +342,18 @@ int forward_impl(const IsaShape& s, const void* Q, const void* K, const void* V,
     e = isa_launch_pool(s, q, k, v, qc, kc, kcb, vcb, st);
   }
   if (e == hipSuccess) e = isa_launch_ctx_topk(s, qc, kc, ctx_idx, ctx_score, st);
-  if (e == hipSuccess) e = isa_launch_coarse_rows(s, qc, kc, ctx_idx, srows, st);
-  if (e == hipSuccess) e = isa_launch_sharpness(s, srows, sharp, st);
+  if (e == hipSuccess) e = isa_launch_sharpness(s, qc, kc, sharp, st);
   if (e == hipSuccess) e = isa_launch_split(s, sharp, sharp_idx, flat_idx, st);
-  if (e == hipSuccess) e = isa_launch_flat_topk(s, srows, ctx_idx, flat_idx, exact, st);
+  if (e == hipSuccess) e = isa_launch_flat_topk(s, qc, kc, ctx_idx, flat_idx, exact, st);
   float* lse = l.lse ? (float*)(w + l.lse) : nullptr;
   if (e == hipSuccess) e = isa_launch_sharp_attn(s, q, k, v, ctx_idx, sharp_idx, (uint16_t*)O, lse, st);
   if (e == hipSuccess)
     e = isa_launch_flat_attn(s, q, k, v, kcb, vcb, ctx_idx, flat_idx, exact, (uint16_t*)O, lse, st);
-  if (e == hipSuccess && s.gamma != 0.0f)
-    e = isa_launch_coarse_residual(s, srows, vcb, ctx_idx, (uint16_t*)O, st);
+  if (e == hipSuccess && s.gamma != 0.0f) {
+    // the residual's pooled attention reads whole coarse rows (kept for the backward)
+    e = isa_launch_coarse_rows(s, qc, kc, ctx_idx, srows, st);
+    if (e == hipSuccess) e = isa_launch_coarse_residual(s, srows, vcb, ctx_idx, (uint16_t*)O, st);
+  }
   if (e == hipSuccess && dbg) {
     const size_t bh = (size_t)s.B * s.H;
     struct { void* dst; const void* src; size_t n; } cp[] = {
@@ -401,6 +406,7 @@ int isa_forward_noalloc(const isa_params_t* p, const void* Q, const void* K, con
 int isa_init(void) {
   hipError_t e = isa_attn_prepare_device();
   if (e == hipSuccess) e = isa_bwd_prepare_device();
+  if (e == hipSuccess) e = isa_select_prepare_device();
   if (e != hipSuccess) return ISA_ERR_HIP;
   void* ws = nullptr;
   return scratch_address(&ws);

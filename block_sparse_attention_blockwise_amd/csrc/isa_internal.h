@@ -63,6 +63,7 @@ constexpr int ISA_MAX_NKV = 4096;
 // attention and dQ kernels); idempotent.
 hipError_t isa_attn_prepare_device();
 hipError_t isa_bwd_prepare_device();
+hipError_t isa_select_prepare_device();
 
 // Launchers: each returns the first HIP error met while enqueueing.
 hipError_t isa_launch_pool(const IsaShape& s, const uint16_t* Q, const uint16_t* K,
@@ -77,13 +78,13 @@ hipError_t isa_launch_ctx_topk(const IsaShape& s, const double* qc, const double
                                int32_t* ctx_idx, double* ctx_score, hipStream_t st);
 hipError_t isa_launch_coarse_rows(const IsaShape& s, const double* qc, const double* kc,
                                   const int32_t* ctx_idx, double* srows, hipStream_t st);
-hipError_t isa_launch_sharpness(const IsaShape& s, const double* srows, double* sharp,
+hipError_t isa_launch_sharpness(const IsaShape& s, const double* qc, const double* kc, double* sharp,
                                 hipStream_t st);
 hipError_t isa_launch_split(const IsaShape& s, const double* sharp, int32_t* sharp_idx,
                             int32_t* flat_idx, hipStream_t st);
-hipError_t isa_launch_flat_topk(const IsaShape& s, const double* srows, const int32_t* ctx_idx,
-                                const int32_t* flat_idx, int32_t* flat_exact_idx,
-                                hipStream_t st);
+hipError_t isa_launch_flat_topk(const IsaShape& s, const double* qc, const double* kc,
+                                const int32_t* ctx_idx, const int32_t* flat_idx,
+                                int32_t* flat_exact_idx, hipStream_t st);
 hipError_t isa_launch_coarse_residual(const IsaShape& s, const double* srows,
                                       const uint16_t* vc_bf16, const int32_t* ctx_idx,
                                       uint16_t* O, hipStream_t st);

@@ -4,16 +4,23 @@
 // section "Method steps":
 //   step (2): context importance = coarse scores of the source query blocks
 //             summed per context key block; keep the top alpha_s fraction;
-//   step (1)+(3): coarse rows S[i, J] = Qc_i . Kc_j / sqrt(D) over the kept
-//             blocks J; sharpness M_i = variance of the softmax of S[i, :]
-//             restricted to the source key blocks; the least sharp alpha_f
-//             fraction of query blocks is "flat";
+//   step (1)+(3): coarse scores S[i, j] = Qc_i . Kc_j / sqrt(D); sharpness
+//             M_i = variance of the softmax of S[i, :] restricted to the
+//             source key blocks; the least sharp alpha_f fraction of query
+//             blocks is "flat";
 //   step (5): per flat block, the exact set E_i = top alpha_ns fraction of J
 //             by coarse score.
+// The coarse scores are formed where they are used, on the fp64 matrix cores
+// (v_mfma_f64_16x16x4f64), and never stored: the sharpness kernel folds each
+// 16 x 16 tile into per-row online softmax statistics, the exact-set kernel
+// keeps only its own flat blocks' rows (in LDS) for their top-k. Only the
+// gamma residual (step (6)) materialises the rows S[i, J] it needs.
 // Every top-k prefers the lower index among equal scores, and every output
 // list is ascending. Selection uses an exact radix bisection on the ordered
 // bit pattern of the fp64 scores (no floating-point comparison tolerance),
 // then resolves ties at the threshold by index order with a block-wide scan.
+#include <initializer_list>
+
 #include "isa_internal.h"
 
 namespace {
@@ -134,6 +141,34 @@ __device__ inline int kept_block_id(const IsaShape& s, const int32_t* ctx_row, i
   return p < s.N_src ? p : ctx_row[p - s.N_src];
 }
 
+// ------------------------------------------- coarse scores on matrix cores
+// v_mfma_f64_16x16x4f64: lane l supplies A[m][k] and B[k][n] with m = n =
+// l % 16, k = l / 16, and receives C[l / 16 + 4 i][l % 16], i = 0..3. Step
+// kk of a D-long dot product pairs dimension (D/4) k + kk of the A row and
+// of the B column, so each lane holds one contiguous quarter of a row.
+typedef double double4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+__device__ inline void load_frag(const double* __restrict__ row, bool valid, int k,
+                                 double (&f)[D / 4]) {
+#pragma unroll
+  for (int x = 0; x < D / 8; ++x) {
+    const double2 v = valid ? *reinterpret_cast<const double2*>(row + (D / 4) * k + 2 * x)
+                            : make_double2(0.0, 0.0);
+    f[2 * x] = v.x;
+    f[2 * x + 1] = v.y;
+  }
+}
+
+// Raw dot products of the 16 A rows with the 16 B rows held by the wave.
+template <int D>
+__device__ inline double4_t coarse_mma(const double (&a)[D / 4], const double (&b)[D / 4]) {
+  double4_t c = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int kk = 0; kk < D / 4; ++kk) c = __builtin_amdgcn_mfma_f64_16x16x4f64(a[kk], b[kk], c, 0, 0, 0);
+  return c;
+}
+
 // ---------------------------------------------------------------- step (2)
 constexpr int kCtxThreads = 1024;
 constexpr int kCtxIPT = ISA_MAX_SEG_BLOCKS / kCtxThreads;
@@ -214,9 +249,11 @@ __global__ __launch_bounds__(kCtxThreads) void ctx_topk_kernel(IsaShape s, const
                                       [n_src](int j) { return n_src + j; }, scratch);
 }
 
-// ------------------------------------------------- step (1) coarse rows
-// S[i, p] = Qc_i . Kc_{J[p]} / sqrt(D) in fp64 for a 64 x 64 tile per
-// workgroup; each thread accumulates a 4 x 4 block from LDS-staged slices.
+// ------------------------------------ coarse rows of the gamma residual
+// S[i, p] = Qc_i . Kc_{J[p]} / sqrt(D) in fp64 for every query block and
+// kept block (the residual's pooled attention and its backward read whole
+// rows); a 64 x 64 tile per workgroup, each thread accumulating a 4 x 4
+// block from LDS-staged slices.
 constexpr int kCoarseRows = 64, kCoarseCols = 64, kCoarseDc = 16;
 
 __global__ __launch_bounds__(256) void coarse_rows_kernel(IsaShape s, const double* __restrict__ qc,
@@ -293,27 +330,81 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(IsaShape s, const doub
 }
 
 // ------------------------------------------------------ step (3) sharpness
-__global__ __launch_bounds__(256) void sharpness_kernel(IsaShape s, const double* __restrict__ srows,
-                                                        double* __restrict__ sharp) {
-  const int wave = threadIdx.x / 64, lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + wave, bh = blockIdx.y;
-  if (i >= s.N) return;   // whole wave; no workgroup barrier below
-  const double* row = srows + ((size_t)bh * s.N + i) * s.N_kv;   // source columns first
-  const int n = s.N_src;
-  double mx = -INFINITY;
-  for (int j = lane; j < n; j += 64) mx = fmax(mx, row[j]);
-  mx = wave_max_f64(mx);
-  double z = 0.0;
-  for (int j = lane; j < n; j += 64) z += exp(row[j] - mx);
-  z = wave_sum_f64(z);
-  const double inv_n = 1.0 / (double)n;
-  double acc = 0.0;
-  for (int j = lane; j < n; j += 64) {
-    const double pr = exp(row[j] - mx) / z - inv_n;
-    acc += pr * pr;
+// M_i = (1/n) sum_j (p_ij - 1/n)^2 with p_i = softmax(S[i, 0..n)), n = N_src,
+// equal to (sum_j p_ij^2 - 1/n) / n. Each wave takes 16 query blocks and
+// walks the source key blocks 16 at a time; every lane keeps, for each of its
+// four rows, the online statistics of its columns: the running maximum m,
+// z = sum exp(S - m) and w = sum exp(2 (S - m)), so sum p^2 = w / z^2. The
+// 16 lanes of a row then merge their statistics in a fixed butterfly order
+// (each merge is symmetric, so every lane ends with the same bits).
+constexpr int kSharpWaves = 4;
+
+__device__ inline void stats_add(double v, double& m, double& z, double& w) {
+  const double d = v - m;                 // +inf while m = -inf
+  const double e = exp(-fabs(d));         // exp(m - v) when v is the new maximum
+  const bool up = d > 0.0;
+  z = up ? z * e + 1.0 : z + e;
+  w = up ? w * (e * e) + 1.0 : w + e * e;
+  m = up ? v : m;
+}
+
+__device__ inline void stats_merge(double& m, double& z, double& w, double m2, double z2, double w2) {
+  const double mm = fmax(m, m2);
+  if (mm == -INFINITY) return;            // neither side has seen a column
+  const double e1 = exp(m - mm), e2 = exp(m2 - mm);
+  z = z * e1 + z2 * e2;
+  w = w * (e1 * e1) + w2 * (e2 * e2);
+  m = mm;
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kSharpWaves) void sharpness_kernel(IsaShape s, const double* __restrict__ qc,
+                                                                     const double* __restrict__ kc,
+                                                                     double* __restrict__ sharp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int bh = blockIdx.y;
+  const int r0 = (blockIdx.x * kSharpWaves + wave) * 16;
+  if (r0 >= s.N) return;   // whole wave; no workgroup barrier in this kernel
+  const int m16 = lane & 15, k = lane >> 4;
+  const double* qh = qc + (size_t)bh * s.N * D;
+  const double* kh = kc + (size_t)bh * s.N * D;   // source key blocks are rows 0..N_src-1
+  double a[D / 4];
+  load_frag<D>(qh + (size_t)(r0 + m16 < s.N ? r0 + m16 : 0) * D, r0 + m16 < s.N, k, a);
+  const double sq = sqrt((double)D);
+  double mx[4], z[4], w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mx[i] = -INFINITY;
+    z[i] = 0.0;
+    w[i] = 0.0;
   }
-  acc = wave_sum_f64(acc);
-  if (lane == 0) sharp[(size_t)bh * s.N + i] = acc / (double)n;
+  for (int c0 = 0; c0 < s.N_src; c0 += 16) {
+    const int c = c0 + m16;   // this lane's column
+    double b[D / 4];
+    load_frag<D>(kh + (size_t)(c < s.N_src ? c : 0) * D, c < s.N_src, k, b);
+    const double4_t acc = coarse_mma<D>(a, b);
+    if (c < s.N_src) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stats_add(acc[i] / sq, mx[i], z[i], w[i]);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double m2 = __shfl_xor(mx[i], off, 64), z2 = __shfl_xor(z[i], off, 64),
+                   w2 = __shfl_xor(w[i], off, 64);
+      stats_merge(mx[i], z[i], w[i], m2, z2, w2);
+    }
+  }
+  if (m16 == 0) {
+    const double n = (double)s.N_src;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + k + 4 * i;
+      if (row < s.N) sharp[(size_t)bh * s.N + row] = (w[i] / (z[i] * z[i]) - 1.0 / n) / n;
+    }
+  }
 }
 
 // ----------------------------------------------------------- step (3) split
@@ -379,35 +470,79 @@ __device__ inline void wave_topk(const unsigned long long (&key)[IPL], int n, in
   }
 }
 
+// One workgroup takes R consecutive flat blocks (R = 16, 8, 4 or 2, as the
+// rows of S fit the LDS budget). Phase 1: the matrix cores form S[i, J] for
+// those R rows (one 16-row tile, rows past R zero), 16 positions of J per
+// tile, tiles spread over the waves, into LDS. Phase 2: one wave per row
+// reads its row back (lane l: positions l + 64 u) and selects the top k_ns.
 constexpr int kFlatTopkWaves = 4;
+constexpr int kFlatTopkLds = 80 * 1024;   // bytes of S rows per workgroup
 
-template <int IPL>
-__global__ __launch_bounds__(64 * kFlatTopkWaves) void flat_topk_kernel(IsaShape s, const double* __restrict__ srows,
+__host__ __device__ inline int flat_topk_rows(int N_kv) {
+  int r = 16;
+  while (r > 2 && (size_t)r * N_kv * sizeof(double) > (size_t)kFlatTopkLds) r >>= 1;
+  return r;
+}
+
+template <int D, int IPL>
+__global__ __launch_bounds__(64 * kFlatTopkWaves) void flat_topk_kernel(IsaShape s, const double* __restrict__ qc,
+                                                                        const double* __restrict__ kc,
                                                                         const int32_t* __restrict__ ctx_idx,
                                                                         const int32_t* __restrict__ flat_idx,
-                                                                        int32_t* __restrict__ exact) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * kFlatTopkWaves + (threadIdx.x >> 6), bh = blockIdx.y;
-  if (r >= s.n_flat) return;   // whole wave; no workgroup barrier below
-  const int i = flat_idx[(size_t)bh * s.n_flat + r];
-  const double* row = srows + ((size_t)bh * s.N + i) * s.N_kv;
-  unsigned long long key[IPL];
-  bool sel[IPL];
-#pragma unroll
-  for (int u = 0; u < IPL; ++u) {
-    const int p = lane + 64 * u;
-    key[u] = p < s.N_kv ? order_key(row[p]) : 0ull;
-  }
-  wave_topk<IPL>(key, s.N_kv, s.k_ns, sel);
+                                                                        int32_t* __restrict__ exact, int R) {
+  extern __shared__ double srow[];   // [R][N_kv]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int bh = blockIdx.y;
+  const int f0 = blockIdx.x * R;
+  const int nr = min(R, s.n_flat - f0);
+  const int m16 = lane & 15, k = lane >> 4;
+  const int32_t* frow = flat_idx + (size_t)bh * s.n_flat;
   const int32_t* ctx_row = ctx_idx + (size_t)bh * s.k_ctx;
-  int32_t* out = exact + ((size_t)bh * s.n_flat + r) * s.k_ns;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  int base = 0;
+  const double* qh = qc + (size_t)bh * s.N * D;
+  const double* kh = kc + (size_t)bh * s.N * D;
+  int qi = -1;
+  if (m16 < nr) {
+    const int i = frow[f0 + m16];
+    qi = (i >= 0 && i < s.N) ? i : -1;
+  }
+  double a[D / 4];
+  load_frag<D>(qh + (size_t)(qi >= 0 ? qi : 0) * D, qi >= 0, k, a);
+  const double sq = sqrt((double)D);
+  const int ntile = (s.N_kv + 15) / 16;
+  for (int t = wave; t < ntile; t += kFlatTopkWaves) {
+    const int p = t * 16 + m16;   // this lane's position in J
+    const int j = p < s.N_kv ? kept_block_id(s, ctx_row, p) : -1;
+    const bool ok = j >= 0 && j < s.N;
+    double b[D / 4];
+    load_frag<D>(kh + (size_t)(ok ? j : 0) * D, ok, k, b);
+    const double4_t acc = coarse_mma<D>(a, b);
+    if (p < s.N_kv) {
 #pragma unroll
-  for (int u = 0; u < IPL; ++u) {
-    const unsigned long long m = __ballot(sel[u]);
-    if (sel[u]) out[base + __popcll(m & below)] = kept_block_id(s, ctx_row, lane + 64 * u);
-    base += __popcll(m);
+      for (int i = 0; i < 4; ++i) {
+        const int r = k + 4 * i;
+        if (r < nr) srow[(size_t)r * s.N_kv + p] = acc[i] / sq;
+      }
+    }
+  }
+  __syncthreads();
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int r = wave; r < nr; r += kFlatTopkWaves) {
+    unsigned long long key[IPL];
+    bool sel[IPL];
+#pragma unroll
+    for (int u = 0; u < IPL; ++u) {
+      const int p = lane + 64 * u;
+      key[u] = p < s.N_kv ? order_key(srow[(size_t)r * s.N_kv + p]) : 0ull;
+    }
+    wave_topk<IPL>(key, s.N_kv, s.k_ns, sel);
+    int32_t* out = exact + ((size_t)bh * s.n_flat + f0 + r) * s.k_ns;
+    int base = 0;
+#pragma unroll
+    for (int u = 0; u < IPL; ++u) {
+      const unsigned long long msk = __ballot(sel[u]);
+      if (sel[u]) out[base + __popcll(msk & below)] = kept_block_id(s, ctx_row, lane + 64 * u);
+      base += __popcll(msk);
+    }
   }
 }
 
@@ -553,10 +688,13 @@ hipError_t isa_launch_coarse_rows(const IsaShape& s, const double* qc, const dou
   return hipGetLastError();
 }
 
-hipError_t isa_launch_sharpness(const IsaShape& s, const double* srows, double* sharp,
+hipError_t isa_launch_sharpness(const IsaShape& s, const double* qc, const double* kc, double* sharp,
                                 hipStream_t st) {
-  dim3 grid((s.N + 3) / 4, s.B * s.H);
-  sharpness_kernel<<<grid, 256, 0, st>>>(s, srows, sharp);
+  dim3 grid((s.N + 16 * kSharpWaves - 1) / (16 * kSharpWaves), s.B * s.H);
+  if (s.D == 128)
+    sharpness_kernel<128><<<grid, 64 * kSharpWaves, 0, st>>>(s, qc, kc, sharp);
+  else
+    sharpness_kernel<64><<<grid, 64 * kSharpWaves, 0, st>>>(s, qc, kc, sharp);
   return hipGetLastError();
 }
 
@@ -566,22 +704,54 @@ hipError_t isa_launch_split(const IsaShape& s, const double* sharp, int32_t* sha
   return hipGetLastError();
 }
 
-hipError_t isa_launch_flat_topk(const IsaShape& s, const double* srows, const int32_t* ctx_idx,
-                                const int32_t* flat_idx, int32_t* flat_exact_idx,
-                                hipStream_t st) {
-  if (s.n_flat == 0 || s.k_ns == 0) return hipSuccess;
-  dim3 grid((s.n_flat + kFlatTopkWaves - 1) / kFlatTopkWaves, s.B * s.H);
-  const int ipl = (s.N_kv + 63) / 64;
-  const int nt = 64 * kFlatTopkWaves;
-  if (ipl <= 4)
-    flat_topk_kernel<4><<<grid, nt, 0, st>>>(s, srows, ctx_idx, flat_idx, flat_exact_idx);
-  else if (ipl <= 8)
-    flat_topk_kernel<8><<<grid, nt, 0, st>>>(s, srows, ctx_idx, flat_idx, flat_exact_idx);
-  else if (ipl <= 16)
-    flat_topk_kernel<16><<<grid, nt, 0, st>>>(s, srows, ctx_idx, flat_idx, flat_exact_idx);
-  else if (ipl <= 32)
-    flat_topk_kernel<32><<<grid, nt, 0, st>>>(s, srows, ctx_idx, flat_idx, flat_exact_idx);
-  else
-    flat_topk_kernel<64><<<grid, nt, 0, st>>>(s, srows, ctx_idx, flat_idx, flat_exact_idx);
+namespace {
+
+// The exact-set kernels keep S rows in dynamic LDS beyond the default
+// limit: raised once per instantiation and device (host-side only).
+template <int D, int IPL>
+hipError_t prepare_topk() {
+  static unsigned long long done = 0;
+  return isa_ensure_dyn_lds(reinterpret_cast<const void*>(&flat_topk_kernel<D, IPL>), kFlatTopkLds, &done);
+}
+
+template <int D, int IPL>
+hipError_t launch_flat_topk(const IsaShape& s, const double* qc, const double* kc, const int32_t* ctx_idx,
+                            const int32_t* flat_idx, int32_t* flat_exact_idx, hipStream_t st) {
+  const hipError_t e = prepare_topk<D, IPL>();
+  if (e != hipSuccess) return e;
+  const int R = flat_topk_rows(s.N_kv);
+  dim3 grid((s.n_flat + R - 1) / R, s.B * s.H);
+  const size_t lds = (size_t)R * s.N_kv * sizeof(double);
+  flat_topk_kernel<D, IPL><<<grid, 64 * kFlatTopkWaves, lds, st>>>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, R);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t flat_topk_for_d(const IsaShape& s, const double* qc, const double* kc, const int32_t* ctx_idx,
+                           const int32_t* flat_idx, int32_t* flat_exact_idx, hipStream_t st) {
+  const int ipl = (s.N_kv + 63) / 64;
+  if (ipl <= 4) return launch_flat_topk<D, 4>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
+  if (ipl <= 8) return launch_flat_topk<D, 8>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
+  if (ipl <= 16) return launch_flat_topk<D, 16>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
+  if (ipl <= 32) return launch_flat_topk<D, 32>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
+  return launch_flat_topk<D, 64>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
+}
+
+}  // namespace
+
+hipError_t isa_launch_flat_topk(const IsaShape& s, const double* qc, const double* kc, const int32_t* ctx_idx,
+                                const int32_t* flat_idx, int32_t* flat_exact_idx, hipStream_t st) {
+  if (s.n_flat == 0 || s.k_ns == 0) return hipSuccess;
+  return s.D == 128 ? flat_topk_for_d<128>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st)
+                    : flat_topk_for_d<64>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
+}
+
+hipError_t isa_select_prepare_device() {
+  hipError_t e = hipSuccess;
+  for (hipError_t x : {prepare_topk<128, 4>(), prepare_topk<128, 8>(), prepare_topk<128, 16>(),
+                       prepare_topk<128, 32>(), prepare_topk<128, 64>(), prepare_topk<64, 4>(),
+                       prepare_topk<64, 8>(), prepare_topk<64, 16>(), prepare_topk<64, 32>(),
+                       prepare_topk<64, 64>()})
+    if (e == hipSuccess) e = x;
+  return e;
 }

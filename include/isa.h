@@ -127,7 +127,8 @@ typedef struct {
 typedef struct {
   int32_t N_src, N_ctx, N, k_ctx, N_kv, n_flat, n_sharp, k_ns;
   size_t workspace_bytes; /* device workspace isa_forward needs */
-  size_t scores_bytes;    /* workspace isa_sharpness_split needs */
+  size_t scores_bytes;    /* workspace isa_sharpness_split and isa_coarse_residual
+                             need (the larger of the two) */
   size_t rope_bytes;      /* workspace isa_rope_pool_coarse needs (0 if RoPE off) */
   size_t noalloc_bytes;   /* scratch isa_forward_noalloc needs (it refuses the
                              call when this exceeds ISA_NOALLOC_SCRATCH_BYTES) */
@@ -177,11 +178,13 @@ ISA_API int isa_rope_pool_coarse(const isa_params_t* p, const void* Q, const voi
 ISA_API int isa_ctx_topk(const isa_params_t* p, const double* qc, const double* kc,
                  int32_t* ctx_idx, double* ctx_score, void* stream);
 
-/* Steps (1) coarse rows, (3) sharpness and split, (5) exact-set choice.
+/* Steps (1) coarse scores, (3) sharpness and split, (5) exact-set choice.
  * Needs qc, kc from isa_pool_coarse and ctx_idx from isa_ctx_topk. Writes
  * sharpness [B,H,N] (may be NULL), sharp_idx [B,H,n_sharp],
  * flat_idx [B,H,n_flat] and flat_exact_idx [B,H,n_flat,k_ns] (global ids,
- * rows ascending). `ws` must hold plan.scores_bytes bytes of device memory. */
+ * rows ascending). The coarse scores are formed where they are used and
+ * never stored; `ws` (at least plan.scores_bytes bytes of device memory)
+ * holds the sharpness values when `sharpness` is NULL. */
 ISA_API int isa_sharpness_split(const isa_params_t* p, const double* qc, const double* kc,
                         const int32_t* ctx_idx, double* sharpness, int32_t* sharp_idx,
                         int32_t* flat_idx, int32_t* flat_exact_idx, void* ws, size_t ws_bytes,
@@ -203,8 +206,8 @@ ISA_API int isa_flat_taylor_attn(const isa_params_t* p, const void* Q, const voi
 /* Step (6) residual: adds gamma * O_coarse_i (see above) to every token row
  * of block i of O, in place (bf16, rounded to nearest even). Needs qc, kc
  * from isa_pool_coarse, vc_bf16 (the bf16 V means) and ctx_idx. `ws` must
- * hold plan.scores_bytes bytes of device memory (the coarse rows are
- * recomputed there). Does nothing when gamma == 0. */
+ * hold plan.scores_bytes bytes of device memory (the coarse rows S[i, J]
+ * are formed there). Does nothing when gamma == 0. */
 ISA_API int isa_coarse_residual(const isa_params_t* p, const double* qc, const double* kc,
                                 const void* vc_bf16, const int32_t* ctx_idx, void* O, void* ws,
                                 size_t ws_bytes, void* stream);

@@ -69,9 +69,13 @@ def test_plan_matches_oracle_counts(isa):
         o = isa_oracle.make_plan(Ls, Lc, b, a_s, a_f, a_ns)
         for k in ("N_src", "N_ctx", "N", "k_ctx", "N_kv", "n_flat", "n_sharp", "k_ns"):
             assert pl[k] == getattr(o, k), (k, Ls, Lc, b, a_s, a_f, a_ns)
-        assert pl["workspace_bytes"] >= 40 * o.N * o.N_kv * 8
-        assert pl["scores_bytes"] >= 40 * o.N * o.N_kv * 8
+        # the coarse scores are never stored: no N * N_kv term without the residual
+        assert pl["scores_bytes"] == (40 * o.N * 8 + 255) // 256 * 256
         assert pl["rope_bytes"] == 0
+        # only the gamma residual keeps the coarse rows S[i, J] (fp64)
+        pg = isa.plan(isa.Params(1, 40, Ls, Lc, D, b, a_s, a_f, a_ns, gamma=0.5))
+        assert pg["scores_bytes"] >= 40 * o.N * o.N_kv * 8
+        assert pg["workspace_bytes"] - pl["workspace_bytes"] >= 40 * o.N * o.N_kv * 8
 
 
 def test_plan_rope_workspace(isa):
@@ -126,7 +130,8 @@ def test_calls_fail_before_launch(isa):
     assert L.isa_flat_taylor_attn(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake,
                                   fake, fake, None) == -1
     assert L.isa_coarse_residual(ctypes.byref(p), fake, fake, fake, fake, None, fake, 1 << 40, None) == -1
-    assert L.isa_coarse_residual(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 16, None) == -3
+    assert L.isa_coarse_residual(ctypes.byref(_params(isa, gamma=0.5)), fake, fake, fake, fake, fake, fake,
+                                 16, None) == -3
     rp = _params(isa, rope_base=10000.0)
     assert L.isa_rope_pool_coarse(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake,
                                   fake, fake, 1 << 40, None) == -1      # RoPE off
