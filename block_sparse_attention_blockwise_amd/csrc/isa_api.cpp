@@ -28,7 +28,7 @@ bool ratio_ok(double a) { return !std::isnan(a) && a >= 0.0 && a <= 1.0; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t qc, kc, kcb, vcb, ctx_idx, ctx_score, sharp, sharp_idx, flat_idx, exact, srows;
+  size_t qc, kc, kcb, vcb, ctx_idx, ctx_score, sharp, sharp_idx, flat_idx, exact, ftk, srows;
   size_t qr, kr, rope;          // RoPE buffers (only when rope_base > 0)
   size_t lse;                   // saved by isa_forward for isa_backward
   size_t delta, dkc, dvc, ebits, inv_off, inv_list;   // backward scratch
@@ -61,6 +61,8 @@ Layout make_layout(const IsaShape& s, bool with_backward = true) {
   l.sharp_idx = o; o = align256(o + at_least1(bh * s.n_sharp) * 4);
   l.flat_idx = o;  o = align256(o + at_least1(bh * s.n_flat) * 4);
   l.exact = o;     o = align256(o + at_least1(bh * s.n_flat * (size_t)s.k_ns) * 4);
+  // exact-set rows of the flat blocks in flight (only when they do not fit LDS)
+  l.ftk = o;       o = align256(o + isa_flat_topk_scratch_bytes(s));
   // coarse rows S[i, J]: only the gamma residual stores them
   l.srows = o;     o = align256(o + (s.gamma != 0.0f ? bh * s.N * (size_t)s.N_kv * 8 : 0));
   const size_t qkr = s.rope_base != 0.0 ? bh * (size_t)s.L * s.D * 2 : 0;
@@ -93,10 +95,15 @@ Layout make_layout(const IsaShape& s, bool with_backward = true) {
 }
 
 // Workspace of isa_sharpness_split: room for the sharpness values when the
-// caller passes none (the coarse scores are never stored). Workspace of
+// caller passes none, then the exact-set kernel's row scratch (the coarse
+// scores of the flat blocks in flight, bounded by its slot count, not by N;
+// none when 16 rows of J fit LDS). Workspace of
 // isa_coarse_residual: the coarse rows S[i, J] of every query block (gamma
 // != 0 only). The plan reports the larger of the two.
-size_t sharp_ws_bytes(const IsaShape& s) { return align256((size_t)s.B * s.H * s.N * 8); }
+size_t sharp_vals_bytes(const IsaShape& s) { return align256((size_t)s.B * s.H * s.N * 8); }
+size_t sharp_ws_bytes(const IsaShape& s) {
+  return sharp_vals_bytes(s) + align256(isa_flat_topk_scratch_bytes(s));
+}
 size_t residual_ws_bytes(const IsaShape& s) {
   return s.gamma != 0.0f ? align256((size_t)s.B * s.H * s.N * (size_t)s.N_kv * 8) : 0;
 }
@@ -250,9 +257,10 @@ int isa_sharpness_split(const isa_params_t* p, const double* qc, const double* k
   if (ws_bytes < sharp_ws_bytes(s)) return ISA_ERR_WORKSPACE;
   hipStream_t st = as_stream(stream);
   double* sharp = sharpness ? sharpness : (double*)ws;
+  double* ftk = (double*)((char*)ws + sharp_vals_bytes(s));
   hipError_t e = isa_launch_sharpness(s, qc, kc, sharp, st);
   if (e == hipSuccess) e = isa_launch_split(s, sharp, sharp_idx, flat_idx, st);
-  if (e == hipSuccess) e = isa_launch_flat_topk(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
+  if (e == hipSuccess) e = isa_launch_flat_topk(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, ftk, st);
   return hip_status(e);
 }
 
@@ -344,7 +352,7 @@ int forward_impl(const IsaShape& s, const void* Q, const void* K, const void* V,
   if (e == hipSuccess) e = isa_launch_ctx_topk(s, qc, kc, ctx_idx, ctx_score, st);
   if (e == hipSuccess) e = isa_launch_sharpness(s, qc, kc, sharp, st);
   if (e == hipSuccess) e = isa_launch_split(s, sharp, sharp_idx, flat_idx, st);
-  if (e == hipSuccess) e = isa_launch_flat_topk(s, qc, kc, ctx_idx, flat_idx, exact, st);
+  if (e == hipSuccess) e = isa_launch_flat_topk(s, qc, kc, ctx_idx, flat_idx, exact, (double*)(w + l.ftk), st);
   float* lse = l.lse ? (float*)(w + l.lse) : nullptr;
   if (e == hipSuccess) e = isa_launch_sharp_attn(s, q, k, v, ctx_idx, sharp_idx, (uint16_t*)O, lse, st);
   if (e == hipSuccess)

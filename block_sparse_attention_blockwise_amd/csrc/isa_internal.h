@@ -82,9 +82,13 @@ hipError_t isa_launch_sharpness(const IsaShape& s, const double* qc, const doubl
                                 hipStream_t st);
 hipError_t isa_launch_split(const IsaShape& s, const double* sharp, int32_t* sharp_idx,
                             int32_t* flat_idx, hipStream_t st);
+// `scratch`: isa_flat_topk_scratch_bytes(s) bytes of device memory (the
+// coarse rows of the flat blocks in flight when they do not fit LDS; may be
+// NULL when that size is 0).
+size_t isa_flat_topk_scratch_bytes(const IsaShape& s);
 hipError_t isa_launch_flat_topk(const IsaShape& s, const double* qc, const double* kc,
                                 const int32_t* ctx_idx, const int32_t* flat_idx,
-                                int32_t* flat_exact_idx, hipStream_t st);
+                                int32_t* flat_exact_idx, double* scratch, hipStream_t st);
 hipError_t isa_launch_coarse_residual(const IsaShape& s, const double* srows,
                                       const uint16_t* vc_bf16, const int32_t* ctx_idx,
                                       uint16_t* O, hipStream_t st);

@@ -141,32 +141,49 @@ __device__ inline int kept_block_id(const IsaShape& s, const int32_t* ctx_row, i
   return p < s.N_src ? p : ctx_row[p - s.N_src];
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2. Work item `id` of `total` (in dispatch order) is renamed so that each
+// XCD receives a contiguous run of items, i.e. mostly one (batch, head),
+// whose pooled keys then stay in that XCD's L2.
+__device__ inline int xcd_order(int id, int total) {
+  if ((total & 7) != 0) return id;
+  return (id & 7) * (total >> 3) + (id >> 3);
+}
+
 // ------------------------------------------- coarse scores on matrix cores
 // v_mfma_f64_16x16x4f64: lane l supplies A[m][k] and B[k][n] with m = n =
 // l % 16, k = l / 16, and receives C[l / 16 + 4 i][l % 16], i = 0..3. Step
-// kk of a D-long dot product pairs dimension (D/4) k + kk of the A row and
-// of the B column, so each lane holds one contiguous quarter of a row.
+// kk = 2x + e of a D-long dot product pairs dimension 8x + 2k + e of the A
+// row and of the B column: the four lanes of one row read 64 contiguous
+// bytes per 16-byte load, so a load instruction touches 16 rows' segments
+// rather than 64 scattered pieces.
 typedef double double4_t __attribute__((ext_vector_type(4)));
 
+// Lane l's D/4 dimensions of one row (pairs 8x + 2k, 8x + 2k + 1). Callers
+// point past-the-end lanes at a readable row (row 0 of the head) and discard
+// the products those lanes feed, so no value needs zeroing.
 template <int D>
-__device__ inline void load_frag(const double* __restrict__ row, bool valid, int k,
-                                 double (&f)[D / 4]) {
+__device__ inline void load_frag(const double* __restrict__ row, int k, double (&f)[D / 4]) {
 #pragma unroll
   for (int x = 0; x < D / 8; ++x) {
-    const double2 v = valid ? *reinterpret_cast<const double2*>(row + (D / 4) * k + 2 * x)
-                            : make_double2(0.0, 0.0);
+    const double2 v = *reinterpret_cast<const double2*>(row + 8 * x + 2 * k);
     f[2 * x] = v.x;
     f[2 * x + 1] = v.y;
   }
 }
 
-// Raw dot products of the 16 A rows with the 16 B rows held by the wave.
+// Raw dot products of the 16 A rows with the 16 B rows held by the wave:
+// two independent accumulation chains (even and odd steps kk), so each
+// product's accumulator was written two products earlier, added at the end.
 template <int D>
 __device__ inline double4_t coarse_mma(const double (&a)[D / 4], const double (&b)[D / 4]) {
-  double4_t c = {0.0, 0.0, 0.0, 0.0};
+  double4_t c0 = {0.0, 0.0, 0.0, 0.0}, c1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int kk = 0; kk < D / 4; ++kk) c = __builtin_amdgcn_mfma_f64_16x16x4f64(a[kk], b[kk], c, 0, 0, 0);
-  return c;
+  for (int kk = 0; kk < D / 4; kk += 2) {
+    c0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[kk], b[kk], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[kk + 1], b[kk + 1], c1, 0, 0, 0);
+  }
+  return c0 + c1;
 }
 
 // ---------------------------------------------------------------- step (2)
@@ -357,20 +374,30 @@ __device__ inline void stats_merge(double& m, double& z, double& w, double m2, d
   m = mm;
 }
 
+// The source key blocks are streamed through LDS 16 rows (one tile of
+// columns) at a time, loaded once per workgroup with contiguous 16-byte
+// loads and shared by its waves; two buffers let the next tile's loads run
+// while the current tile's products do. A staged row is D + 2 doubles, so the
+// 16 lanes of one k read 16 different bank groups.
 template <int D>
 __global__ __launch_bounds__(64 * kSharpWaves) void sharpness_kernel(IsaShape s, const double* __restrict__ qc,
                                                                      const double* __restrict__ kc,
                                                                      double* __restrict__ sharp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int bh = blockIdx.y;
-  const int r0 = (blockIdx.x * kSharpWaves + wave) * 16;
-  if (r0 >= s.N) return;   // whole wave; no workgroup barrier in this kernel
+  constexpr int NT = 64 * kSharpWaves;
+  constexpr int ST2 = (D + 2) / 2;            // double2 per staged row
+  constexpr int CPT = 16 * (D / 2) / NT;      // double2 each thread stages per tile
+  static_assert(CPT * NT == 16 * (D / 2), "tile must split evenly over the threads");
+  __shared__ double2 tile[2][16 * ST2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int id = xcd_order(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int bh = id / gridDim.x;
+  const int r0 = ((id % gridDim.x) * kSharpWaves + wave) * 16;   // may be >= N: computes, never writes
   const int m16 = lane & 15, k = lane >> 4;
   const double* qh = qc + (size_t)bh * s.N * D;
   const double* kh = kc + (size_t)bh * s.N * D;   // source key blocks are rows 0..N_src-1
-  double a[D / 4];
-  load_frag<D>(qh + (size_t)(r0 + m16 < s.N ? r0 + m16 : 0) * D, r0 + m16 < s.N, k, a);
-  const double sq = sqrt((double)D);
+  double a[D / 4];   // rows past N read row 0; their statistics are never written
+  load_frag<D>(qh + (size_t)(r0 + m16 < s.N ? r0 + m16 : 0) * D, k, a);
+  const double rsq = 1.0 / sqrt((double)D);   // S = dot / sqrt(D) as a product (one rounding)
   double mx[4], z[4], w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -378,15 +405,50 @@ __global__ __launch_bounds__(64 * kSharpWaves) void sharpness_kernel(IsaShape s,
     z[i] = 0.0;
     w[i] = 0.0;
   }
-  for (int c0 = 0; c0 < s.N_src; c0 += 16) {
-    const int c = c0 + m16;   // this lane's column
-    double b[D / 4];
-    load_frag<D>(kh + (size_t)(c < s.N_src ? c : 0) * D, c < s.N_src, k, b);
-    const double4_t acc = coarse_mma<D>(a, b);
-    if (c < s.N_src) {
+  // thread tid stages double2 c2 of tile row `row`, for q = tid + NT u
+  const int ntile = (s.N_src + 15) / 16;
+  double2 g[CPT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) stats_add(acc[i] / sq, mx[i], z[i], w[i]);
+  for (int u = 0; u < CPT; ++u) {   // columns past N_src stage row 0; their products are skipped
+    const int q = tid + NT * u, row = q / (D / 2), c2 = q % (D / 2);
+    const int col = row < s.N_src ? row : 0;
+    g[u] = reinterpret_cast<const double2*>(kh + (size_t)col * D)[c2];
+  }
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int q = tid + NT * u, row = q / (D / 2), c2 = q % (D / 2);
+    tile[0][row * ST2 + c2] = g[u];
+  }
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    // the next tile (the last tile again on the last pass: a harmless
+    // re-read into the buffer nobody reads any more)
+    const int cn = 16 * (t + 1 < ntile ? t + 1 : t);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int q = tid + NT * u, row = q / (D / 2), c2 = q % (D / 2);
+      const int col = cn + row < s.N_src ? cn + row : 0;
+      g[u] = reinterpret_cast<const double2*>(kh + (size_t)col * D)[c2];
     }
+    double b[D / 4];
+    const double2* rp = &tile[t & 1][m16 * ST2];
+#pragma unroll
+    for (int x = 0; x < D / 8; ++x) {
+      const double2 v = rp[4 * x + k];
+      b[2 * x] = v.x;
+      b[2 * x + 1] = v.y;
+    }
+    const double4_t acc = coarse_mma<D>(a, b);
+    if (16 * t + m16 < s.N_src) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stats_add(acc[i] * rsq, mx[i], z[i], w[i]);
+    }
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int q = tid + NT * u, row = q / (D / 2), c2 = q % (D / 2);
+      tile[(t + 1) & 1][row * ST2 + c2] = g[u];
+    }
+    __syncthreads();
   }
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) {
@@ -435,20 +497,22 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(IsaShape s, const 
 }
 
 // --------------------------------------------- step (5) exact set per block
-// One wave selects the k largest of the n keys it holds (lower index wins
-// ties). Lane l holds items p = l + 64u, so index order is u-major,
-// lane-minor. Counting uses ballots (scalar popcounts), no workgroup barrier.
+// One wave selects the k largest keys it holds (lower index wins ties).
+// Lane l holds items p = l + 64u, so index order is u-major, lane-minor;
+// padding items hold key 0, below every key of a real score (order_key of a
+// non-NaN fp64 value is nonzero), so they are never counted (k >= 1).
+// Counting uses ballots (scalar popcounts), no workgroup barrier. Returns the
+// k-th largest key T; the selected items are every key > T and the first
+// `need` = k - #{key > T} keys equal to T in index order.
 template <int IPL>
-__device__ inline void wave_topk(const unsigned long long (&key)[IPL], int n, int k,
-                                 bool (&sel)[IPL]) {
-  const int lane = threadIdx.x & 63;
-  const unsigned long long below = (1ull << lane) - 1ull;
+__device__ inline unsigned long long wave_topk_threshold(const unsigned long long (&key)[IPL], int k,
+                                                         int& need) {
   unsigned long long T = 0;
   for (int bit = 63; bit >= 0; --bit) {
     const unsigned long long trial = T | (1ull << bit);
     int c = 0;
 #pragma unroll
-    for (int u = 0; u < IPL; ++u) c += __popcll(__ballot(lane + 64 * u < n && key[u] >= trial));
+    for (int u = 0; u < IPL; ++u) c += __popcll(__ballot(key[u] >= trial));
     if (c >= k) {
       T = trial;
       if (c == k) break;   // exactly k at or above T: the top k (see block_topk)
@@ -456,46 +520,43 @@ __device__ inline void wave_topk(const unsigned long long (&key)[IPL], int n, in
   }
   int gt = 0;
 #pragma unroll
-  for (int u = 0; u < IPL; ++u) gt += __popcll(__ballot(lane + 64 * u < n && key[u] > T));
-  const int need = k - gt;
-  int before = 0;
-#pragma unroll
-  for (int u = 0; u < IPL; ++u) {
-    const bool valid = lane + 64 * u < n;
-    const bool tie = valid && key[u] == T;
-    const unsigned long long m = __ballot(tie);
-    const int rank = before + __popcll(m & below);
-    sel[u] = (valid && key[u] > T) || (tie && rank < need);
-    before += __popcll(m);
-  }
+  for (int u = 0; u < IPL; ++u) gt += __popcll(__ballot(key[u] > T));
+  need = k - gt;
+  return T;
 }
 
-// One workgroup takes R consecutive flat blocks (R = 16, 8, 4 or 2, as the
-// rows of S fit the LDS budget). Phase 1: the matrix cores form S[i, J] for
-// those R rows (one 16-row tile, rows past R zero), 16 positions of J per
-// tile, tiles spread over the waves, into LDS. Phase 2: one wave per row
-// reads its row back (lane l: positions l + 64 u) and selects the top k_ns.
-constexpr int kFlatTopkWaves = 4;
-constexpr int kFlatTopkLds = 80 * 1024;   // bytes of S rows per workgroup
+// Work item g = one group of 16 consecutive flat blocks of one (batch, head)
+// (one 16-row matrix-core tile). Phase 1: the matrix cores form the raw dot
+// products Qc_i . Kc_j (S[i, J] up to the positive factor 1/sqrt(D), which
+// does not change the order) of those rows, 16 positions of J per tile,
+// tiles spread over the waves; the next tile's fragments load while the
+// current tile's products run. The rows go to LDS when 16 rows of J fit
+// (N_kv <= kFlatLdsCols), else to this workgroup's own slot of a global
+// scratch buffer, and the grid is then persistent (kFlatSlots workgroups
+// walking the groups), which bounds the scratch by the slot count, not by N.
+// Phase 2: one wave per row reads its row back (lane l: positions l + 64 u)
+// and selects the top k_ns.
+// Each pass of the grid takes its groups in XCD-contiguous order.
+constexpr int kFlatLdsWaves = 4;
+constexpr int kFlatGlobalWaves = 8;
+constexpr int kFlatLdsCols = 640;   // 16 rows x 640 fp64 = 80 KiB of LDS
+constexpr int kFlatSlots = 256;
 
-__host__ __device__ inline int flat_topk_rows(int N_kv) {
-  int r = 16;
-  while (r > 2 && (size_t)r * N_kv * sizeof(double) > (size_t)kFlatTopkLds) r >>= 1;
-  return r;
-}
+__host__ __device__ inline bool flat_rows_in_lds(int N_kv) { return N_kv <= kFlatLdsCols; }
 
-template <int D, int IPL>
-__global__ __launch_bounds__(64 * kFlatTopkWaves) void flat_topk_kernel(IsaShape s, const double* __restrict__ qc,
-                                                                        const double* __restrict__ kc,
-                                                                        const int32_t* __restrict__ ctx_idx,
-                                                                        const int32_t* __restrict__ flat_idx,
-                                                                        int32_t* __restrict__ exact, int R) {
-  extern __shared__ double srow[];   // [R][N_kv]
+// One group: flat blocks f0 .. f0 + 15 of (batch, head) bh; `srow` holds
+// 16 x N_kv doubles. DB: double-buffered fragment loads (the LDS form, at
+// most two waves per SIMD); the global form (twice the waves) single-buffers.
+template <int D, int IPL, int NW, bool DB>
+__device__ inline void flat_group(const IsaShape& s, const double* __restrict__ qc,
+                                  const double* __restrict__ kc, const int32_t* __restrict__ ctx_idx,
+                                  const int32_t* __restrict__ flat_idx, int32_t* __restrict__ exact,
+                                  double* __restrict__ srow, int bh, int f0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int bh = blockIdx.y;
-  const int f0 = blockIdx.x * R;
-  const int nr = min(R, s.n_flat - f0);
   const int m16 = lane & 15, k = lane >> 4;
+  const int ntile = (s.N_kv + 15) / 16;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const int nr = min(16, s.n_flat - f0);
   const int32_t* frow = flat_idx + (size_t)bh * s.n_flat;
   const int32_t* ctx_row = ctx_idx + (size_t)bh * s.k_ctx;
   const double* qh = qc + (size_t)bh * s.N * D;
@@ -505,44 +566,97 @@ __global__ __launch_bounds__(64 * kFlatTopkWaves) void flat_topk_kernel(IsaShape
     const int i = frow[f0 + m16];
     qi = (i >= 0 && i < s.N) ? i : -1;
   }
-  double a[D / 4];
-  load_frag<D>(qh + (size_t)(qi >= 0 ? qi : 0) * D, qi >= 0, k, a);
-  const double sq = sqrt((double)D);
-  const int ntile = (s.N_kv + 15) / 16;
-  for (int t = wave; t < ntile; t += kFlatTopkWaves) {
-    const int p = t * 16 + m16;   // this lane's position in J
-    const int j = p < s.N_kv ? kept_block_id(s, ctx_row, p) : -1;
-    const bool ok = j >= 0 && j < s.N;
-    double b[D / 4];
-    load_frag<D>(kh + (size_t)(ok ? j : 0) * D, ok, k, b);
-    const double4_t acc = coarse_mma<D>(a, b);
+  double a[D / 4];   // rows past the group's flat blocks read row 0; never stored
+  load_frag<D>(qh + (size_t)(qi >= 0 ? qi : 0) * D, k, a);
+  // lane's position p = 16 t + m16 of J; positions past N_kv read row 0
+  auto col_row = [&](int t) -> const double* {
+    const int p = t * 16 + m16;
+    const int j = (t < ntile && p < s.N_kv) ? kept_block_id(s, ctx_row, p) : -1;
+    return kh + (size_t)((j >= 0 && j < s.N) ? j : 0) * D;
+  };
+  auto put = [&](int t, const double4_t& acc) {
+    const int p = t * 16 + m16;
     if (p < s.N_kv) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = k + 4 * i;
-        if (r < nr) srow[(size_t)r * s.N_kv + p] = acc[i] / sq;
+        if (r < nr) srow[(size_t)r * s.N_kv + p] = acc[i];
       }
+    }
+  };
+  if constexpr (DB) {
+    double b0[D / 4], b1[D / 4];
+    load_frag<D>(col_row(wave), k, b0);
+    for (int t = wave; t < ntile; t += 2 * NW) {
+      load_frag<D>(col_row(t + NW), k, b1);
+      put(t, coarse_mma<D>(a, b0));
+      load_frag<D>(col_row(t + 2 * NW), k, b0);
+      if (t + NW < ntile) put(t + NW, coarse_mma<D>(a, b1));
+    }
+  } else {
+    for (int t = wave; t < ntile; t += NW) {
+      double b[D / 4];
+      load_frag<D>(col_row(t), k, b);
+      put(t, coarse_mma<D>(a, b));
     }
   }
   __syncthreads();
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (int r = wave; r < nr; r += kFlatTopkWaves) {
+  for (int r = wave; r < nr; r += NW) {
     unsigned long long key[IPL];
-    bool sel[IPL];
 #pragma unroll
     for (int u = 0; u < IPL; ++u) {
       const int p = lane + 64 * u;
       key[u] = p < s.N_kv ? order_key(srow[(size_t)r * s.N_kv + p]) : 0ull;
     }
-    wave_topk<IPL>(key, s.N_kv, s.k_ns, sel);
+    int need;
+    const unsigned long long T = wave_topk_threshold<IPL>(key, s.k_ns, need);
+    // selected positions of J in ascending order, then their global block
+    // ids (the map from positions to ids is increasing)
     int32_t* out = exact + ((size_t)bh * s.n_flat + f0 + r) * s.k_ns;
-    int base = 0;
+    int base = 0, ties = 0;
 #pragma unroll
     for (int u = 0; u < IPL; ++u) {
-      const unsigned long long msk = __ballot(sel[u]);
-      if (sel[u]) out[base + __popcll(msk & below)] = kept_block_id(s, ctx_row, lane + 64 * u);
+      const bool tie = key[u] == T;
+      const unsigned long long tm = __ballot(tie);
+      const bool sel = key[u] > T || (tie && ties + __popcll(tm & below) < need);
+      ties += __popcll(tm);
+      const unsigned long long msk = __ballot(sel);
+      if (sel) out[base + __popcll(msk & below)] = lane + 64 * u;
       base += __popcll(msk);
     }
+    for (int q = lane; q < s.k_ns; q += 64) out[q] = kept_block_id(s, ctx_row, out[q]);
+  }
+}
+
+// LDS form: one group per workgroup.
+template <int D, int IPL>
+__global__ __launch_bounds__(64 * kFlatLdsWaves) void flat_topk_lds_kernel(
+    IsaShape s, const double* __restrict__ qc, const double* __restrict__ kc,
+    const int32_t* __restrict__ ctx_idx, const int32_t* __restrict__ flat_idx,
+    int32_t* __restrict__ exact) {
+  extern __shared__ double lds_rows[];   // [16][N_kv]
+  const int gph = (s.n_flat + 15) / 16;   // groups per (batch, head)
+  const int g = xcd_order(blockIdx.x, gridDim.x);
+  flat_group<D, IPL, kFlatLdsWaves, true>(s, qc, kc, ctx_idx, flat_idx, exact, lds_rows, g / gph,
+                                          (g % gph) * 16);
+}
+
+// Global form: persistent; workgroup x owns rows x of the scratch and walks
+// the groups x, x + gridDim.x, ... (each pass of the grid remapped on its own).
+template <int D, int IPL>
+__global__ __launch_bounds__(64 * kFlatGlobalWaves) void flat_topk_global_kernel(
+    IsaShape s, const double* __restrict__ qc, const double* __restrict__ kc,
+    const int32_t* __restrict__ ctx_idx, const int32_t* __restrict__ flat_idx,
+    int32_t* __restrict__ exact, double* __restrict__ scratch) {
+  double* srow = scratch + (size_t)blockIdx.x * 16 * s.N_kv;
+  const int gph = (s.n_flat + 15) / 16;
+  const int total = gph * s.B * s.H;
+  for (int pass0 = 0; pass0 + (int)blockIdx.x < total; pass0 += gridDim.x) {
+    const int npass = min((int)gridDim.x, total - pass0);
+    const int g = pass0 + xcd_order(blockIdx.x, npass);
+    flat_group<D, IPL, kFlatGlobalWaves, false>(s, qc, kc, ctx_idx, flat_idx, exact, srow, g / gph,
+                                                (g % gph) * 16);
+    __syncthreads();   // the rows' storage is reused by the next group
   }
 }
 
@@ -706,52 +820,70 @@ hipError_t isa_launch_split(const IsaShape& s, const double* sharp, int32_t* sha
 
 namespace {
 
-// The exact-set kernels keep S rows in dynamic LDS beyond the default
-// limit: raised once per instantiation and device (host-side only).
+// The LDS form of the exact-set kernel keeps 16 rows of S in dynamic LDS
+// beyond the default limit: raised once per instantiation and device
+// (host-side only).
 template <int D, int IPL>
 hipError_t prepare_topk() {
   static unsigned long long done = 0;
-  return isa_ensure_dyn_lds(reinterpret_cast<const void*>(&flat_topk_kernel<D, IPL>), kFlatTopkLds, &done);
+  return isa_ensure_dyn_lds(reinterpret_cast<const void*>(&flat_topk_lds_kernel<D, IPL>),
+                            16 * kFlatLdsCols * (int)sizeof(double), &done);
 }
 
 template <int D, int IPL>
 hipError_t launch_flat_topk(const IsaShape& s, const double* qc, const double* kc, const int32_t* ctx_idx,
-                            const int32_t* flat_idx, int32_t* flat_exact_idx, hipStream_t st) {
-  const hipError_t e = prepare_topk<D, IPL>();
-  if (e != hipSuccess) return e;
-  const int R = flat_topk_rows(s.N_kv);
-  dim3 grid((s.n_flat + R - 1) / R, s.B * s.H);
-  const size_t lds = (size_t)R * s.N_kv * sizeof(double);
-  flat_topk_kernel<D, IPL><<<grid, 64 * kFlatTopkWaves, lds, st>>>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, R);
+                            const int32_t* flat_idx, int32_t* flat_exact_idx, double* scratch,
+                            hipStream_t st) {
+  const int total = (s.n_flat + 15) / 16 * s.B * s.H;
+  if (flat_rows_in_lds(s.N_kv)) {
+    const hipError_t e = prepare_topk<D, IPL>();
+    if (e != hipSuccess) return e;
+    const size_t lds = (size_t)16 * s.N_kv * sizeof(double);
+    flat_topk_lds_kernel<D, IPL><<<total, 64 * kFlatLdsWaves, lds, st>>>(s, qc, kc, ctx_idx, flat_idx,
+                                                                          flat_exact_idx);
+  } else {
+    const int grid = total < kFlatSlots ? total : kFlatSlots;
+    flat_topk_global_kernel<D, IPL><<<grid, 64 * kFlatGlobalWaves, 0, st>>>(s, qc, kc, ctx_idx, flat_idx,
+                                                                            flat_exact_idx, scratch);
+  }
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t flat_topk_for_d(const IsaShape& s, const double* qc, const double* kc, const int32_t* ctx_idx,
-                           const int32_t* flat_idx, int32_t* flat_exact_idx, hipStream_t st) {
+                           const int32_t* flat_idx, int32_t* flat_exact_idx, double* scratch,
+                           hipStream_t st) {
   const int ipl = (s.N_kv + 63) / 64;
-  if (ipl <= 4) return launch_flat_topk<D, 4>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
-  if (ipl <= 8) return launch_flat_topk<D, 8>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
-  if (ipl <= 16) return launch_flat_topk<D, 16>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
-  if (ipl <= 32) return launch_flat_topk<D, 32>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
-  return launch_flat_topk<D, 64>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
+  if (ipl <= 4) return launch_flat_topk<D, 4>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, scratch, st);
+  if (ipl <= 8) return launch_flat_topk<D, 8>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, scratch, st);
+  if (ipl <= 12) return launch_flat_topk<D, 12>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, scratch, st);
+  if (ipl <= 16) return launch_flat_topk<D, 16>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, scratch, st);
+  if (ipl <= 24) return launch_flat_topk<D, 24>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, scratch, st);
+  if (ipl <= 32) return launch_flat_topk<D, 32>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, scratch, st);
+  if (ipl <= 48) return launch_flat_topk<D, 48>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, scratch, st);
+  return launch_flat_topk<D, 64>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, scratch, st);
 }
 
 }  // namespace
 
+size_t isa_flat_topk_scratch_bytes(const IsaShape& s) {
+  if (s.n_flat == 0 || s.k_ns == 0 || flat_rows_in_lds(s.N_kv)) return 0;
+  return (size_t)kFlatSlots * 16 * s.N_kv * sizeof(double);
+}
+
 hipError_t isa_launch_flat_topk(const IsaShape& s, const double* qc, const double* kc, const int32_t* ctx_idx,
-                                const int32_t* flat_idx, int32_t* flat_exact_idx, hipStream_t st) {
+                                const int32_t* flat_idx, int32_t* flat_exact_idx, double* scratch,
+                                hipStream_t st) {
   if (s.n_flat == 0 || s.k_ns == 0) return hipSuccess;
-  return s.D == 128 ? flat_topk_for_d<128>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st)
-                    : flat_topk_for_d<64>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, st);
+  return s.D == 128 ? flat_topk_for_d<128>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, scratch, st)
+                    : flat_topk_for_d<64>(s, qc, kc, ctx_idx, flat_idx, flat_exact_idx, scratch, st);
 }
 
 hipError_t isa_select_prepare_device() {
   hipError_t e = hipSuccess;
-  for (hipError_t x : {prepare_topk<128, 4>(), prepare_topk<128, 8>(), prepare_topk<128, 16>(),
-                       prepare_topk<128, 32>(), prepare_topk<128, 64>(), prepare_topk<64, 4>(),
-                       prepare_topk<64, 8>(), prepare_topk<64, 16>(), prepare_topk<64, 32>(),
-                       prepare_topk<64, 64>()})
+  // LDS rows are used only while 16 rows of J fit (at most 10 keys per lane)
+  for (hipError_t x : {prepare_topk<128, 4>(), prepare_topk<128, 8>(), prepare_topk<128, 12>(),
+                       prepare_topk<64, 4>(), prepare_topk<64, 8>(), prepare_topk<64, 12>()})
     if (e == hipSuccess) e = x;
   return e;
 }

@@ -183,8 +183,11 @@ ISA_API int isa_ctx_topk(const isa_params_t* p, const double* qc, const double* 
  * sharpness [B,H,N] (may be NULL), sharp_idx [B,H,n_sharp],
  * flat_idx [B,H,n_flat] and flat_exact_idx [B,H,n_flat,k_ns] (global ids,
  * rows ascending). The coarse scores are formed where they are used and
- * never stored; `ws` (at least plan.scores_bytes bytes of device memory)
- * holds the sharpness values when `sharpness` is NULL. */
+ * never stored as a whole; `ws` (at least plan.scores_bytes bytes of device
+ * memory) holds the sharpness values when `sharpness` is NULL, then, when
+ * N_kv > 640 (16 rows of J no longer fit LDS), the exact-set selection's row
+ * scratch: 256 x 16 x N_kv fp64 (the rows of the flat blocks in flight,
+ * independent of N). */
 ISA_API int isa_sharpness_split(const isa_params_t* p, const double* qc, const double* kc,
                         const int32_t* ctx_idx, double* sharpness, int32_t* sharp_idx,
                         int32_t* flat_idx, int32_t* flat_exact_idx, void* ws, size_t ws_bytes,

@@ -69,8 +69,11 @@ def test_plan_matches_oracle_counts(isa):
         o = isa_oracle.make_plan(Ls, Lc, b, a_s, a_f, a_ns)
         for k in ("N_src", "N_ctx", "N", "k_ctx", "N_kv", "n_flat", "n_sharp", "k_ns"):
             assert pl[k] == getattr(o, k), (k, Ls, Lc, b, a_s, a_f, a_ns)
-        # the coarse scores are never stored: no N * N_kv term without the residual
-        assert pl["scores_bytes"] == (40 * o.N * 8 + 255) // 256 * 256
+        # the coarse scores are never stored: no N * N_kv term without the
+        # residual; only the exact-set kernel's row scratch (256 slots of 16
+        # rows of J, fp64) when 16 rows of J (N_kv > 640) do not fit LDS
+        ftk = 256 * 16 * o.N_kv * 8 if (o.N_kv > 640 and o.n_flat > 0 and o.k_ns > 0) else 0
+        assert pl["scores_bytes"] == (40 * o.N * 8 + 255) // 256 * 256 + (ftk + 255) // 256 * 256
         assert pl["rope_bytes"] == 0
         # only the gamma residual keeps the coarse rows S[i, J] (fp64)
         pg = isa.plan(isa.Params(1, 40, Ls, Lc, D, b, a_s, a_f, a_ns, gamma=0.5))
