@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "ISA fwd latency (ms) + effective TFLOP/s & MFMA util at 64K tokens, H=40, D=128"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PEAK_FP64_TFLOPS = 78.6     # dense fp64 matrix-core peak
 WORKLOAD = dict(stream=4, B=1, H=40, L_src=32768, L_ctx=32768, D=128, b=64,
                 alpha_s=0.125, alpha_f=0.5, alpha_ns=0.0625)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sharp_attn_64k_traffic.json")
@@ -296,8 +297,20 @@ def selection_bytes(p, pl):
         "ctx_topk_kernel": BH * ((pl["N_src"] + pl["N_ctx"]) * D * 8 + pl["k_ctx"] * 4 + pl["N_ctx"] * 8),
         "sharpness_kernel": BH * ((N + pl["N_src"]) * D * 8 + N * 8),
         "split_kernel": BH * N * (8 + 4),
-        "flat_topk_kernel": BH * ((pl["n_flat"] + pl["N_kv"]) * D * 8 + pl["k_ctx"] * 4 + pl["n_flat"] * 4
-                                  + pl["n_flat"] * pl["k_ns"] * 4),
+        # LDS-row and persistent global-row forms share this prefix
+        "flat_topk_": BH * ((pl["n_flat"] + pl["N_kv"]) * D * 8 + pl["k_ctx"] * 4 + pl["n_flat"] * 4
+                            + pl["n_flat"] * pl["k_ns"] * 4),
+    }
+
+
+# fp64 matrix-core FLOPs per launch of the selection kernels that form coarse
+# scores (2*D per score): these are bound by the fp64 MFMA rate, not by HBM.
+def selection_flops(p, pl):
+    BH, D = p.B * p.H, p.D
+    return {
+        "ctx_topk_kernel": BH * 2 * D * pl["N_src"] * pl["N_ctx"],
+        "sharpness_kernel": BH * 2 * D * pl["N"] * pl["N_src"],
+        "flat_topk_": BH * 2 * D * pl["n_flat"] * pl["N_kv"],
     }
 
 
@@ -339,6 +352,10 @@ def selection_rates(torch, p, pl, fn, reps):
         ms = float(np.mean(hits))
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[kern] = {"ms": ms, "bytes": nbytes, "gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
+        fl = selection_flops(p, pl).get(kern)
+        if fl is not None:
+            tf = fl / (ms * 1e-3) / 1e12
+            out[kern].update({"fp64_flops": fl, "tflops": tf, "frac_of_fp64_mfma_peak": tf / PEAK_FP64_TFLOPS})
     return out
 
 

@@ -33,10 +33,11 @@
 //   * exp is exp2 with log2(e)/sqrt(D) folded into the exponent's fma.
 // The sharp and dense paths are software pipelined: while the softmax of
 // tile t runs on the vector ALUs, the matrix cores already compute the scores
-// of tile t+1 (K double buffered, V and the per-key logit offsets triple
-// buffered in LDS, one workgroup barrier per tile). Tiles that need additive
-// logits (padding, partial blocks) are ordered last so the steady state runs
-// without them.
+// of tile t+1; K and V are triple buffered in LDS and copied there straight
+// from global memory (global_load_lds_dwordx4: no register staging, no LDS
+// store instructions) two tiles ahead, one workgroup barrier per tile. Tiles
+// that need additive logits (padding, partial blocks) are ordered last so
+// the steady state runs without them.
 // K and V rows are padded to 2D+32 bytes in LDS; with that stride the 16-byte
 // K reads and the 8-byte transposing V reads measure free of bank conflicts.
 #include "isa_internal.h"
@@ -366,12 +367,17 @@ void attn_kernel(AttnArgs a) {
   static_assert(CH >= 1 && (kKeyTile * CPR) % NT == 0, "tile split");
   static_assert(NT % CPR == 0, "chunk column must be fixed per thread");
 
-  constexpr int NKB = PIPE ? 2 : 1;    // K buffers
-  constexpr int NVB = PIPE ? 3 : 1;    // V / logit-offset buffers
-  static_assert(NVB == 1 || NVB == 2 || NVB == 3, "buffers");
-  __shared__ __attribute__((aligned(16))) char k_lds[NKB][kKeyTile * KSTR];
-  __shared__ __attribute__((aligned(16))) char v_lds[NVB][kKeyTile * VSTR];
-  __shared__ __attribute__((aligned(16))) float bias_lds[NVB][kKeyTile];
+  // Buffer 0 of K and V (the tail and non-pipelined paths use only these);
+  // the pipelined path adds two more of each as separate arrays, so that the
+  // compiler can tell the asynchronous global->LDS copies into one buffer
+  // apart from the reads of another.
+  __shared__ __attribute__((aligned(16))) char k_lds[1][kKeyTile * KSTR];
+  __shared__ __attribute__((aligned(16))) char v_lds[1][kKeyTile * VSTR];
+  __shared__ __attribute__((aligned(16))) char k_ld1[PIPE ? kKeyTile * KSTR : 16];
+  __shared__ __attribute__((aligned(16))) char k_ld2[PIPE ? kKeyTile * KSTR : 16];
+  __shared__ __attribute__((aligned(16))) char v_ld1[PIPE ? kKeyTile * VSTR : 16];
+  __shared__ __attribute__((aligned(16))) char v_ld2[PIPE ? kKeyTile * VSTR : 16];
+  __shared__ __attribute__((aligned(16))) float bias_lds[1][kKeyTile];
   // Sharp path: token range of every kept block, packed (start << 7) | n_j,
   // indexed by position in J. Flat path (dynamic LDS): the same for E_i, then
   // (j << 8) | (n_j << 1) | in_E for every position of J.
@@ -590,68 +596,101 @@ void attn_kernel(AttnArgs a) {
       pv_tile<D, QT, NMT>(vb, pk, oacc, g, c16);
     }
   } else {
-    // Steady state: the leading tiles, which carry no additive logits.
+    // Steady state: the leading tiles, which carry no additive logits. K
+    // and V go global -> LDS directly (global_load_lds_dwordx4, no register
+    // staging), three buffers each; tile t+2 is copied while tile t is
+    // processed and waited for before the barrier that ends the step.
     const int P = a.ntiles_plain;
     if (P > 0) {
-      // Prologue: tiles 0 and 1 in LDS, scores of tile 0 in registers.
-      ISA_LOAD_PLAIN(0)
-      ISA_STORE_PLAIN(0, 0)
-      if (P > 1) {
-        ISA_LOAD_PLAIN(1)
-        ISA_STORE_PLAIN(1, 1)
+      constexpr int KTB = kKeyTile * KSTR;            // bytes of one staged tile
+      constexpr int NPC = KTB / 1024;                  // 1 KiB pieces per tile
+      constexpr int NPW = (NPC + NWAVES - 1) / NWAVES; // pieces per wave, at most
+      static_assert(KTB % 1024 == 0, "tile must be whole 1 KiB pieces");
+      // Wave w copies pieces w, w + NWAVES, ... of each buffer; lane l of a
+      // piece holds its bytes 16 l .. 16 l + 15, i.e. chunk (x % KSTR) / 16 of
+      // staged row x / KSTR (padding chunks copy row data that is never read).
+      // A piece never straddles a kept block (block starts fall on 1 KiB
+      // boundaries for b = 32, 64), so its block start is wave-uniform; the
+      // lane's element offset within the block is fixed for every tile.
+      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+      int dma_off[NPW];
+#pragma unroll
+      for (int pp = 0; pp < NPW; ++pp) {
+        const int x = (pp * NWAVES + wave_u) * 1024 + 16 * lane;
+        const int row = x / KSTR, col = x - row * KSTR;
+        const int ce = col < 2 * D ? col / 2 : 0;
+        dma_off[pp] = (MODE == kDense ? row : (row & (b - 1))) * D + ce;
       }
+#define ISA_DMA_TILE(T, KD, VD)                                                  \
+      _Pragma("unroll") for (int pp = 0; pp < NPW; ++pp) {                       \
+        const int piece = pp * NWAVES + wave_u;                                  \
+        if (piece < NPC) {                                                       \
+          size_t base;                                                           \
+          if (MODE == kDense) {                                                  \
+            base = (size_t)(T) * kKeyTile;                                       \
+          } else {                                                               \
+            const int blk = ((piece * 1024) / KSTR) >> lb;                       \
+            base = (size_t)(__builtin_amdgcn_readfirstlane(tc.tab[(T) * tc.per + blk]) >> 7); \
+          }                                                                      \
+          __builtin_amdgcn_global_load_lds((const void*)(tc.K + base * D + dma_off[pp]), \
+              (__attribute__((address_space(3))) void*)((KD) + piece * 1024), 16, 0, 0); \
+          __builtin_amdgcn_global_load_lds((const void*)(tc.V + base * D + dma_off[pp]), \
+              (__attribute__((address_space(3))) void*)((VD) + piece * 1024), 16, 0, 0); \
+        }                                                                        \
+      }
+      ISA_DMA_TILE(0, k_lds[0], v_lds[0])
+      if (P > 1) { ISA_DMA_TILE(1, k_ld1, v_ld1) }
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies landed
       __syncthreads();
       float4_t scur[QT][4], snext[QT][4];
       qk_tile<D, QT>(k_lds[0], qf, scur, g, c16);
       float mx[QT];
       row_max<QT>(scur, cscale, mx);
-      int vb_cur = 0, vb_load = 2;   // t % 3 and (t + 2) % 3
-      for (int t = 0; t < P; ++t) {
-        __syncthreads();
-        const bool more2 = t + 2 < P;
-        if (more2) { ISA_LOAD_PLAIN(t + 2) }
-        rescale<D, QT>(mx, m, lsum, oacc);
-        // matrix cores: scores of tile t+1 (stale data on the last tile,
-        // unused); vector ALUs meanwhile: probabilities of tile t. The group
-        // barriers interleave them: per step two MFMAs, six VALU ops and one
-        // K read issued two steps ahead of its use.
-        qk_tile<D, QT>(k_lds[(t + 1) & 1], qf, snext, g, c16);
-        exp_pack<QT>(scur, cscale, m, lsum, pb);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two K reads ahead
-#pragma unroll
-        for (int i = 0; i < 14; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-        }
-        // matrix cores: O += V P of tile t; vector ALUs: row max of tile t+1.
-        pv_tile<D, QT>(v_lds[vb_cur], pb, oacc, g, c16);
-        row_max<QT>(snext, cscale, mx);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);   // two V operands ahead
-#pragma unroll
-        for (int i = 0; i < 14; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
-        }
-        if (more2) { ISA_STORE_PLAIN(t & 1, vb_load) }
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) scur[qt][mt] = snext[qt][mt];
-        vb_cur = vb_cur == 2 ? 0 : vb_cur + 1;
-        vb_load = vb_load == 2 ? 0 : vb_load + 1;
+      // One step: scores of tile t+1 from KC, probabilities of tile t, O += V P
+      // with VC; tile t+2 copied into (KD, VD).
+#define ISA_STEP(t, KC, VC, KD, VD)                                              \
+      {                                                                          \
+        __syncthreads();                                                         \
+        const bool more2 = (t) + 2 < P;                                          \
+        if (more2) { ISA_DMA_TILE((t) + 2, KD, VD) }                             \
+        rescale<D, QT>(mx, m, lsum, oacc);                                       \
+        qk_tile<D, QT>(KC, qf, snext, g, c16);                                   \
+        exp_pack<QT>(scur, cscale, m, lsum, pb);                                 \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                       \
+        _Pragma("unroll") for (int i = 0; i < 14; ++i) {                         \
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                     \
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                     \
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                     \
+        }                                                                        \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i) {                          \
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                     \
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                     \
+        }                                                                        \
+        pv_tile<D, QT>(VC, pb, oacc, g, c16);                                    \
+        row_max<QT>(snext, cscale, mx);                                          \
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);                       \
+        _Pragma("unroll") for (int i = 0; i < 14; ++i) {                         \
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);                     \
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);                     \
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);                     \
+        }                                                                        \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i) {                          \
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);                     \
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);                     \
+        }                                                                        \
+        if (more2) __builtin_amdgcn_s_waitcnt(0x0F70);                           \
+        _Pragma("unroll") for (int qt = 0; qt < QT; ++qt)                        \
+          _Pragma("unroll") for (int mt = 0; mt < 4; ++mt) scur[qt][mt] = snext[qt][mt]; \
       }
+      for (int t = 0; t < P; t += 3) {
+        ISA_STEP(t, k_ld1, v_lds[0], k_ld2, v_ld2)
+        if (t + 1 >= P) break;
+        ISA_STEP(t + 1, k_ld2, v_ld1, k_lds[0], v_lds[0])
+        if (t + 2 >= P) break;
+        ISA_STEP(t + 2, k_lds[0], v_ld2, k_ld1, v_ld1)
+      }
+#undef ISA_STEP
+#undef ISA_DMA_TILE
       __syncthreads();
     }
     // Tail: the few tiles with padding or partial blocks, one at a time.
