@@ -30,6 +30,10 @@
 //     rows of pruned blocks;
 //   * dkv_pooled_kernel (key-major over the pooled keys): per 64 positions of
 //     J, over every flat block; writes dKc, dVc (fp32).
+// The sharp dq_kernel and dkv_pc_kernel stage their streamed operands (key
+// tiles, query blocks) with global_load_lds_dwordx4 straight into LDS buffers
+// that are separate arrays, one step ahead; rows past a block's valid tokens
+// copy real rows and are masked by a -inf logit offset or a +inf log-sum-exp.
 // With decoupled RoPE the gradients of the rotated Q and K are turned back by
 // the transposed rotation in the epilogues.
 #include <initializer_list>
@@ -698,11 +702,16 @@ void dq_kernel(BwdArgs a) {
   constexpr int RW = NWAVES / KS;     // waves per key half
   constexpr int ROWS = RW * ROWS_W;
   constexpr int MTW = 4 / KS;         // 16-key sub-tiles per wave and tile
-  constexpr int NB = PIPE ? 2 : 1;
   static_assert(CH >= 1 && NT % CPR == 0, "tile split");
-  __shared__ __attribute__((aligned(16))) char k_lds[NB][kKeyTile * STR];
-  __shared__ __attribute__((aligned(16))) char v_lds[NB][kKeyTile * STR];
-  __shared__ __attribute__((aligned(16))) float bias_lds[NB][kKeyTile];
+  // Buffer 0 of K, V and the logit offsets; the pipelined form adds buffer 1
+  // as separate arrays, so that the compiler can tell the asynchronous
+  // global->LDS copies into one buffer apart from the reads of the other.
+  __shared__ __attribute__((aligned(16))) char k_lds[1][kKeyTile * STR];
+  __shared__ __attribute__((aligned(16))) char v_lds[1][kKeyTile * STR];
+  __shared__ __attribute__((aligned(16))) float bias_lds[1][kKeyTile];
+  __shared__ __attribute__((aligned(16))) char k_ld1[PIPE ? kKeyTile * STR : 16];
+  __shared__ __attribute__((aligned(16))) char v_ld1[PIPE ? kKeyTile * STR : 16];
+  __shared__ __attribute__((aligned(16))) float bias_ld1[PIPE ? kKeyTile : 4];
   extern __shared__ int tabs[];   // sharp: [N_kv]; flat: [k_ns] then [N_kv]
 
   const IsaShape& s = a.s;
@@ -828,22 +837,22 @@ void dq_kernel(BwdArgs a) {
       vr[i] = *reinterpret_cast<const uint4*>(vp + c8 * 8);
     }
   };
-  auto put = [&](int buf) {
+  auto put = [&]() {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int slot = (tid + i * NT) / CPR;
       const uint32_t m = vm[i];
-      *reinterpret_cast<uint4*>(&k_lds[buf][slot * STR + c8 * 16]) =
+      *reinterpret_cast<uint4*>(&k_lds[0][slot * STR + c8 * 16]) =
           make_uint4(kr[i].x & m, kr[i].y & m, kr[i].z & m, kr[i].w & m);
-      *reinterpret_cast<uint4*>(&v_lds[buf][slot * STR + c8 * 16]) =
+      *reinterpret_cast<uint4*>(&v_lds[0][slot * STR + c8 * 16]) =
           make_uint4(vr[i].x & m, vr[i].y & m, vr[i].z & m, vr[i].w & m);
-      if (c8 == 0) bias_lds[buf][slot] = br[i];
+      if (c8 == 0) bias_lds[0][slot] = br[i];
     }
   };
-  auto consume = [&](int buf) {
-    const char* kb = k_lds[buf] + kh * 16 * MTW * STR;   // this wave's keys
-    const char* vb = v_lds[buf] + kh * 16 * MTW * STR;
-    const float* bb = bias_lds[buf] + kh * 16 * MTW;
+  auto consume = [&](const char* kbuf, const char* vbuf, const float* bbuf) {
+    const char* kb = kbuf + kh * 16 * MTW * STR;   // this wave's keys
+    const char* vb = vbuf + kh * 16 * MTW * STR;
+    const float* bb = bbuf + kh * 16 * MTW;
     float4_t sc[QT][MTW], dp[QT][MTW];
     mm_rows<D, MTW, QT>(kb, qf, sc, g, c16);
     // the probabilities need only S: the vector ALUs form them while the
@@ -875,24 +884,78 @@ void dq_kernel(BwdArgs a) {
     mm_tr<D, MTW, QT>(kb, pk, dq, g, c16);
   };
 
-  if (PIPE) {
-    fetch(0);
-    put(0);
+  if constexpr (PIPE) {
+    // K and V go global -> LDS directly (global_load_lds_dwordx4), one tile
+    // ahead. Wave w copies the 1 KiB pieces w, w + NWAVES, ... of each padded
+    // tile; lane l of a piece holds its bytes 16 l .. 16 l + 15, i.e. chunk
+    // (x % STR) / 16 of key slot x / STR (padding chunks copy data that is
+    // never read). A piece lies within one listed block (block starts fall
+    // on 1 KiB boundaries for b = 32, 64); a slot past the block's n tokens
+    // copies the block's first row and gets logit offset -inf, so it adds
+    // exactly zero. Each wave waits for its own copies before the barrier
+    // that ends the step.
+    static_assert(MODE == kSharp, "pipelined dQ is the sharp path");
+    constexpr int KTB = kKeyTile * STR;
+    constexpr int NPC = KTB / 1024;
+    constexpr int NPW = (NPC + NWAVES - 1) / NWAVES;
+    static_assert(KTB % 1024 == 0, "tile must be whole 1 KiB pieces");
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int poff[NPW], pslot[NPW];
+#pragma unroll
+    for (int pp = 0; pp < NPW; ++pp) {
+      const int x = (pp * NWAVES + wave_u) * 1024 + 16 * lane;
+      const int row = x / STR, col = x - row * STR;
+      pslot[pp] = row;
+      poff[pp] = col < 2 * D ? col / 2 : 0;
+    }
+    auto dma = [&](int t, char* kd, char* vd, float* bd) {
+#pragma unroll
+      for (int pp = 0; pp < NPW; ++pp) {
+        const int piece = pp * NWAVES + wave_u;
+        if (piece < NPC) {
+          const int q = t * per + (((piece * 1024) / STR) >> lb);
+          const int e = __builtin_amdgcn_readfirstlane(q < ntab ? jtab[q] : 0);
+          const int o = pslot[pp] & (b - 1);
+          const size_t row = (size_t)((e >> 7) + (o < (e & 127) ? o : 0));
+          __builtin_amdgcn_global_load_lds((const void*)(Kh + row * D + poff[pp]),
+                                           (__attribute__((address_space(3))) void*)(kd + piece * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)(Vh + row * D + poff[pp]),
+                                           (__attribute__((address_space(3))) void*)(vd + piece * 1024), 16, 0, 0);
+        }
+      }
+      if (tid < kKeyTile) {
+        const int q = t * per + (tid >> lb), o = tid & (b - 1);
+        const int e = q < ntab ? jtab[q] : 0;
+        bd[tid] = o < (e & 127) ? 0.0f : -INFINITY;
+      }
+    };
+    dma(0, k_lds[0], v_lds[0], bias_lds[0]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies landed
     __syncthreads();
-    for (int t = 0; t < a.ntiles; ++t) {
-      const bool more = t + 1 < a.ntiles;
-      if (more) fetch(t + 1);
-      consume(t & 1);
-      if (more) put((t + 1) & 1);
-      __syncthreads();
+    for (int t = 0; t < a.ntiles; t += 2) {
+      {
+        const bool more = t + 1 < a.ntiles;
+        if (more) dma(t + 1, k_ld1, v_ld1, bias_ld1);
+        consume(k_lds[0], v_lds[0], bias_lds[0]);
+        if (more) __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (!more) break;
+      }
+      {
+        const bool more = t + 2 < a.ntiles;
+        if (more) dma(t + 2, k_lds[0], v_lds[0], bias_lds[0]);
+        consume(k_ld1, v_ld1, bias_ld1);
+        if (more) __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+      }
     }
   } else {
     for (int t = 0; t < a.ntiles; ++t) {
       fetch(t);
       if (t > 0) __syncthreads();
-      put(0);
+      put();
       __syncthreads();
-      consume(0);
+      consume(k_lds[0], v_lds[0], bias_lds[0]);
     }
   }
   if constexpr (KS == 2) {
@@ -941,10 +1004,11 @@ void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-// The key-major kernels stream query blocks (b token rows of Q and dO, with
+// The pooled-key kernel streams query blocks (b token rows of Q and dO, with
 // the rows' log-sum-exp and Delta) through two LDS buffers: the next block is
 // fetched into registers while the current one is used. Rows past a block's
 // n valid tokens are zero with log-sum-exp +inf, so they get probability 0.
+// (The exact-key kernel below copies its query blocks straight into LDS.)
 template <int D, int NT, int BR>
 struct QueryStage {
   static constexpr int STR = 2 * D + 32;
@@ -1033,7 +1097,8 @@ __device__ __forceinline__ void kv_block(const char* q_lds, const char* d_lds, c
 // and dK^T += Q^T dS. Each operand read from LDS feeds two matrix-core
 // products (32 keys per wave) while both roles stay within 256 registers, so
 // two waves share each SIMD. Query blocks stream through three LDS buffers
-// (the producer's, the consumer's and the one being filled).
+// (the producer's, the consumer's and the one being filled), copied there
+// with global_load_lds_dwordx4 while the other two are in use.
 template <int D, int BR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void dkv_pc_kernel(BwdArgs a) {
@@ -1046,8 +1111,15 @@ void dkv_pc_kernel(BwdArgs a) {
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;
   constexpr int PX = NF * MT * 2;          // packed bf16 pairs of P per lane
-  __shared__ __attribute__((aligned(16))) char q_lds[3][BR * STR];
-  __shared__ __attribute__((aligned(16))) char d_lds[3][BR * STR];
+  // The three query-block buffers of Q and of dO are separate arrays, so
+  // that the compiler can tell the asynchronous global->LDS copies into one
+  // buffer apart from the reads of the others.
+  __shared__ __attribute__((aligned(16))) char q_l0[BR * STR];
+  __shared__ __attribute__((aligned(16))) char q_l1[BR * STR];
+  __shared__ __attribute__((aligned(16))) char q_l2[BR * STR];
+  __shared__ __attribute__((aligned(16))) char d_l0[BR * STR];
+  __shared__ __attribute__((aligned(16))) char d_l1[BR * STR];
+  __shared__ __attribute__((aligned(16))) char d_l2[BR * STR];
   __shared__ __attribute__((aligned(16))) float l_lds[3][BR];
   __shared__ __attribute__((aligned(16))) float dl_lds[3][BR];
   __shared__ uint32_t pex[2][4][PX][64];
@@ -1133,19 +1205,80 @@ void dkv_pc_kernel(BwdArgs a) {
     for (int dt = 0; dt < DT; ++dt) acc[nf][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   if (total > 0) {
-    QueryStage<D, NT, BR> stage;
+    // Query blocks go global -> LDS directly (global_load_lds_dwordx4) one
+    // block ahead. Wave w copies the 1 KiB pieces w, w + 8, ... of the padded
+    // Q block and pieces 7 - w, 15 - w, ... of the dO block; lane l of a piece
+    // holds its bytes 16 l .. 16 l + 15, i.e. chunk (x % STR) / 16 of row
+    // x / STR (padding chunks copy data that is never read). Rows past the
+    // block's n tokens copy its first row and get log-sum-exp +inf, so their
+    // probabilities, and every product they feed, are exactly zero. Each
+    // wave waits for its own copies before the barrier that ends the step.
+    constexpr int QTB = BR * STR;
+    constexpr int NPC = QTB / 1024;
+    constexpr int NPW = (NPC + 7) / 8;
+    static_assert(QTB % 1024 == 0 && NT == 512, "query block must be whole 1 KiB pieces");
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int qrow[NPW], qoff[NPW], drow[NPW], doff[NPW];
+#pragma unroll
+    for (int pp = 0; pp < NPW; ++pp) {
+      {
+        const int x = (pp * 8 + wave_u) * 1024 + 16 * lane;
+        qrow[pp] = x / STR;
+        const int col = x - qrow[pp] * STR;
+        qoff[pp] = col < 2 * D ? col / 2 : 0;
+      }
+      {
+        const int x = (pp * 8 + 7 - wave_u) * 1024 + 16 * lane;
+        drow[pp] = x / STR;
+        const int col = x - drow[pp] * STR;
+        doff[pp] = col < 2 * D ? col / 2 : 0;
+      }
+    }
+    float lv = INFINITY, dv = 0.0f;
+    auto fetch = [&](int jq, char* qd, char* dd) {
+      int st, n;
+      isa_block_range_checked(s, jq, st, n);
+#pragma unroll
+      for (int pp = 0; pp < NPW; ++pp) {
+        const int pq = pp * 8 + wave_u, pd = pp * 8 + 7 - wave_u;
+        if (pq < NPC) {
+          const size_t r = head + st + (qrow[pp] < n ? qrow[pp] : 0);
+          __builtin_amdgcn_global_load_lds((const void*)(a.Q + r * D + qoff[pp]),
+                                           (__attribute__((address_space(3))) void*)(qd + pq * 1024), 16, 0, 0);
+        }
+        if (pd < NPC) {
+          const size_t r = head + st + (drow[pp] < n ? drow[pp] : 0);
+          __builtin_amdgcn_global_load_lds((const void*)(a.dO + r * D + doff[pp]),
+                                           (__attribute__((address_space(3))) void*)(dd + pd * 1024), 16, 0, 0);
+        }
+      }
+      lv = INFINITY;
+      dv = 0.0f;
+      if (tid < BR && tid < n) {
+        lv = a.lse[head + st + tid];
+        dv = a.delta[head + st + tid];
+      }
+    };
+    auto put_stats = [&](int buf) {
+      if (tid < BR) {
+        l_lds[buf][tid] = lv;
+        dl_lds[buf][tid] = -dv;   // stored negated: the dP sums start from it
+      }
+    };
     int act_cur;
-    stage.fetch(a, head, query_at(0, act_cur), tid);
-    stage.put(q_lds[0], d_lds[0], l_lds[0], dl_lds[0], tid);
+    fetch(query_at(0, act_cur), q_l0, d_l0);
+    put_stats(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies landed
     __syncthreads();
-    for (int i = 0; i <= total; ++i) {
-      int cur = i % 3, prev = (i + 2) % 3, next = (i + 1) % 3, par = i & 1;
-      // opaque buffer indices: one base per buffer and iteration, the rest as
-      // immediate offsets
+    // One step i: producer on buffer cur (i % 3), consumer on prev
+    // ((i + 2) % 3), next block copied into next ((i + 1) % 3).
+    auto step = [&](int i, int cur, int prev, int next, const char* QC, const char* DC, const char* QP,
+                    const char* DP, char* QN, char* DN) __attribute__((always_inline)) {
+      int par = i & 1;
       asm volatile("" : "+s"(cur), "+s"(prev), "+s"(next), "+s"(par));
       int act_next = -1;
       const bool more = i + 1 < total;
-      if (more) stage.fetch(a, head, query_at(i + 1, act_next), tid);
+      if (more) fetch(query_at(i + 1, act_next), QN, DN);
       if (producer) {
         if (i < total) {
           float kbias[NF];
@@ -1153,7 +1286,7 @@ void dkv_pc_kernel(BwdArgs a) {
           for (int nf = 0; nf < NF; ++nf)
             kbias[nf] = (kval[nf] && (act_cur < 0 || act_cur == kb[nf])) ? 0.0f : -INFINITY;
           float4_t sc[NF][MT];
-          mm_rows<D, MT, NF>(q_lds[cur], fr, sc, g, c16);
+          mm_rows<D, MT, NF>(QC, fr, sc, g, c16);
           ahead<KK * MT, NF, 1, kDkvAhead, 1>();
           bool open = act_cur < 0;   // no key of this wave masked (sharp blocks, full kept blocks)
 #pragma unroll
@@ -1195,13 +1328,13 @@ void dkv_pc_kernel(BwdArgs a) {
               px[(2 * nf * MT + 4 * kc + 2) * 64] = w.z;
               px[(2 * nf * MT + 4 * kc + 3) * 64] = w.w;
             }
-          mm_tr<D, MT, NF>(d_lds[cur], pp, acc, g, c16);
+          mm_tr<D, MT, NF>(DC, pp, acc, g, c16);
           ahead<DT * (MT / 2), NF, 2, kDkvAhead, 2>();
         }
       } else if (i > 0) {
         // dP - Delta: the sums start from -Delta of each row
         float4_t dp[NF][MT];
-        mm_rows_from<D, MT, NF>(d_lds[prev], fr, dp, dl_lds[prev], g, c16);
+        mm_rows_from<D, MT, NF>(DP, fr, dp, dl_lds[prev], g, c16);
         ahead<KK * MT, NF, 1, kDkvAhead, 3>();
         const uint32_t* px = &pex[par ^ 1][pair][0][lane];
 #pragma unroll
@@ -1217,12 +1350,22 @@ void dkv_pc_kernel(BwdArgs a) {
         }
         bf16x8_t pd[NF][MT / 2];
         pack_bf16<MT, NF>(dp, pd);
-        mm_tr<D, MT, NF>(q_lds[prev], pd, acc, g, c16);
+        mm_tr<D, MT, NF>(QP, pd, acc, g, c16);
         ahead<DT * (MT / 2), NF, 2, kDkvAhead, 4>();
       }
-      if (more) stage.put(q_lds[next], d_lds[next], l_lds[next], dl_lds[next], tid);
+      if (more) {
+        put_stats(next);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
       __syncthreads();
       act_cur = act_next;
+    };
+    for (int i = 0; i <= total; i += 3) {
+      step(i, 0, 2, 1, q_l0, d_l0, q_l2, d_l2, q_l1, d_l1);
+      if (i + 1 > total) break;
+      step(i + 1, 1, 0, 2, q_l1, d_l1, q_l0, d_l0, q_l2, d_l2);
+      if (i + 2 > total) break;
+      step(i + 2, 2, 1, 0, q_l2, d_l2, q_l1, d_l1, q_l0, d_l0);
     }
   }
 
