@@ -129,7 +129,7 @@ def compare_head(plan, Qv, Kv, Vv, gpu, rows=None, oracle_result=None):
 # started fresh (spawn: no GPU state is inherited, and workers import numpy
 # and the oracle only). Each worker regenerates its head from the seeded
 # generator, so only the GPU's results travel to it.
-ORACLE_WORKERS = 4          # x ORACLE_THREADS BLAS threads: the 16 cores of a one-GPU machine
+ORACLE_WORKERS = 4          # x ORACLE_THREADS BLAS threads: 16 host cores
 ORACLE_THREADS = 4
 
 

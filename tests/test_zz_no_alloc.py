@@ -39,7 +39,10 @@ def test_noalloc_forward_matches_forward():
     dev = torch.device("cuda:0")
     isa.init()
     cases = [
-        # a large call first, then smaller ones that reuse the same scratch
+        # a large call first, then smaller ones that reuse the same scratch;
+        # the first has N_kv = 656 > 640, so its exact sets go through the
+        # exact-set selection's row scratch in the static array as well
+        isa.Params(1, 1, 40960, 8192, 128, 64),
         isa.Params(1, 8, 8192, 8192, 128, 64),
         isa.Params(1, 2, 700, 451, 64, 32, 0.25, 0.5, 0.125, gamma=0.5),
         isa.Params(2, 3, 333, 290, 128, 64, 0.5, 0.25, 0.25, rope_base=10000.0),
