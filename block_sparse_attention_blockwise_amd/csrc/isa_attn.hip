@@ -343,8 +343,9 @@ __device__ __forceinline__ void pv_tile(const char* vb, const bf16x8_t (&pb)[QT]
 }
 
 // PIPE: software pipelined (scores of the next tile overlap the softmax of
-// the current one; K double-, V triple-buffered), else one LDS buffer per
-// tile with the latency hidden by the other resident workgroups.
+// the current one; K and V triple-buffered, copied global->LDS directly),
+// else one LDS buffer per tile with the latency hidden by the other
+// resident workgroups.
 // KS = 2 (flat path only): the waves split each key tile in two halves of 32
 // keys, each half with its own online-softmax state for the same rows, merged
 // at the end; twice the waves per workgroup for the same LDS.
