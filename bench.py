@@ -382,29 +382,45 @@ def torch_sdpa_ms(torch, Q, K, V, reps):
 
 def measured_peaks(torch, dev):
     """Achievable peaks on this device: bf16 matrix-core rate from the probe
-    kernel (independent MFMA chains, no memory traffic), HBM read bandwidth
-    of a streaming 16-byte-load kernel over 2 GiB, HBM bandwidth of a
-    2 GiB device-to-device copy (read + write bytes), and the LDS read rate
-    of the attention kernels' two operand patterns (16-byte row reads and
-    8-byte transposed reads, 2048 workgroups of 256 threads)."""
+    kernel (independent MFMA chains, no memory traffic) on random operands
+    (as the attention products see) and on constant low-activity operands,
+    with the shader clock each held (the matrix cores' power, so the clock,
+    depends on the operand bits); HBM read bandwidth of a streaming
+    16-byte-load kernel over 2 GiB, HBM bandwidth of a 2 GiB
+    device-to-device copy (read + write bytes), and the LDS read rate of the
+    attention kernels' two operand patterns (16-byte row reads and 8-byte
+    transposed reads, 2048 workgroups of 256 threads)."""
     from block_sparse_attention_blockwise_amd import _build
     probe = ctypes.CDLL(_build.PROBE_PATH)
-    probe.isa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe.isa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]
     probe.isa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     probe.isa_probe_mfma_flops.restype = ctypes.c_double
-    blocks, iters = 4096, 1024
+    probe.isa_probe_wallclock_khz.restype = ctypes.c_int
+    blocks, iters = 4096, 512   # about 4.5 ms per launch at 2 PFLOP/s
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clk = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
     sp = torch.cuda.current_stream(dev).cuda_stream
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    rc = probe.isa_probe_mfma_bf16(blocks, iters, out.data_ptr(), sp)
-    if rc != 0:
-        raise RuntimeError(f"probe launch failed: {rc}")
-    e0.record()
-    for _ in range(3):
-        probe.isa_probe_mfma_bf16(blocks, iters, out.data_ptr(), sp)
-    e1.record()
-    torch.cuda.synchronize()
-    mfma_tflops = 3 * probe.isa_probe_mfma_flops(blocks, iters) / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    wall_khz = probe.isa_probe_wallclock_khz()
+    mfma = {}
+    for mode, name in ((1, "mfma_bf16"), (0, "mfma_bf16_low_activity")):
+        rc = probe.isa_probe_mfma_bf16(blocks, iters, mode, out.data_ptr(), None, sp)
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed: {rc}")
+        for _ in range(40):   # let the clock settle under this load (about 0.2 s)
+            probe.isa_probe_mfma_bf16(blocks, iters, mode, out.data_ptr(), None, sp)
+        e0.record()
+        for _ in range(3):
+            probe.isa_probe_mfma_bf16(blocks, iters, mode, out.data_ptr(), clk.data_ptr(), sp)
+        e1.record()
+        torch.cuda.synchronize()
+        mfma[name + "_tflops"] = 3 * probe.isa_probe_mfma_flops(blocks, iters) / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        ticks = clk.view(-1, 2).double().cpu()
+        ok = ticks[:, 1] > 0
+        mfma[name + "_clock_ghz"] = (float((ticks[ok, 0] / ticks[ok, 1]).median()) * wall_khz * 1e-6
+                                     if wall_khz > 0 and bool(ok.any()) else None)
+    del clk
     n = 1 << 30   # 2^30 bf16 = 2 GiB
     src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
@@ -446,7 +462,7 @@ def measured_peaks(torch, dev):
         torch.cuda.synchronize()
         lds[name] = 3 * probe.isa_probe_lds_bytes(lblocks, liters, mode) / (e0.elapsed_time(e1) * 1e-3) / 1e12
     del lout
-    return {"mfma_bf16_tflops": mfma_tflops, "hbm_read_gbs": hbm_read, "hbm_copy_gbs": hbm_copy, **lds}
+    return {**mfma, "hbm_read_gbs": hbm_read, "hbm_copy_gbs": hbm_copy, **lds}
 
 
 def sweep_128k(isa, torch, dev, args):

@@ -1,7 +1,8 @@
 // Achievable-peak probes for the measurement harness (not part of the ISA
 // operator): a kernel that keeps the bf16 matrix cores busy with
 // independent v_mfma_f32_16x16x32_bf16 chains and touches no memory in its
-// loop (its rate is the matrix-core throughput the chip sustains), and a
+// loop (its rate is the matrix-core throughput the chip sustains, which
+// depends on the operand data through the clock), and a
 // kernel that streams a large buffer from HBM with 16-byte loads (the read
 // bandwidth it sustains), and a kernel that reads LDS tiles with the access
 // patterns of the attention kernels' operand reads (the LDS read rate).
@@ -17,29 +18,63 @@ typedef float float4_t __attribute__((__vector_size__(16)));
 typedef short short4_t __attribute__((__vector_size__(8)));
 
 constexpr int kChains = 8;   // independent accumulators per wave (hide the MFMA latency)
+constexpr int kMfmaPerIter = 64;   // kChains chains x 8 operand pairs
 
-__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* out) {
+__device__ inline uint32_t mix32(uint32_t x) {
+  x ^= x >> 16; x *= 0x7feb352dU; x ^= x >> 15; x *= 0x846ca68bU; x ^= x >> 16;
+  return x;
+}
+
+// The matrix cores' power, and with it the clock the chip holds, depends on
+// the operand bits. mode 0: every product takes the same two operands made of
+// a few small values (little bit activity); mode 1: each wave holds eight A
+// and eight B operands of uniform random bf16 values in (-1, 1) and each of
+// the 64 products of an iteration takes a different (A, B) pair, as the
+// attention kernels' products do. When `clk` is not null, thread 0 of every
+// workgroup stores the shader-clock and constant-rate (wall clock) ticks that
+// elapsed over the workgroup (two 64-bit words).
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, int mode, float* out,
+                                                         unsigned long long* clk) {
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime(), w0 = __builtin_amdgcn_s_memrealtime();
   const int t = threadIdx.x;
-  bf16x8_t a, b;
+  const uint32_t gt = (uint32_t)blockIdx.x * 256u + (uint32_t)t;
+  bf16x8_t a[8], b[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(0.001f * (float)((t + i) & 7));
-    b[i] = (__bf16)(0.002f * (float)((t * 3 + i) & 7));
-  }
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float va, vb;
+      if (mode == 0) {
+        va = 0.001f * (float)((t + i) & 7);
+        vb = 0.002f * (float)((t * 3 + i) & 7);
+      } else {
+        va = (float)(mix32(gt * 131u + k * 17u + i) >> 8) * (2.0f / 16777216.0f) - 1.0f;
+        vb = (float)(mix32(gt * 977u + k * 29u + i + 7777u) >> 8) * (2.0f / 16777216.0f) - 1.0f;
+      }
+      a[k][i] = (__bf16)va;
+      b[k][i] = (__bf16)vb;
+    }
   float4_t c[kChains];
 #pragma unroll
   for (int k = 0; k < kChains; ++k) c[k] = float4_t{0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < iters; ++i) {
+  for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int k = 0; k < kChains; ++k)
-      // accumulate in place: the builtin form made the compiler rotate the
-      // accumulators through register copies on every iteration
-      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c[k]) : "v"(a), "v"(b));
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int k = 0; k < kChains; ++k)
+        // accumulate in place: the builtin form made the compiler rotate the
+        // accumulators through register copies on every iteration
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c[k]) : "v"(a[(k + j) & 7]), "v"(b[k]));
   }
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < kChains; ++k) s += c[k][0] + c[k][1] + c[k][2] + c[k][3];
   out[(size_t)blockIdx.x * blockDim.x + t] = s;
+  if (clk != nullptr && t == 0) {
+    const unsigned long long c1 = __builtin_amdgcn_s_memtime(), w1 = __builtin_amdgcn_s_memrealtime();
+    clk[2 * (size_t)blockIdx.x] = c1 - c0;
+    clk[2 * (size_t)blockIdx.x + 1] = w1 - w0;
+  }
 }
 
 // Streams `n16` 16-byte chunks with one load per chunk (grid-stride), adds
@@ -112,17 +147,29 @@ PROBE_API int isa_probe_read(const void* src, size_t bytes, int blocks, float* o
 }
 
 // Launches `blocks` workgroups of 256 threads, each wave issuing
-// iters * 8 MFMAs of 16x16x32 (16384 flops each); `out` must hold
-// blocks * 256 floats. Returns 0 or the HIP error code.
-PROBE_API int isa_probe_mfma_bf16(int blocks, int iters, float* out, void* stream) {
-  if (blocks < 1 || iters < 1 || !out) return -1;
-  mfma_probe_kernel<<<blocks, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(iters, out);
+// iters * 64 MFMAs of 16x16x32 (16384 flops each) on operands of the given
+// mode (0: constant low-activity operands, 1: random operands); `out` must
+// hold blocks * 256 floats, `clk` (may be null) 2 * blocks 64-bit words.
+// Returns 0 or the HIP error code (-1 for bad arguments).
+PROBE_API int isa_probe_mfma_bf16(int blocks, int iters, int mode, float* out, unsigned long long* clk,
+                                  void* stream) {
+  if (blocks < 1 || iters < 1 || (mode != 0 && mode != 1) || !out) return -1;
+  mfma_probe_kernel<<<blocks, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(iters, mode, out, clk);
   return (int)hipGetLastError();
 }
 
 // Flops one isa_probe_mfma_bf16 launch performs.
 PROBE_API double isa_probe_mfma_flops(int blocks, int iters) {
-  return (double)blocks * 4.0 * iters * kChains * 16.0 * 16.0 * 32.0 * 2.0;
+  return (double)blocks * 4.0 * iters * kMfmaPerIter * 16.0 * 16.0 * 32.0 * 2.0;
+}
+
+// Rate of the constant-rate clock read by s_memrealtime on the current
+// device, in kHz (0 on error).
+PROBE_API int isa_probe_wallclock_khz() {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+  return khz;
 }
 
 // Launches `blocks` workgroups of 256 threads reading LDS (mode 0: 16-byte
