@@ -34,8 +34,9 @@
 // The sharp and dense paths are software pipelined: while the softmax of
 // tile t runs on the vector ALUs, the matrix cores already compute the scores
 // of tile t+1; K and V are triple buffered in LDS and copied there straight
-// from global memory (global_load_lds_dwordx4: no register staging, no LDS
-// store instructions) two tiles ahead, one workgroup barrier per tile. Tiles
+// from global memory (buffer_load_dwordx4 ... lds: no register staging, no
+// LDS store instructions, no vector address arithmetic) two tiles ahead,
+// one workgroup barrier per tile. Tiles
 // that need additive logits (padding, partial blocks) are ordered last so
 // the steady state runs without them.
 // K and V rows are padded to 2D+32 bytes in LDS; with that stride the 16-byte
@@ -598,7 +599,7 @@ void attn_kernel(AttnArgs a) {
     }
   } else {
     // Steady state: the leading tiles, which carry no additive logits. K
-    // and V go global -> LDS directly (global_load_lds_dwordx4, no register
+    // and V go global -> LDS directly (buffer loads into LDS, no register
     // staging), three buffers each; tile t+2 is copied while tile t is
     // processed and waited for before the barrier that ends the step.
     const int P = a.ntiles_plain;
@@ -614,29 +615,41 @@ void attn_kernel(AttnArgs a) {
       // boundaries for b = 32, 64), so its block start is wave-uniform; the
       // lane's element offset within the block is fixed for every tile.
       const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-      int dma_off[NPW];
+      uint32_t dma_off[NPW];   // byte offset of the lane's chunk from its block start
+      int dma_blk[NPW];        // which of the tile's (at most two) blocks the piece is in
 #pragma unroll
       for (int pp = 0; pp < NPW; ++pp) {
         const int x = (pp * NWAVES + wave_u) * 1024 + 16 * lane;
         const int row = x / KSTR, col = x - row * KSTR;
         const int ce = col < 2 * D ? col / 2 : 0;
-        dma_off[pp] = (MODE == kDense ? row : (row & (b - 1))) * D + ce;
+        dma_off[pp] = (uint32_t)(((MODE == kDense ? row : (row & (b - 1))) * D + ce) * 2);
+        dma_blk[pp] = MODE == kDense ? 0 : ((pp * NWAVES + wave_u) * 1024 / KSTR) >> lb;
       }
+      // The copies are buffer loads into LDS: a buffer resource over this
+      // head's rows (out-of-range reads return zero), the lane's fixed 32-bit
+      // offset and the wave-uniform byte offset of the block, so no address
+      // arithmetic runs on the vector units. Both block entries of a tile
+      // are read before either is used (the second repeats the first for
+      // b = 64).
+      const int head_bytes = (int)((size_t)s.L * D * 2);
+      const RowsRsrc k_rs = rows_rsrc(tc.K, head_bytes);
+      const RowsRsrc v_rs = rows_rsrc(tc.V, head_bytes);
 #define ISA_DMA_TILE(T, KD, VD)                                                  \
-      _Pragma("unroll") for (int pp = 0; pp < NPW; ++pp) {                       \
-        const int piece = pp * NWAVES + wave_u;                                  \
-        if (piece < NPC) {                                                       \
-          size_t base;                                                           \
-          if (MODE == kDense) {                                                  \
-            base = (size_t)(T) * kKeyTile;                                       \
-          } else {                                                               \
-            const int blk = ((piece * 1024) / KSTR) >> lb;                       \
-            base = (size_t)(__builtin_amdgcn_readfirstlane(tc.tab[(T) * tc.per + blk]) >> 7); \
+      {                                                                          \
+        uint32_t base0 = (uint32_t)(T) * kKeyTile, base1 = base0;                \
+        if (MODE != kDense) {                                                    \
+          const int e0 = tc.tab[(T) * tc.per];                                   \
+          const int e1 = tc.tab[(T) * tc.per + tc.per - 1];                      \
+          base0 = (uint32_t)(__builtin_amdgcn_readfirstlane(e0) >> 7);           \
+          base1 = (uint32_t)(__builtin_amdgcn_readfirstlane(e1) >> 7);           \
+        }                                                                        \
+        _Pragma("unroll") for (int pp = 0; pp < NPW; ++pp) {                     \
+          const int piece = pp * NWAVES + wave_u;                                \
+          if (piece < NPC) {                                                     \
+            const int bo = (int)((dma_blk[pp] ? base1 : base0) * (uint32_t)(2 * D)); \
+            copy16_to_lds(k_rs, (KD) + piece * 1024, dma_off[pp], bo);          \
+            copy16_to_lds(v_rs, (VD) + piece * 1024, dma_off[pp], bo);          \
           }                                                                      \
-          __builtin_amdgcn_global_load_lds((const void*)(tc.K + base * D + dma_off[pp]), \
-              (__attribute__((address_space(3))) void*)((KD) + piece * 1024), 16, 0, 0); \
-          __builtin_amdgcn_global_load_lds((const void*)(tc.V + base * D + dma_off[pp]), \
-              (__attribute__((address_space(3))) void*)((VD) + piece * 1024), 16, 0, 0); \
         }                                                                        \
       }
       ISA_DMA_TILE(0, k_lds[0], v_lds[0])

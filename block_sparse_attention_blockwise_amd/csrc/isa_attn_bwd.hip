@@ -31,7 +31,7 @@
 //   * dkv_pooled_kernel (key-major over the pooled keys): per 64 positions of
 //     J, over every flat block; writes dKc, dVc (fp32).
 // The sharp dq_kernel and dkv_pc_kernel stage their streamed operands (key
-// tiles, query blocks) with global_load_lds_dwordx4 straight into LDS buffers
+// tiles, query blocks) with buffer loads straight into LDS buffers
 // that are separate arrays, one step ahead; rows past a block's valid tokens
 // copy real rows and are masked by a -inf logit offset or a +inf log-sum-exp.
 // With decoupled RoPE the gradients of the rotated Q and K are turned back by
@@ -885,7 +885,7 @@ void dq_kernel(BwdArgs a) {
   };
 
   if constexpr (PIPE) {
-    // K and V go global -> LDS directly (global_load_lds_dwordx4), one tile
+    // K and V go global -> LDS directly (buffer loads into LDS), one tile
     // ahead. Wave w copies the 1 KiB pieces w, w + NWAVES, ... of each padded
     // tile; lane l of a piece holds its bytes 16 l .. 16 l + 15, i.e. chunk
     // (x % STR) / 16 of key slot x / STR (padding chunks copy data that is
@@ -908,6 +908,9 @@ void dq_kernel(BwdArgs a) {
       pslot[pp] = row;
       poff[pp] = col < 2 * D ? col / 2 : 0;
     }
+    const int head_bytes = (int)((size_t)s.L * D * 2);
+    const RowsRsrc k_rs = rows_rsrc(Kh, head_bytes);
+    const RowsRsrc v_rs = rows_rsrc(Vh, head_bytes);
     auto dma = [&](int t, char* kd, char* vd, float* bd) {
 #pragma unroll
       for (int pp = 0; pp < NPW; ++pp) {
@@ -916,11 +919,9 @@ void dq_kernel(BwdArgs a) {
           const int q = t * per + (((piece * 1024) / STR) >> lb);
           const int e = __builtin_amdgcn_readfirstlane(q < ntab ? jtab[q] : 0);
           const int o = pslot[pp] & (b - 1);
-          const size_t row = (size_t)((e >> 7) + (o < (e & 127) ? o : 0));
-          __builtin_amdgcn_global_load_lds((const void*)(Kh + row * D + poff[pp]),
-                                           (__attribute__((address_space(3))) void*)(kd + piece * 1024), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((const void*)(Vh + row * D + poff[pp]),
-                                           (__attribute__((address_space(3))) void*)(vd + piece * 1024), 16, 0, 0);
+          const uint32_t lane_off = (uint32_t)(((o < (e & 127) ? o : 0) * D + poff[pp]) * 2);
+          copy16_to_lds(k_rs, kd + piece * 1024, lane_off, (e >> 7) * D * 2);
+          copy16_to_lds(v_rs, vd + piece * 1024, lane_off, (e >> 7) * D * 2);
         }
       }
       if (tid < kKeyTile) {
@@ -1098,7 +1099,7 @@ __device__ __forceinline__ void kv_block(const char* q_lds, const char* d_lds, c
 // products (32 keys per wave) while both roles stay within 256 registers, so
 // two waves share each SIMD. Query blocks stream through three LDS buffers
 // (the producer's, the consumer's and the one being filled), copied there
-// with global_load_lds_dwordx4 while the other two are in use.
+// with buffer loads into LDS while the other two are in use.
 template <int D, int BR>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void dkv_pc_kernel(BwdArgs a) {
@@ -1205,7 +1206,7 @@ void dkv_pc_kernel(BwdArgs a) {
     for (int dt = 0; dt < DT; ++dt) acc[nf][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   if (total > 0) {
-    // Query blocks go global -> LDS directly (global_load_lds_dwordx4) one
+    // Query blocks go global -> LDS directly (buffer loads into LDS) one
     // block ahead. Wave w copies the 1 KiB pieces w, w + 8, ... of the padded
     // Q block and pieces 7 - w, 15 - w, ... of the dO block; lane l of a piece
     // holds its bytes 16 l .. 16 l + 15, i.e. chunk (x % STR) / 16 of row
@@ -1235,22 +1236,21 @@ void dkv_pc_kernel(BwdArgs a) {
       }
     }
     float lv = INFINITY, dv = 0.0f;
+    const int head_bytes = (int)((size_t)s.L * D * 2);
+    const RowsRsrc q_rs = rows_rsrc(a.Q + head * D, head_bytes);
+    const RowsRsrc d_rs = rows_rsrc(a.dO + head * D, head_bytes);
     auto fetch = [&](int jq, char* qd, char* dd) {
       int st, n;
       isa_block_range_checked(s, jq, st, n);
 #pragma unroll
       for (int pp = 0; pp < NPW; ++pp) {
         const int pq = pp * 8 + wave_u, pd = pp * 8 + 7 - wave_u;
-        if (pq < NPC) {
-          const size_t r = head + st + (qrow[pp] < n ? qrow[pp] : 0);
-          __builtin_amdgcn_global_load_lds((const void*)(a.Q + r * D + qoff[pp]),
-                                           (__attribute__((address_space(3))) void*)(qd + pq * 1024), 16, 0, 0);
-        }
-        if (pd < NPC) {
-          const size_t r = head + st + (drow[pp] < n ? drow[pp] : 0);
-          __builtin_amdgcn_global_load_lds((const void*)(a.dO + r * D + doff[pp]),
-                                           (__attribute__((address_space(3))) void*)(dd + pd * 1024), 16, 0, 0);
-        }
+        if (pq < NPC)
+          copy16_to_lds(q_rs, qd + pq * 1024, (uint32_t)(((qrow[pp] < n ? qrow[pp] : 0) * D + qoff[pp]) * 2),
+                        st * D * 2);
+        if (pd < NPC)
+          copy16_to_lds(d_rs, dd + pd * 1024, (uint32_t)(((drow[pp] < n ? drow[pp] : 0) * D + doff[pp]) * 2),
+                        st * D * 2);
       }
       lv = INFINITY;
       dv = 0.0f;

@@ -42,6 +42,44 @@ __host__ __device__ inline void isa_block_range_checked(const IsaShape& s, int j
   isa_block_range(s, j, start, n);
 }
 
+// Buffer loads into LDS (buffer_load_dwordx4 ... lds): a buffer resource over
+// a head's rows in scalar registers, a 32-bit lane offset and a wave-uniform
+// byte offset, with no address arithmetic on the vector units; reads past
+// the resource's size return zero. The resource type exists only in the
+// device compilation; the host pass parses the kernels but never runs them.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t RowsRsrc;
+#else
+struct RowsRsrc { int words[4]; };
+#endif
+
+__device__ inline RowsRsrc rows_rsrc(const void* p, int bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // both halves of the (wave-uniform) base from the first lane, so that the
+  // resource lives in scalar registers
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), 0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+#else
+  (void)p; (void)bytes;
+  return RowsRsrc{};
+#endif
+}
+
+// Copies 16 bytes per lane from `r` at byte offset lane_off + block_off into
+// LDS at `lds` + 16 * lane (`lds` and `block_off` wave-uniform).
+__device__ inline void copy16_to_lds(RowsRsrc r, char* lds, uint32_t lane_off, int block_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, lane_off,
+                                           __builtin_amdgcn_readfirstlane(block_off), 0, 0);
+#else
+  (void)r; (void)lds; (void)lane_off; (void)block_off;
+#endif
+}
+
+
 // Raises a kernel's dynamic-LDS limit on the current device, once per device
 // (the attribute is per device; `done` is a per-kernel bit set of devices).
 inline hipError_t isa_ensure_dyn_lds(const void* kernel, int bytes, unsigned long long* done) {
