@@ -17,8 +17,10 @@
 //   * a workgroup owns ROWS query rows; each wave owns 16*QT rows (for
 //     32-token flat blocks two waves share each row group, one per 32-key
 //     half of every tile, and merge their softmax states at the end);
-//   * key tiles of 64 keys are staged in LDS; global loads of a later tile
-//     are in flight while the current one is consumed;
+//   * key tiles of 64 keys are copied into LDS by buffer loads (no register
+//     staging); in the pipelined paths the copy of a later tile is in flight
+//     while the current one is consumed, in the flat path the other resident
+//     workgroups cover the copy's latency;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q
 //     fragments kept in registers); lane (g = lane/16, c = lane%16) then holds
 //     4 keys of each 16-key sub-tile for query c, so the row max needs only
@@ -164,17 +166,6 @@ __device__ inline SlotSrc slot_src(const TileCtx& c, int t, int slot) {
   r.v = c.V + row;
   r.bias = r.valid ? 0.0f : -INFINITY;
   return r;
-}
-
-// Key row of `slot` in a plain tile (full kept blocks or full dense tiles,
-// no additive logits). Each wave's 16-byte chunks of one tile fall inside
-// one kept block, so the block's start is read once per wave into a scalar
-// register and the row addresses need no per-lane table lookups or masks.
-template <int MODE>
-__device__ inline int plain_row(const TileCtx& c, int t, int slot) {
-  if (MODE == kDense) return t * kKeyTile + slot;
-  const int e = __builtin_amdgcn_readfirstlane(c.tab[t * c.per + (slot >> c.lb)]);
-  return (e >> 7) + (slot & (c.b - 1));
 }
 
 // Whether tile t carries any non-zero additive logit (uniform over the
@@ -345,8 +336,8 @@ __device__ __forceinline__ void pv_tile(const char* vb, const bf16x8_t (&pb)[QT]
 
 // PIPE: software pipelined (scores of the next tile overlap the softmax of
 // the current one; K and V triple-buffered, copied global->LDS directly),
-// else one LDS buffer per tile with the latency hidden by the other
-// resident workgroups.
+// else one LDS buffer, also filled global->LDS directly, with the copy
+// latency hidden by the other resident workgroups.
 // KS = 2 (flat path only): the waves split each key tile in two halves of 32
 // keys, each half with its own online-softmax state for the same rows, merged
 // at the end; twice the waves per workgroup for the same LDS.
@@ -533,18 +524,6 @@ void attn_kernel(AttnArgs a) {
     kr[i] = *reinterpret_cast<const uint4*>(ss.k + c8 * 8);                     \
     vr[i] = *reinterpret_cast<const uint4*>(ss.v + c8 * 8);                     \
   }
-#define ISA_LOAD_PLAIN(T)                                                       \
-  _Pragma("unroll") for (int i = 0; i < CH; ++i) {                              \
-    const size_t row = (size_t)plain_row<MODE>(tc, (T), (tid + i * NT) / CPR);  \
-    kr[i] = *reinterpret_cast<const uint4*>(tc.K + row * D + c8 * 8);           \
-    vr[i] = *reinterpret_cast<const uint4*>(tc.V + row * D + c8 * 8);           \
-  }
-#define ISA_STORE_PLAIN(KB, VB)                                                 \
-  _Pragma("unroll") for (int i = 0; i < CH; ++i) {                              \
-    const int slot = (tid + i * NT) / CPR;                                      \
-    *reinterpret_cast<uint4*>(&k_lds[(KB)][slot * KSTR + c8 * 16]) = kr[i];     \
-    *reinterpret_cast<uint4*>(&v_lds[(VB)][slot * VSTR + c8 * 16]) = vr[i];     \
-  }
 #define ISA_STORE_TILE(KB, VB)                                                  \
   _Pragma("unroll") for (int i = 0; i < CH; ++i) {                              \
     const int slot = (tid + i * NT) / CPR;                                      \
@@ -577,11 +556,58 @@ void attn_kernel(AttnArgs a) {
     const char* kb = k_lds[0] + kh * 16 * NMT * KSTR;
     const char* vb = v_lds[0] + kh * 16 * NMT * VSTR;
     const float* bb = bias_lds[0] + kh * 16 * NMT;
+    // Each tile goes global -> LDS directly with buffer loads (no register
+    // staging): wave w copies the 1 KiB pieces w, w + NWAVES, ... of the
+    // padded K and V tiles, lane l of a piece bytes 16 l .. 16 l + 15 of it,
+    // i.e. row x / KSTR, byte column x % KSTR (padding columns copy the row's
+    // first chunk, never read). A slot that holds no key (past a block's n
+    // tokens, a pooled position inside E_i or outside J) gets an offset past
+    // the end of every resource, so the copy writes zeros.
+    constexpr int KTB = kKeyTile * KSTR;
+    constexpr int NPC = KTB / 1024;
+    constexpr int NPW = (NPC + NWAVES - 1) / NWAVES;
+    static_assert(KTB % 1024 == 0, "tile must be whole 1 KiB pieces");
+    constexpr uint32_t kNoRow = 0x80000000u;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int pslot[NPW];
+    uint32_t pcol[NPW];
+#pragma unroll
+    for (int pp = 0; pp < NPW; ++pp) {
+      const int x = (pp * NWAVES + wave_u) * 1024 + 16 * lane;
+      pslot[pp] = x / KSTR;
+      const int col = x - pslot[pp] * KSTR;
+      pcol[pp] = (uint32_t)(col < 2 * D ? col : 0);
+    }
+    const RowsRsrc k_rs = rows_rsrc(tc.K, (int)((size_t)s.L * D * 2));
+    const RowsRsrc v_rs = rows_rsrc(tc.V, (int)((size_t)s.L * D * 2));
+    const RowsRsrc kc_rs = rows_rsrc(tc.kc, (int)((size_t)s.N * D * 2));
+    const RowsRsrc vc_rs = rows_rsrc(tc.vc, (int)((size_t)s.N * D * 2));
     for (int t = 0; t < ntiles; ++t) {
-      ISA_LOAD_TILE(t)
       const bool hb = tile_has_bias<MODE>(tc, t);
       if (t > 0) __syncthreads();   // previous tile fully consumed
-      ISA_STORE_TILE(0, 0)
+      const bool pooled = t >= tc.ntiles_exact;
+#pragma unroll
+      for (int pp = 0; pp < NPW; ++pp) {
+        const int piece = pp * NWAVES + wave_u;
+        if (piece < NPC) {
+          const int slot = pslot[pp];
+          uint32_t off;
+          if (!pooled) {
+            const int q = t * tc.per + (slot >> tc.lb), o = slot & (tc.b - 1);
+            const int e = q < tc.ntab ? tc.tab[q] : 0;
+            off = o < (e & 127) ? (uint32_t)(((e >> 7) + o) * D * 2) + pcol[pp] : kNoRow;
+          } else {
+            const int p = (t - tc.ntiles_exact) * kKeyTile + slot;
+            const int e = p < tc.N_kv ? tc.ptab[p] : 1;
+            const bool valid = !(e & 1) && ((e >> 1) & 127) > 0;
+            off = valid ? (uint32_t)((e >> 8) * D * 2) + pcol[pp] : kNoRow;
+          }
+          copy16_to_lds(pooled ? kc_rs : k_rs, k_lds[0] + piece * 1024, off, 0);
+          copy16_to_lds(pooled ? vc_rs : v_rs, v_lds[0] + piece * 1024, off, 0);
+        }
+      }
+      if (tid < kKeyTile) bias_lds[0][tid] = slot_src<D, MODE>(tc, t, tid).bias;
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies landed
       __syncthreads();
       float4_t sc[QT][NMT];
       bf16x8_t pk[QT][NMT / 2];
@@ -725,8 +751,6 @@ void attn_kernel(AttnArgs a) {
   }
 #undef ISA_LOAD_TILE
 #undef ISA_STORE_TILE
-#undef ISA_LOAD_PLAIN
-#undef ISA_STORE_PLAIN
 
   float ltot[QT];   // softmax denominator of each owned row
 #pragma unroll

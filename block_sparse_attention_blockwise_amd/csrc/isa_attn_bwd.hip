@@ -795,7 +795,6 @@ void dq_kernel(BwdArgs a) {
   const uint16_t* Vh = a.V + head * D;
   const uint16_t* kch = MODE == kFlat ? a.kcb + (size_t)bh * s.N * D : nullptr;
   const uint16_t* vch = MODE == kFlat ? a.vcb + (size_t)bh * s.N * D : nullptr;
-  const int c8 = tid % CPR;
   const float cscale = kLog2e / sqrtf((float)D);
   float4_t dq[QT][DT];
 #pragma unroll
@@ -803,52 +802,6 @@ void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) dq[qt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 kr[CH], vr[CH];
-  float br[CH];
-  uint32_t vm[CH];
-  auto fetch = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int slot = (tid + i * NT) / CPR;
-      const uint16_t *kp, *vp;
-      bool valid;
-      float bias;
-      if (MODE == kFlat && t >= a.ntiles_exact) {
-        const int p = (t - a.ntiles_exact) * kKeyTile + slot;
-        const int e = p < s.N_kv ? ptab[p] : 1;
-        const int n = (e >> 1) & 127;
-        valid = !(e & 1) && n > 0;
-        const size_t row = (size_t)(valid ? (e >> 8) : 0) * D;
-        kp = kch + row;
-        vp = vch + row;
-        bias = valid ? __log2f((float)n) : -INFINITY;
-      } else {
-        const int q = t * per + (slot >> lb), o = slot & (b - 1);
-        const int e = q < ntab ? jtab[q] : 0;
-        valid = o < (e & 127);
-        const size_t row = (size_t)(valid ? (e >> 7) + o : 0) * D;
-        kp = Kh + row;
-        vp = Vh + row;
-        bias = valid ? 0.0f : -INFINITY;
-      }
-      vm[i] = valid ? 0xffffffffu : 0u;
-      br[i] = bias;
-      kr[i] = *reinterpret_cast<const uint4*>(kp + c8 * 8);
-      vr[i] = *reinterpret_cast<const uint4*>(vp + c8 * 8);
-    }
-  };
-  auto put = [&]() {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int slot = (tid + i * NT) / CPR;
-      const uint32_t m = vm[i];
-      *reinterpret_cast<uint4*>(&k_lds[0][slot * STR + c8 * 16]) =
-          make_uint4(kr[i].x & m, kr[i].y & m, kr[i].z & m, kr[i].w & m);
-      *reinterpret_cast<uint4*>(&v_lds[0][slot * STR + c8 * 16]) =
-          make_uint4(vr[i].x & m, vr[i].y & m, vr[i].z & m, vr[i].w & m);
-      if (c8 == 0) bias_lds[0][slot] = br[i];
-    }
-  };
   auto consume = [&](const char* kbuf, const char* vbuf, const float* bbuf) {
     const char* kb = kbuf + kh * 16 * MTW * STR;   // this wave's keys
     const char* vb = vbuf + kh * 16 * MTW * STR;
@@ -951,10 +904,69 @@ void dq_kernel(BwdArgs a) {
       }
     }
   } else {
+    // One LDS buffer, filled global -> LDS directly by buffer loads (the other
+    // resident workgroups cover the copy latency): wave w copies the 1 KiB
+    // pieces w, w + NWAVES, ... of the padded K and V tiles, lane l bytes
+    // 16 l .. 16 l + 15 of a piece (row x / STR, byte column x % STR; padding
+    // columns copy the row's first chunk, never read). A slot that holds no
+    // key gets an offset past the end of every resource, so the copy writes
+    // zeros, and logit offset -inf.
+    constexpr int KTB = kKeyTile * STR;
+    constexpr int NPC = KTB / 1024;
+    constexpr int NPW = (NPC + NWAVES - 1) / NWAVES;
+    static_assert(KTB % 1024 == 0, "tile must be whole 1 KiB pieces");
+    constexpr uint32_t kNoRow = 0x80000000u;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int pslot[NPW];
+    uint32_t pcol[NPW];
+#pragma unroll
+    for (int pp = 0; pp < NPW; ++pp) {
+      const int x = (pp * NWAVES + wave_u) * 1024 + 16 * lane;
+      pslot[pp] = x / STR;
+      const int col = x - pslot[pp] * STR;
+      pcol[pp] = (uint32_t)(col < 2 * D ? col : 0);
+    }
+    const int head_bytes = (int)((size_t)s.L * D * 2), pooled_bytes = (int)((size_t)s.N * D * 2);
+    const RowsRsrc k_rs = rows_rsrc(Kh, head_bytes), v_rs = rows_rsrc(Vh, head_bytes);
+    const RowsRsrc kc_rs = rows_rsrc(kch, pooled_bytes), vc_rs = rows_rsrc(vch, pooled_bytes);
     for (int t = 0; t < a.ntiles; ++t) {
-      fetch(t);
-      if (t > 0) __syncthreads();
-      put();
+      if (t > 0) __syncthreads();   // previous tile fully consumed
+      const bool pooled = MODE == kFlat && t >= a.ntiles_exact;
+#pragma unroll
+      for (int pp = 0; pp < NPW; ++pp) {
+        const int piece = pp * NWAVES + wave_u;
+        if (piece < NPC) {
+          const int slot = pslot[pp];
+          uint32_t off;
+          if (pooled) {
+            const int p = (t - a.ntiles_exact) * kKeyTile + slot;
+            const int e = p < s.N_kv ? ptab[p] : 1;
+            const bool valid = !(e & 1) && ((e >> 1) & 127) > 0;
+            off = valid ? (uint32_t)((e >> 8) * D * 2) + pcol[pp] : kNoRow;
+          } else {
+            const int q = t * per + (slot >> lb), o = slot & (b - 1);
+            const int e = q < ntab ? jtab[q] : 0;
+            off = o < (e & 127) ? (uint32_t)(((e >> 7) + o) * D * 2) + pcol[pp] : kNoRow;
+          }
+          copy16_to_lds(pooled ? kc_rs : k_rs, k_lds[0] + piece * 1024, off, 0);
+          copy16_to_lds(pooled ? vc_rs : v_rs, v_lds[0] + piece * 1024, off, 0);
+        }
+      }
+      if (tid < kKeyTile) {
+        float bias;
+        if (pooled) {
+          const int p = (t - a.ntiles_exact) * kKeyTile + tid;
+          const int e = p < s.N_kv ? ptab[p] : 1;
+          const int n = (e >> 1) & 127;
+          bias = (!(e & 1) && n > 0) ? __log2f((float)n) : -INFINITY;
+        } else {
+          const int q = t * per + (tid >> lb), o = tid & (b - 1);
+          const int e = q < ntab ? jtab[q] : 0;
+          bias = o < (e & 127) ? 0.0f : -INFINITY;
+        }
+        bias_lds[0][tid] = bias;
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies landed
       __syncthreads();
       consume(k_lds[0], v_lds[0], bias_lds[0]);
     }
