@@ -1197,17 +1197,44 @@ void dkv_pc_kernel(BwdArgs a) {
     fb[u + 1] = fb[u] + __builtin_amdgcn_readfirstlane(c);   // the same in every lane
   }
   const int total = fb[KPB];
-  auto query_at = [&](int i, int& act) -> int {
-    if (i < s.n_sharp) {
-      act = -1;
-      return srow[i];
-    }
+  // start of each kept block's flat list (the same in every lane)
+  int lbase[KPB];
+#pragma unroll
+  for (int u = 0; u < KPB; ++u)
+    lbase[u] = (s.n_flat > 0 && pb + u < s.N_kv) ? __builtin_amdgcn_readfirstlane(off[pb + u]) : 0;
+  // which of this workgroup's kept blocks a stream entry belongs to (-1: a
+  // sharp block, read by all of them)
+  auto act_of = [&](int i) -> int {
+    if (i < s.n_sharp) return -1;
     int u = 0;
 #pragma unroll
     for (int v = 0; v < KPB; ++v)
       if (i >= fb[v + 1]) u = v + 1;
-    act = u;
-    return lst[off[pb + u] + (i - fb[u])];
+    return u;
+  };
+  // block id of stream entry j (per lane; 0 past the end)
+  auto entry_at = [&](int j) -> int {
+    if (j >= total) return 0;
+    if (j < s.n_sharp) return srow[j];
+    const int u = act_of(j);
+    return lst[lbase[u] + (j - fb[u])];
+  };
+  // The stream's block ids sit in two 64-entry windows across the lanes
+  // (entries W .. W+63 and W+64 .. W+127), read with v_readlane: no memory
+  // access on the step's critical path. The next window is loaded 64 steps
+  // before it is needed.
+  int W = 0;
+  int win = entry_at(lane), wnext = entry_at(64 + lane);
+  auto id_at = [&](int i) -> int {
+    const int r = __builtin_amdgcn_readfirstlane(i - W);
+    return r < 64 ? __builtin_amdgcn_readlane(win, r) : __builtin_amdgcn_readlane(wnext, r - 64);
+  };
+  auto slide = [&](int i) {   // keep entries i+1 .. i+2 inside the windows
+    if (i + 1 >= W + 64) {
+      W += 64;
+      win = wnext;
+      wnext = entry_at(W + 64 + lane);
+    }
   };
 
   const float cscale = kLog2e / sqrtf((float)D);
@@ -1277,8 +1304,8 @@ void dkv_pc_kernel(BwdArgs a) {
         dl_lds[buf][tid] = -dv;   // stored negated: the dP sums start from it
       }
     };
-    int act_cur;
-    fetch(query_at(0, act_cur), q_l0, d_l0);
+    int act_cur = act_of(0);
+    fetch(id_at(0), q_l0, d_l0);
     put_stats(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies landed
     __syncthreads();
@@ -1288,9 +1315,10 @@ void dkv_pc_kernel(BwdArgs a) {
                     const char* DP, char* QN, char* DN) __attribute__((always_inline)) {
       int par = i & 1;
       asm volatile("" : "+s"(cur), "+s"(prev), "+s"(next), "+s"(par));
-      int act_next = -1;
+      slide(i);
       const bool more = i + 1 < total;
-      if (more) fetch(query_at(i + 1, act_next), QN, DN);
+      const int act_next = more ? act_of(i + 1) : -1;
+      if (more) fetch(id_at(i + 1), QN, DN);
       if (producer) {
         if (i < total) {
           float kbias[NF];
