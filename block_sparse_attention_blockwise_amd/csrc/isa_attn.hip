@@ -632,7 +632,6 @@ void attn_kernel(AttnArgs a) {
     if (P > 0) {
       constexpr int KTB = kKeyTile * KSTR;            // bytes of one staged tile
       constexpr int NPC = KTB / 1024;                  // 1 KiB pieces per tile
-      constexpr int NPW = (NPC + NWAVES - 1) / NWAVES; // pieces per wave, at most
       static_assert(KTB % 1024 == 0, "tile must be whole 1 KiB pieces");
       // Wave w copies pieces w, w + NWAVES, ... of each buffer; lane l of a
       // piece holds its bytes 16 l .. 16 l + 15, i.e. chunk (x % KSTR) / 16 of
@@ -641,15 +640,26 @@ void attn_kernel(AttnArgs a) {
       // boundaries for b = 32, 64), so its block start is wave-uniform; the
       // lane's element offset within the block is fixed for every tile.
       const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-      uint32_t dma_off[NPW];   // byte offset of the lane's chunk from its block start
-      int dma_blk[NPW];        // which of the tile's (at most two) blocks the piece is in
+      // Pieces 0 .. NFULL*NWAVES - 1 of K and of V go to every wave in turn;
+      // the NREM pieces left over of each tensor go one per wave to the last
+      // 2 NREM waves (K, then V), so that the two waves sharing a SIMD
+      // (w and w + 4) issue the same number of copies between them.
+      constexpr int NFULL = NPC / NWAVES;
+      constexpr int NREM = NPC - NFULL * NWAVES;
+      static_assert(!PIPE || (2 * NREM <= NWAVES && NWAVES == 8), "leftover pieces, one per wave");
+      uint32_t dma_off[NFULL + 1];   // byte offset of the lane's chunk from its block start
+      int dma_blk[NFULL + 1];        // which of the tile's (at most two) blocks the piece is in
+      const bool extra = wave_u >= NWAVES - 2 * NREM;
+      const bool extra_v = wave_u >= NWAVES - NREM;
+      const int xpiece = NFULL * NWAVES + (extra_v ? wave_u - (NWAVES - NREM) : wave_u - (NWAVES - 2 * NREM));
 #pragma unroll
-      for (int pp = 0; pp < NPW; ++pp) {
-        const int x = (pp * NWAVES + wave_u) * 1024 + 16 * lane;
+      for (int pp = 0; pp <= NFULL; ++pp) {
+        const int piece = pp < NFULL ? pp * NWAVES + wave_u : (extra ? xpiece : 0);
+        const int x = piece * 1024 + 16 * lane;
         const int row = x / KSTR, col = x - row * KSTR;
         const int ce = col < 2 * D ? col / 2 : 0;
         dma_off[pp] = (uint32_t)(((MODE == kDense ? row : (row & (b - 1))) * D + ce) * 2);
-        dma_blk[pp] = MODE == kDense ? 0 : ((pp * NWAVES + wave_u) * 1024 / KSTR) >> lb;
+        dma_blk[pp] = MODE == kDense ? 0 : (piece * 1024 / KSTR) >> lb;
       }
       // The copies are buffer loads into LDS: a buffer resource over this
       // head's rows (out-of-range reads return zero), the lane's fixed 32-bit
@@ -669,13 +679,16 @@ void attn_kernel(AttnArgs a) {
           base0 = (uint32_t)(__builtin_amdgcn_readfirstlane(e0) >> 7);           \
           base1 = (uint32_t)(__builtin_amdgcn_readfirstlane(e1) >> 7);           \
         }                                                                        \
-        _Pragma("unroll") for (int pp = 0; pp < NPW; ++pp) {                     \
+        _Pragma("unroll") for (int pp = 0; pp < NFULL; ++pp) {                   \
           const int piece = pp * NWAVES + wave_u;                                \
-          if (piece < NPC) {                                                     \
-            const int bo = (int)((dma_blk[pp] ? base1 : base0) * (uint32_t)(2 * D)); \
-            copy16_to_lds(k_rs, (KD) + piece * 1024, dma_off[pp], bo);          \
-            copy16_to_lds(v_rs, (VD) + piece * 1024, dma_off[pp], bo);          \
-          }                                                                      \
+          const int bo = (int)((dma_blk[pp] ? base1 : base0) * (uint32_t)(2 * D)); \
+          copy16_to_lds(k_rs, (KD) + piece * 1024, dma_off[pp], bo);            \
+          copy16_to_lds(v_rs, (VD) + piece * 1024, dma_off[pp], bo);            \
+        }                                                                        \
+        if (NREM > 0 && extra) {                                                 \
+          const int bo = (int)((dma_blk[NFULL] ? base1 : base0) * (uint32_t)(2 * D)); \
+          if (extra_v) copy16_to_lds(v_rs, (VD) + xpiece * 1024, dma_off[NFULL], bo); \
+          else copy16_to_lds(k_rs, (KD) + xpiece * 1024, dma_off[NFULL], bo);   \
         }                                                                        \
       }
       ISA_DMA_TILE(0, k_lds[0], v_lds[0])
