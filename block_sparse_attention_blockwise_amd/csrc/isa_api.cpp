@@ -472,6 +472,8 @@ int isa_dense_attn(int32_t B, int32_t H, int32_t L, int32_t D, const void* Q, co
   if (!aligned16({Q, K, V, O})) return ISA_ERR_ARG;
   if (D != 64 && D != 128) return ISA_ERR_UNSUPPORTED;
   if ((int64_t)B * H > kMaxHeads) return ISA_ERR_UNSUPPORTED;
+  // one head's rows must be addressable with 32-bit byte offsets
+  if ((int64_t)L * D * 2 > (int64_t)INT32_MAX) return ISA_ERR_UNSUPPORTED;
   return hip_status(isa_launch_dense_attn(B, H, L, D, (const uint16_t*)Q, (const uint16_t*)K,
                                           (const uint16_t*)V, (uint16_t*)O, as_stream(stream)));
 }

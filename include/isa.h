@@ -267,7 +267,8 @@ ISA_API int isa_backward(const isa_params_t* p, const void* Q, const void* K, co
 
 /* Dense baseline: O = softmax(Q K^T / sqrt(D)) V over all L tokens (no mask),
  * bf16 in/out, same tile engine as isa_sharp_attn. D in {64, 128},
- * B * H <= 65535 (else ISA_ERR_UNSUPPORTED). The
+ * B * H <= 65535 and L * D * 2 < 2^31 bytes per head (else
+ * ISA_ERR_UNSUPPORTED). The
  * comparison line the pages measure ISA against (rainbus.top summary,
  * "Prerequisites", SDPA and FlashAttention paragraph). */
 ISA_API int isa_dense_attn(int32_t B, int32_t H, int32_t L, int32_t D, const void* Q, const void* K,

@@ -157,6 +157,8 @@ def test_calls_fail_before_launch(isa):
     assert L.isa_dense_attn(1, 1, 0, 128, fake, fake, fake, fake, None) == -1
     assert L.isa_dense_attn(1, 1, 16, 96, fake, fake, fake, fake, None) == -2
     assert L.isa_dense_attn(256, 256, 16, 64, fake, fake, fake, fake, None) == -2
+    # a head's rows beyond 32-bit byte offsets
+    assert L.isa_dense_attn(1, 1, 1 << 23, 128, fake, fake, fake, fake, None) == -2
     assert L.isa_dense_attn(1, 1, 16, 128, None, fake, fake, fake, None) == -1
     # 16-byte alignment of the vector-accessed tensors
     odd = fake + 8
