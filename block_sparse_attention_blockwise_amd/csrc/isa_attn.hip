@@ -709,7 +709,7 @@ void attn_kernel(AttnArgs a) {
         rescale<D, QT>(mx, m, lsum, oacc);                                       \
         qk_tile<D, QT>(KC, qf, snext, g, c16);                                   \
         exp_pack<QT>(scur, cscale, m, lsum, pb);                                 \
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                       \
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                       \
         _Pragma("unroll") for (int i = 0; i < 14; ++i) {                         \
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                     \
           __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                     \
