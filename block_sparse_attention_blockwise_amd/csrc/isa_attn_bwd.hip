@@ -1104,9 +1104,11 @@ __device__ __forceinline__ void kv_block(const char* q_lds, const char* d_lds, c
 
 // Exact keys, producer/consumer form: one workgroup per 128 keys of J (whole
 // kept blocks), 8 waves in 4 pairs, each pair owning 32 keys. The producer
-// wave of a pair computes S = Q K^T and P for the current query block,
-// passes P (bf16) to its consumer through LDS and accumulates dV^T += dO^T P;
-// the consumer works one query block behind: dP = dO V^T, dS = P (dP - Delta)
+// wave of a pair computes S = Q K^T and P for the current query block and
+// passes P (bf16) to its consumer through LDS; it keeps its own packed copy
+// and accumulates dV^T += dO^T P for that block at the start of the next
+// step, so that its exponentials run while the consumer's products do. The
+// consumer works one query block behind: dP = dO V^T, dS = P (dP - Delta)
 // and dK^T += Q^T dS. Each operand read from LDS feeds two matrix-core
 // products (32 keys per wave) while both roles stay within 256 registers, so
 // two waves share each SIMD. Query blocks stream through three LDS buffers
@@ -1304,6 +1306,7 @@ void dkv_pc_kernel(BwdArgs a) {
         dl_lds[buf][tid] = -dv;   // stored negated: the dP sums start from it
       }
     };
+    bf16x8_t pcar[NF][MT / 2];
     int act_cur = act_of(0);
     fetch(id_at(0), q_l0, d_l0);
     put_stats(0);
@@ -1320,6 +1323,10 @@ void dkv_pc_kernel(BwdArgs a) {
       const int act_next = more ? act_of(i + 1) : -1;
       if (more) fetch(id_at(i + 1), QN, DN);
       if (producer) {
+        if (i > 0) {
+          mm_tr<D, MT, NF>(DP, pcar, acc, g, c16);
+          ahead<DT * (MT / 2), NF, 2, kDkvAhead, 2>();
+        }
         if (i < total) {
           float kbias[NF];
 #pragma unroll
@@ -1352,7 +1359,7 @@ void dkv_pc_kernel(BwdArgs a) {
                   sc[nf][mt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nf][mt][e], cscale, kbias[nf]) - lv[e]);
             }
           }
-          bf16x8_t pp[NF][MT / 2];
+          bf16x8_t (&pp)[NF][MT / 2] = pcar;
           pack_bf16<MT, NF>(sc, pp);
           // the consumer's copy of P: the operand words themselves. Word u of
           // pp[nf][kc] holds the bf16 pair (2h, 2h+1), h = u % 2, of fragment
@@ -1368,8 +1375,6 @@ void dkv_pc_kernel(BwdArgs a) {
               px[(2 * nf * MT + 4 * kc + 2) * 64] = w.z;
               px[(2 * nf * MT + 4 * kc + 3) * 64] = w.w;
             }
-          mm_tr<D, MT, NF>(DC, pp, acc, g, c16);
-          ahead<DT * (MT / 2), NF, 2, kDkvAhead, 2>();
         }
       } else if (i > 0) {
         // dP - Delta: the sums start from -Delta of each row
