@@ -31,7 +31,7 @@ struct Layout {
   size_t qc, kc, kcb, vcb, ctx_idx, ctx_score, sharp, sharp_idx, flat_idx, exact, ftk, srows;
   size_t qr, kr, rope;          // RoPE buffers (only when rope_base > 0)
   size_t lse;                   // saved by isa_forward for isa_backward
-  size_t delta, dkc, dvc, ebits, inv_off, inv_list;   // backward scratch
+  size_t delta, dkc, dvc, ebits, inv_off, inv_list, chunk_ord;   // backward scratch
   size_t dqc, doc, ocs, dsc, pc;                     // backward of the residual (gamma != 0)
   size_t total;
 };
@@ -70,7 +70,7 @@ Layout make_layout(const IsaShape& s, bool with_backward = true) {
   l.kr = o;        o = align256(o + qkr);
   l.rope = o;      o = align256(o + rope_table_bytes(s));
   if (!with_backward) {
-    l.lse = l.delta = l.dkc = l.dvc = l.ebits = l.inv_off = l.inv_list = 0;
+    l.lse = l.delta = l.dkc = l.dvc = l.ebits = l.inv_off = l.inv_list = l.chunk_ord = 0;
     l.dqc = l.doc = l.ocs = l.dsc = l.pc = 0;
     l.total = o;
     return l;
@@ -82,6 +82,7 @@ Layout make_layout(const IsaShape& s, bool with_backward = true) {
   l.ebits = o;     o = align256(o + bh * s.n_flat * (size_t)((s.N_kv + 63) / 64) * 8);
   l.inv_off = o;   o = align256(o + bh * (size_t)(s.N_kv + 1) * 4);
   l.inv_list = o;  o = align256(o + bh * s.n_flat * (size_t)s.k_ns * 4);
+  l.chunk_ord = o; o = align256(o + bh * (size_t)s.N_kv * 4);
   const bool res = s.gamma != 0.0f;
   const size_t rnd = res ? nd * 4 : 0;
   const size_t rnk = res ? bh * s.N * (size_t)s.N_kv * 4 : 0;
@@ -449,6 +450,7 @@ int isa_backward(const isa_params_t* p, const void* Q, const void* K, const void
   b.ebits = (uint64_t*)(w + l.ebits);
   b.inv_off = (int32_t*)(w + l.inv_off);
   b.inv_list = (int32_t*)(w + l.inv_list);
+  b.chunk_ord = (int32_t*)(w + l.chunk_ord);
   b.dkc = (float*)(w + l.dkc);
   b.dvc = (float*)(w + l.dvc);
   b.rope = rope ? (const float2*)(w + l.rope) : nullptr;

@@ -70,6 +70,7 @@ struct BwdArgs {
   const uint64_t* ebits;      // [B,H,n_flat,W] bit p of row r: position p of J is in E_r
   const int32_t* inv_off;     // [B,H,N_kv+1]
   const int32_t* inv_list;    // [B,H,n_flat*k_ns] flat block ids reading each position exactly
+  const int32_t* chunk_ord;   // [B,H,N_kv] 128-key chunks of J, longest stream first (n_flat > 0)
   const float* dkc;           // [B,H,N,D] pooled-key gradients (nullable)
   const float* dvc;
   float* dkc_out;
@@ -255,9 +256,10 @@ __device__ inline void store4(uint16_t* row, int d0, float4_t v, const float2* r
 // ---------------------------------------------------------------- prep
 // One workgroup per head: the E bitmap (one row of ceil(N_kv/64) words per
 // flat block), the count of flat blocks per kept position, their offsets,
-// and then each position's list of flat blocks, filled in ascending order by
-// one thread walking the bitmap column (linear in n_flat, no sort, so the
-// order is fixed however many flat blocks share a position).
+// the order of the dK/dV kernel's 128-key chunks, and then each position's
+// list of flat blocks, filled in ascending order by one thread walking the
+// bitmap column (linear in n_flat, no sort, so the order is fixed however
+// many flat blocks share a position).
 constexpr int kPrepThreads = 1024;
 
 __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
@@ -271,6 +273,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
   int32_t* lst = const_cast<int32_t*>(a.inv_list) + (size_t)bh * s.n_flat * s.k_ns;
   __shared__ int cnt[ISA_MAX_NKV + 1];
   __shared__ int part[kPrepThreads];
+  __shared__ int clen[ISA_MAX_NKV / 2];
   for (int p = tid; p <= s.N_kv; p += kPrepThreads) cnt[p] = 0;
   __syncthreads();
   for (int r = tid; r < s.n_flat; r += kPrepThreads) {
@@ -315,6 +318,35 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(BwdArgs a) {
   }
   if (tid == kPrepThreads - 1) off[s.N_kv] = part[tid] + sum;
   __syncthreads();
+  // Chunk order of the dK/dV grid: the chunks whose keys the most flat
+  // blocks read exactly (the longest streams) first, ties by position. The
+  // workgroups dispatched together then run streams of about the same length,
+  // so they stay in step through the part all of them read in the same order
+  // (the sharp blocks), and each of its blocks is fetched into L2 once for
+  // all of them rather than again for each straggler.
+  {
+    const int kpb = 128 / s.b;
+    const int C = (s.N_kv + kpb - 1) / kpb;
+    for (int c = tid; c < C; c += kPrepThreads) {
+      int n = 0;
+      for (int u = 0; u < kpb; ++u) {
+        const int p = c * kpb + u;
+        if (p < s.N_kv) n += cnt[p];
+      }
+      clen[c] = n;
+    }
+    __syncthreads();
+    int32_t* ord = const_cast<int32_t*>(a.chunk_ord) + (size_t)bh * s.N_kv;
+    for (int c = tid; c < C; c += kPrepThreads) {
+      const int n = clen[c];
+      int r = 0;
+      for (int d = 0; d < C; ++d) {
+        const int m = clen[d];
+        r += (m > n || (m == n && d < c)) ? 1 : 0;
+      }
+      ord[r] = c;
+    }
+  }
   // each position's flat blocks in ascending order: walk the bitmap column
   for (int p = tid; p < s.N_kv; p += kPrepThreads) {
     int k = off[p];
@@ -1158,6 +1190,8 @@ void dkv_pc_kernel(BwdArgs a) {
       bh = logical / gridDim.x;
     }
   }
+  // chunks in the order the prep kernel set (longest streams first)
+  if (s.n_flat > 0) cx = __builtin_amdgcn_readfirstlane(a.chunk_ord[(size_t)bh * s.N_kv + cx]);
   const int pb = cx * KPB;
   const size_t head = (size_t)bh * s.L;
   const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
@@ -1651,6 +1685,7 @@ hipError_t isa_launch_backward(const IsaShape& s, const IsaBwdBuffers& w, hipStr
   a.ebits = w.ebits;
   a.inv_off = w.inv_off;
   a.inv_list = w.inv_list;
+  a.chunk_ord = w.chunk_ord;
   a.dkc = a.dkc_out = w.dkc;
   a.dvc = a.dvc_out = w.dvc;
   a.rope = w.rope;

@@ -160,6 +160,7 @@ struct IsaBwdBuffers {
   uint64_t* ebits;
   int32_t* inv_off;
   int32_t* inv_list;
+  int32_t* chunk_ord;
   float* dkc;
   float* dvc;
   const float2* rope;         // nullable
