@@ -28,7 +28,7 @@ bool ratio_ok(double a) { return !std::isnan(a) && a >= 0.0 && a <= 1.0; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t qc, kc, kcb, vcb, ctx_idx, ctx_score, sharp, sharp_idx, flat_idx, exact, ftk, srows;
+  size_t qc, kc, kcb, vcb, ctx_idx, ctx_score, sharp, sharp_idx, flat_idx, exact, flat_ord, ftk, srows;
   size_t qr, kr, rope;          // RoPE buffers (only when rope_base > 0)
   size_t lse;                   // saved by isa_forward for isa_backward
   size_t delta, dkc, dvc, ebits, inv_off, inv_list, chunk_ord;   // backward scratch
@@ -61,6 +61,7 @@ Layout make_layout(const IsaShape& s, bool with_backward = true) {
   l.sharp_idx = o; o = align256(o + at_least1(bh * s.n_sharp) * 4);
   l.flat_idx = o;  o = align256(o + at_least1(bh * s.n_flat) * 4);
   l.exact = o;     o = align256(o + at_least1(bh * s.n_flat * (size_t)s.k_ns) * 4);
+  l.flat_ord = o;  o = align256(o + at_least1(bh * s.n_flat) * 4);
   // exact-set rows of the flat blocks in flight (only when they do not fit LDS)
   l.ftk = o;       o = align256(o + isa_flat_topk_scratch_bytes(s));
   // coarse rows S[i, J]: only the gamma residual stores them
@@ -292,7 +293,7 @@ int isa_flat_taylor_attn(const isa_params_t* p, const void* Q, const void* K, co
   return hip_status(isa_launch_flat_attn(s, (const uint16_t*)Q, (const uint16_t*)K,
                                          (const uint16_t*)V, (const uint16_t*)kc_bf16,
                                          (const uint16_t*)vc_bf16, ctx_idx, flat_idx,
-                                         flat_exact_idx, (uint16_t*)O, nullptr,
+                                         flat_exact_idx, nullptr, (uint16_t*)O, nullptr,
                                          as_stream(stream)));
 }
 
@@ -354,10 +355,12 @@ int forward_impl(const IsaShape& s, const void* Q, const void* K, const void* V,
   if (e == hipSuccess) e = isa_launch_sharpness(s, qc, kc, sharp, st);
   if (e == hipSuccess) e = isa_launch_split(s, sharp, sharp_idx, flat_idx, st);
   if (e == hipSuccess) e = isa_launch_flat_topk(s, qc, kc, ctx_idx, flat_idx, exact, (double*)(w + l.ftk), st);
+  int32_t* flat_ord = (s.n_flat > 0 && s.k_ns > 0) ? (int32_t*)(w + l.flat_ord) : nullptr;
+  if (e == hipSuccess && flat_ord) e = isa_launch_flat_order(s, exact, flat_ord, st);
   float* lse = l.lse ? (float*)(w + l.lse) : nullptr;
   if (e == hipSuccess) e = isa_launch_sharp_attn(s, q, k, v, ctx_idx, sharp_idx, (uint16_t*)O, lse, st);
   if (e == hipSuccess)
-    e = isa_launch_flat_attn(s, q, k, v, kcb, vcb, ctx_idx, flat_idx, exact, (uint16_t*)O, lse, st);
+    e = isa_launch_flat_attn(s, q, k, v, kcb, vcb, ctx_idx, flat_idx, exact, flat_ord, (uint16_t*)O, lse, st);
   if (e == hipSuccess && s.gamma != 0.0f) {
     // the residual's pooled attention reads whole coarse rows (kept for the backward)
     e = isa_launch_coarse_rows(s, qc, kc, ctx_idx, srows, st);
@@ -447,6 +450,7 @@ int isa_backward(const isa_params_t* p, const void* Q, const void* K, const void
   b.sharp_idx = (const int32_t*)(w + l.sharp_idx);
   b.flat_idx = (const int32_t*)(w + l.flat_idx);
   b.exact = (const int32_t*)(w + l.exact);
+  b.flat_ord = (s.n_flat > 0 && s.k_ns > 0) ? (const int32_t*)(w + l.flat_ord) : nullptr;
   b.ebits = (uint64_t*)(w + l.ebits);
   b.inv_off = (int32_t*)(w + l.inv_off);
   b.inv_list = (int32_t*)(w + l.inv_list);

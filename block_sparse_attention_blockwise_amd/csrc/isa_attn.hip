@@ -73,6 +73,7 @@ struct AttnArgs {
   const int32_t* ctx_idx;    // [B,H,k_ctx] kept context blocks (global ids)
   const int32_t* qlist;      // sharp_idx or flat_idx [B,H,n_q]
   const int32_t* exact;      // flat: [B,H,n_flat,k_ns]
+  const int32_t* flat_ord;   // flat: [B,H,n_flat] grid order of the rows (nullable: plain order)
   float* lse;                // optional [B,H,L]: log2 of each row's softmax denominator
   int n_q;
   int ntiles_exact;
@@ -387,9 +388,12 @@ void attn_kernel(AttnArgs a) {
   // contiguous run of tiles, i.e. mostly one head at a time. The flat
   // kernel for 32-token blocks (twice the blocks, each gathering its own
   // exact set) takes the same order: it doubles its L2 hit rate when the
-  // exact sets are large; the 64-token flat kernel keeps the plain order.
+  // exact sets are large; the 64-token flat kernel keeps the plain order
+  // unless the flat blocks come with a grid order (flat_ord: blocks whose
+  // exact sets overlap next to each other), which each XCD's run follows.
   int tile_x = blockIdx.x, bh = blockIdx.y;
-  if (MODE != kFlat || KS == 2) {
+  const bool ordered = MODE == kFlat && a.flat_ord != nullptr;
+  if (MODE != kFlat || KS == 2 || ordered) {
     const int total = gridDim.x * gridDim.y;
     if ((total & 7) == 0) {
       const int id = blockIdx.x + gridDim.x * blockIdx.y;
@@ -398,6 +402,7 @@ void attn_kernel(AttnArgs a) {
       bh = logical / gridDim.x;
     }
   }
+  if (ordered) tile_x = __builtin_amdgcn_readfirstlane(a.flat_ord[(size_t)bh * s.n_flat + tile_x]);
   const size_t head = (size_t)bh * s.L;     // first token row of this (batch, head)
   const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
   const int b = s.b;
@@ -890,9 +895,10 @@ hipError_t isa_launch_flat_attn(const IsaShape& s, const uint16_t* Q, const uint
                                 const uint16_t* V, const uint16_t* kc_bf16,
                                 const uint16_t* vc_bf16, const int32_t* ctx_idx,
                                 const int32_t* flat_idx, const int32_t* flat_exact_idx,
-                                uint16_t* O, float* lse, hipStream_t st) {
+                                const int32_t* flat_ord, uint16_t* O, float* lse, hipStream_t st) {
   if (s.n_flat == 0) return hipSuccess;
   AttnArgs a = base_args(s, Q, K, V, O);
+  a.flat_ord = flat_ord;
   a.lse = lse;
   a.kcb = kc_bf16;
   a.vcb = vc_bf16;
@@ -911,6 +917,44 @@ hipError_t isa_launch_flat_attn(const IsaShape& s, const uint16_t* Q, const uint
                       : launch<64, kFlat, 1, 4, false>(a, grid, st);
   return s.D == 128 ? launch<128, kFlat, 1, 4, false, 2>(a, grid, st)
                     : launch<64, kFlat, 1, 4, false, 2>(a, grid, st);
+}
+
+// Grid order of the flat blocks: by the first (smallest) block id of each
+// exact set E_i, ties by row (a stable rank, one workgroup per head, the
+// keys in LDS). Flat blocks whose exact sets begin at the same block share
+// many of their blocks when attention is local, so the workgroups that one
+// XCD runs together gather overlapping blocks and find them in its L2; with
+// no such structure the order is as good as any other.
+namespace {
+
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void flat_order_kernel(IsaShape s, const int32_t* exact,
+                                                                    int32_t* ord) {
+  __shared__ int key[2 * ISA_MAX_SEG_BLOCKS];
+  const int bh = blockIdx.x;
+  const int32_t* ex = exact + (size_t)bh * s.n_flat * s.k_ns;
+  for (int r = threadIdx.x; r < s.n_flat; r += kOrderThreads) key[r] = ex[(size_t)r * s.k_ns];
+  __syncthreads();
+  int32_t* o = ord + (size_t)bh * s.n_flat;
+  for (int r = threadIdx.x; r < s.n_flat; r += kOrderThreads) {
+    const int k = key[r];
+    int rank = 0;
+    for (int q = 0; q < s.n_flat; ++q) {
+      const int m = key[q];
+      rank += (m < k || (m == k && q < r)) ? 1 : 0;
+    }
+    o[rank] = r;
+  }
+}
+
+}  // namespace
+
+hipError_t isa_launch_flat_order(const IsaShape& s, const int32_t* flat_exact_idx, int32_t* flat_ord,
+                                 hipStream_t st) {
+  if (s.n_flat == 0 || s.k_ns == 0) return hipSuccess;
+  flat_order_kernel<<<s.B * s.H, kOrderThreads, 0, st>>>(s, flat_exact_idx, flat_ord);
+  return hipGetLastError();
 }
 
 hipError_t isa_launch_dense_attn(int B, int H, int L, int D, const uint16_t* Q,

@@ -67,6 +67,7 @@ struct BwdArgs {
   const int32_t* sharp_idx;   // [B,H,n_sharp]
   const int32_t* flat_idx;    // [B,H,n_flat]
   const int32_t* exact;       // [B,H,n_flat,k_ns]
+  const int32_t* flat_ord;    // [B,H,n_flat] grid order of the flat dQ kernel (nullable: plain order)
   const uint64_t* ebits;      // [B,H,n_flat,W] bit p of row r: position p of J is in E_r
   const int32_t* inv_off;     // [B,H,N_kv+1]
   const int32_t* inv_list;    // [B,H,n_flat*k_ns] flat block ids reading each position exactly
@@ -750,7 +751,19 @@ void dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int rwave = wave % RW, kh = wave / RW;   // row group, key half
-  const int qx = blockIdx.x, bh = blockIdx.y;
+  int qx = blockIdx.x, bh = blockIdx.y;
+  // flat blocks in the forward's grid order (exact sets that overlap next
+  // to each other), each XCD taking a contiguous run of it
+  if (MODE == kFlat && a.flat_ord != nullptr) {
+    const int total = gridDim.x * gridDim.y;
+    if ((total & 7) == 0) {
+      const int id = blockIdx.x + gridDim.x * blockIdx.y;
+      const int logical = (id & 7) * (total >> 3) + (id >> 3);
+      qx = logical % gridDim.x;
+      bh = logical / gridDim.x;
+    }
+    qx = __builtin_amdgcn_readfirstlane(a.flat_ord[(size_t)bh * s.n_flat + qx]);
+  }
   const size_t head = (size_t)bh * s.L;
   const int32_t* ctx_row = a.ctx_idx + (size_t)bh * s.k_ctx;
   const int b = s.b, lb = b == 64 ? 6 : 5;
@@ -1682,6 +1695,7 @@ hipError_t isa_launch_backward(const IsaShape& s, const IsaBwdBuffers& w, hipStr
   a.sharp_idx = w.sharp_idx;
   a.flat_idx = w.flat_idx;
   a.exact = w.exact;
+  a.flat_ord = w.flat_ord;
   a.ebits = w.ebits;
   a.inv_off = w.inv_off;
   a.inv_list = w.inv_list;

@@ -140,7 +140,10 @@ hipError_t isa_launch_flat_attn(const IsaShape& s, const uint16_t* Q, const uint
                                 const uint16_t* V, const uint16_t* kc_bf16,
                                 const uint16_t* vc_bf16, const int32_t* ctx_idx,
                                 const int32_t* flat_idx, const int32_t* flat_exact_idx,
-                                uint16_t* O, float* lse, hipStream_t st);
+                                const int32_t* flat_ord, uint16_t* O, float* lse, hipStream_t st);
+// Grid order of the flat blocks (flat_ord [B,H,n_flat]) for the flat kernels.
+hipError_t isa_launch_flat_order(const IsaShape& s, const int32_t* flat_exact_idx, int32_t* flat_ord,
+                                 hipStream_t st);
 // Buffers of the backward pass (device pointers; the forward's saved state
 // and the backward's scratch live in the forward workspace).
 struct IsaBwdBuffers {
@@ -157,6 +160,7 @@ struct IsaBwdBuffers {
   const int32_t* sharp_idx;
   const int32_t* flat_idx;
   const int32_t* exact;
+  const int32_t* flat_ord;   // nullable: flat blocks in plain order
   uint64_t* ebits;
   int32_t* inv_off;
   int32_t* inv_list;
