@@ -168,29 +168,35 @@ def cpu_baseline(host, budget_s):
     rng = np.random.default_rng(0)
     sharp_order = rng.permutation(sel.sharp_idx)
     flat_order = rng.permutation(sel.flat_idx)
+    # Each oracle call with injected selections repeats the head's pooling
+    # and coarse steps; G blocks per call spread that fixed part, and its
+    # own time (the median of a few calls with no rows) is taken off.
+    G = 8
+    t_fixed = []
+    for _ in range(3):
+        t1 = time.perf_counter()
+        O.isa_head(Q, K, V, plan, selections=sel_d, rows=np.zeros(0, dtype=np.int64))
+        t_fixed.append(time.perf_counter() - t1)
+    t_fixed = float(np.median(t_fixed))
     done = {"sharp": [], "flat": []}
+    per_call = {"sharp": [], "flat": []}
     deadline = time.perf_counter() + budget_s
     k = 0
-    while time.perf_counter() < deadline or min(len(done["sharp"]), len(done["flat"])) < 2:
+    while time.perf_counter() < deadline or min(len(per_call["sharp"]), len(per_call["flat"])) < 2:
         for kind, order in (("sharp", sharp_order), ("flat", flat_order)):
-            if k >= len(order):
+            blocks = order[k:k + G]
+            if len(blocks) == 0:
                 continue
-            i = order[k]
-            s = plan.starts[i]
-            rows = np.arange(s, s + plan.counts[i])
+            rows = np.concatenate([np.arange(plan.starts[i], plan.starts[i] + plan.counts[i]) for i in blocks])
             t1 = time.perf_counter()
             O.isa_head(Q, K, V, plan, selections=sel_d, rows=rows)
-            done[kind].append(time.perf_counter() - t1)
-        k += 1
+            per_call[kind].append((time.perf_counter() - t1 - t_fixed) / len(blocks))
+            done[kind].extend(blocks)
+        k += G
         if k >= max(len(sharp_order), len(flat_order)):
             break
-    # isa_head with injected selections repeats the (cheap) pooling/coarse
-    # steps each call; subtract that share using a call with no rows.
-    t1 = time.perf_counter()
-    O.isa_head(Q, K, V, plan, selections=sel_d, rows=np.zeros(0, dtype=np.int64))
-    t_fixed = time.perf_counter() - t1
-    per_sharp = max(np.mean(done["sharp"]) - t_fixed, 0.0)
-    per_flat = max(np.mean(done["flat"]) - t_fixed, 0.0)
+    per_sharp = max(float(np.median(per_call["sharp"])), 0.0) if per_call["sharp"] else 0.0
+    per_flat = max(float(np.median(per_call["flat"])), 0.0) if per_call["flat"] else 0.0
     per_head = t_sel + per_sharp * plan.n_sharp + per_flat * plan.n_flat
     total_ms = per_head * w["B"] * w["H"] * 1e3
     host_cores, model = host_cpu()
@@ -198,7 +204,8 @@ def cpu_baseline(host, budget_s):
             "cpu_model": model, "kind": "oracle",
             "sample": (f"head (0,0) of {w['B'] * w['H']}: selections in full ({t_sel:.2f} s), outputs of "
                        f"{len(done['sharp'])} sharp and {len(done['flat'])} flat query blocks "
-                       f"(of {plan.n_sharp}/{plan.n_flat}); per-block times extrapolated to all "
+                       f"(of {plan.n_sharp}/{plan.n_flat}), {G} per oracle call less the call's fixed "
+                       f"part ({t_fixed:.3f} s); median per-block times extrapolated to all "
                        f"blocks and heads, numpy fp64 with {threads} BLAS threads")}
 
 
