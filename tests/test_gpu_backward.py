@@ -121,6 +121,18 @@ def test_backward_batch_and_heads(dev):
     _check_all_rows(p, heads=[(0, 0), (1, 2)])
 
 
+def test_backward_ordered_grids(dev):
+    """The dK/dV grid takes each head's key chunks longest stream first and
+    the flat dQ grid the forward's flat-block order, each XCD taking a
+    contiguous run when the workgroup count is a multiple of 8: B*H = 8
+    distinct heads, b = 64, many flat blocks per kept block; every gradient
+    element of every head against the oracle."""
+    p = isa.Params(2, 4, 1536, 1600, 128, 64, 0.25, 0.75, 0.25)
+    pl = isa.plan(p)
+    assert (pl["n_flat"] * p.B * p.H) % 8 == 0 and pl["k_ns"] > 1
+    _check_all_rows(p)
+
+
 @pytest.mark.parametrize("a_s,a_f,a_ns,L_ctx", [
     (1.0, 0.0, 0.25, 451),    # dense special case: every block sharp over every token
     (1.0, 1.0, 0.0, 451),     # pure Taylor: every block flat over pooled keys only

@@ -262,6 +262,29 @@ def test_flat_grid_order_with_distinct_heads(dev):
     _check(p, inp, res, heads, None)
 
 
+def test_flat_block_order_b64_distinct_heads(dev):
+    """isa_forward runs the 64-token flat kernel in the grid order that the
+    library ranks the flat blocks into (by the first block of their exact
+    sets, each XCD taking a contiguous run when the workgroup count is a
+    multiple of 8). Here B*H = 8 distinct heads, b = 64, a large exact set:
+    every selection and every output row of every head against the oracle,
+    and the stand-alone flat entry point (plain order) gives the same bits."""
+    p = isa.Params(2, 4, 3072, 3200, 128, 64, 0.25, 0.75, 0.25)
+    pl = isa.plan(p)
+    assert (pl["n_flat"] * p.B * p.H) % 8 == 0 and pl["k_ns"] > 1
+    inp = _inputs(STREAM["23768_ragged"], p)
+    res = _run(p, inp, dev)
+    heads = {(bi, h) for bi in range(p.B) for h in range(p.H)}
+    _check(p, inp, res, heads, None)
+    Q, K, V = (bf16_tensor(inp[n][0], dev) for n in "QKV")
+    O_ref, dbg = isa.forward(Q, K, V, p, debug=True)
+    _, _, kcb, vcb = isa.pool_coarse(Q, K, V, p)
+    O = O_ref.clone()
+    isa.flat_taylor_attn(Q, K, V, kcb, vcb, dbg["ctx_idx"], dbg["flat_idx"], dbg["flat_exact_idx"], p, out=O)
+    torch.cuda.synchronize()
+    assert torch.equal(O.view(torch.int16), O_ref.view(torch.int16))
+
+
 @pytest.mark.parametrize("B,H", [(2, 3), (3, 5)])
 def test_batch_and_odd_head_counts(dev, B, H):
     """B > 1 and head counts that do not fill the XCD remap evenly."""
